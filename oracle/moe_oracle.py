@@ -1,0 +1,420 @@
+"""Plain, slow, obviously-correct CPU oracle of the DeepSeekMoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. It shares no code
+with the HIP library.
+
+Sources, cited below by tag:
+
+[MH] "DeepSeek-V3 高效训练关键技术全景解析：从 MoE 架构到并行、通信与显存的极致优化"
+     (www.mhpq.cn/news/1102932): §1.1 (1 shared + 256 routed experts, 8 active,
+     the shared expert processes every token), §1.2 (per-expert bias adjusts
+     the routing score, not trained by gradient, raised for under-used experts
+     every step), §3.1 (each token limited to 4 of the EP nodes), §4.1 (gating
+     kept in high precision; 1x128 activation tiles, 128x128 weight blocks,
+     online max-abs scaling, fp32 accumulation).
+[GK] DeepSeek-V3 notes with Q&A (gkm0120.cn/p/38322.html): Q3 (the bias
+     enters the affinity score for routing only and never the gate values;
+     over-used experts lose bias, idle ones gain), Q8 (tile-wise 1x128 per
+     token / 128 channels; block-wise 128 in x 128 out channels).
+[KY] DeepSeek-V3 report walkthrough (kaiyunto.com/xinwenzhongxin/3873.html),
+     DeepSeekMoE paragraphs: sigmoid affinity scores, normalisation over the
+     selected scores gives the gates; overloaded expert -> bias minus gamma,
+     underloaded -> bias plus gamma (gamma = bias update speed); 1 shared + 256
+     routed, 8 active; experts are FFNs.
+[WX] "DeepSeek-V3核心技术解析：MoE、MLA、MTP与FP8训练详解" (wenxiaobai), §二(一):
+     top-K selection by affinity score; the shared expert takes part globally.
+
+Readings where the pages are silent (each listed with its reason in the design doc):
+SwiGLU experts without biases; group score = fp32 sum of the top-``topn``
+biased scores of the group; ties go to the lower index; gates divide by the
+plain fp32 sum of the selected unbiased scores (no extra scale); "overloaded"
+means count*E > T*K, compared exactly in integers; OCP E4M3FN with RNE and
+saturation to +-448; scale = amax/448.
+
+Floating point: routing is fp32, one IEEE op at a time (NumPy float32 ops are
+correctly rounded per op and never fused). Expert FFNs run in fp64 on the exact
+input values and are rounded once at the end.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+__all__ = [
+    "sigmoid_f32", "router_logits", "route", "permute", "bias_update",
+    "swiglu_expert", "layer_output", "forward", "round_bf16",
+    "e4m3_decode", "e4m3_encode", "quantize_rows_1x128", "quantize_blocks_128",
+    "dequant_rows_1x128", "dequant_blocks_128", "layer_output_fp8",
+    "RouteResult", "PermuteResult",
+]
+
+# ---------------------------------------------------------------------------
+# fp32 sigmoid built from IEEE + - * /, rint and ldexp only.
+# Affinity scores are sigmoids of the router logits [KY, DeepSeekMoE paragraph].
+# exp(v) = 2^n * exp(r) with n = rint(v*log2(e)) and r = v - n*ln2 taken in two
+# pieces (Cody-Waite); exp(r) by the degree-7 Taylor polynomial in Horner form.
+# C1 = 355/512 has 9 significant bits so n*C1 is exact for |n| < 2^15.
+# ---------------------------------------------------------------------------
+LOG2E_F32 = F32(1.4426950408889634)
+LN2_HI = F32(0.693359375)
+LN2_LO = F32(math.log(2.0) - 0.693359375)
+INV_FACT = [F32(1.0 / math.factorial(k)) for k in range(8)]
+
+
+def sigmoid_f32(u) -> np.ndarray:
+    """fp32 sigmoid 1/(1+exp(-u)) evaluated by a fixed sequence of fp32 ops."""
+    u = np.asarray(u, dtype=F32)
+    v = -u
+    out = np.empty_like(v)
+    big = v > F32(87.0)          # exp(v) would leave the normal range: result 0
+    small = v < F32(-20.0)       # 1 + exp(v) rounds to 1: result 1
+    mid = ~(big | small)
+    out[big] = F32(0.0)
+    out[small] = F32(1.0)
+    vm = v[mid]
+    n = np.rint(vm * LOG2E_F32)
+    r = (vm - n * LN2_HI) - n * LN2_LO
+    p = np.full_like(vm, INV_FACT[7])
+    for k in range(6, -1, -1):
+        p = p * r
+        p = p + INV_FACT[k]
+    e = np.ldexp(p, n.astype(np.int32)).astype(F32)
+    out[mid] = F32(1.0) / (F32(1.0) + e)
+    return out
+
+
+def router_logits(x, w_router) -> np.ndarray:
+    """u[t,e] = sum_j x[t,j] * Wr[e,j] in fp64, rounded once to fp32.
+
+    The gating module stays in high precision while the GEMMs go to FP8
+    [MH §4.1]; here the router product is exact up to fp64 rounding.
+    """
+    x64 = np.asarray(x, dtype=F64)
+    w64 = np.asarray(w_router, dtype=F64)
+    return (x64 @ w64.T).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+class RouteResult:
+    """topk_idx [T,K] int32 (slot order = biased score descending), topk_gate
+    [T,K] fp32, near_tie [T] bool, plus the fp32 scores for inspection."""
+
+    def __init__(self, idx, gate, near_tie, s, c, group_scores):
+        self.idx = idx
+        self.gate = gate
+        self.near_tie = near_tie
+        self.s = s
+        self.c = c
+        self.group_scores = group_scores
+
+
+def _desc_order(vals: np.ndarray) -> np.ndarray:
+    """Indices sorted by value descending, ties to the lower index."""
+    ids = np.arange(vals.shape[0])
+    return np.lexsort((ids, -vals))
+
+
+def route(logits, bias, top_k: int, n_groups: int = 1, topk_groups: int = 1,
+          group_topn: int = 2, eps: float = 1e-6) -> RouteResult:
+    """Selection and gate values for every token.
+
+    1. s = sigmoid(u) [KY]; c = s + b, the bias used for routing only
+       [GK Q3; MH §1.2].
+    2. With G > 1 groups of E/G consecutive experts: group score = fp32 sum of
+       the ``group_topn`` largest c of the group, largest first; the
+       ``topk_groups`` best groups stay eligible (node-limited routing, at most
+       4 of 8 nodes [MH §3.1]).
+    3. The K largest c among eligible experts, in descending order, ties to
+       the lower id [WX §二(一)].
+    4. Gates: the selected unbiased s, divided by their fp32 sum taken in slot
+       order [KY]; the bias never enters [GK Q3]. A zero sum gives 1/K.
+    5. Near tie: fl32(c_(K) - c_(K+1)) <= fl32(eps) among eligible experts, or
+       the same between the M-th and (M+1)-th group score.
+    """
+    u = np.asarray(logits, dtype=F32)
+    b = np.asarray(bias, dtype=F32)
+    T, E = u.shape
+    K, G, M = int(top_k), int(n_groups), int(topk_groups)
+    assert E % G == 0 and 1 <= M <= G and K <= M * (E // G)
+    GS = E // G
+    eps32 = F32(eps)
+    s = sigmoid_f32(u)
+    c = (s + b[None, :]).astype(F32)
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), F32)
+    near = np.zeros(T, bool)
+    gsc = np.zeros((T, G), F32)
+    for t in range(T):
+        ct = c[t]
+        if G > 1:
+            gs = np.empty(G, F32)
+            for g in range(G):
+                top = np.sort(ct[g * GS:(g + 1) * GS])[::-1][:group_topn]
+                acc = F32(top[0])
+                for v in top[1:]:
+                    acc = F32(acc + v)
+                gs[g] = acc
+            gsc[t] = gs
+            gord = _desc_order(gs)
+            allowed = np.sort(gord[:M])
+            if G > M and F32(gs[gord[M - 1]] - gs[gord[M]]) <= eps32:
+                near[t] = True
+            elig = np.concatenate([np.arange(g * GS, (g + 1) * GS) for g in allowed])
+        else:
+            elig = np.arange(E)
+        order = elig[_desc_order(ct[elig])]
+        sel = order[:K]
+        if order.shape[0] > K and F32(ct[order[K - 1]] - ct[order[K]]) <= eps32:
+            near[t] = True
+        idx[t] = sel
+        ssum = F32(s[t, sel[0]])
+        for k in range(1, K):
+            ssum = F32(ssum + s[t, sel[k]])
+        if ssum == F32(0.0):
+            gate[t] = F32(1.0) / F32(K)
+        else:
+            gate[t] = (s[t, sel] / ssum).astype(F32)
+    return RouteResult(idx, gate, near, s, c, gsc)
+
+
+class PermuteResult:
+    """counts [E], offsets [E+1], perm [T*K] (token ids, expert-major, token
+    ascending inside an expert), inv [T,K] (position of pair (t,k) in perm)."""
+
+    def __init__(self, counts, offsets, perm, inv):
+        self.counts = counts
+        self.offsets = offsets
+        self.perm = perm
+        self.inv = inv
+
+
+def permute(topk_idx, n_experts: int) -> PermuteResult:
+    """Per-expert token segments sized to the data routed to each expert
+    (memory opened for the data actually sent [MH §3.1]); a stable counting
+    sort of the (t,k) pairs by expert, written as plain loops."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    E = int(n_experts)
+    buckets = [[] for _ in range(E)]
+    for t in range(T):
+        for k in range(K):
+            buckets[idx[t, k]].append((t, k))
+    counts = np.array([len(bk) for bk in buckets], np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    perm = np.empty(T * K, np.int32)
+    inv = np.empty((T, K), np.int32)
+    pos = 0
+    for e in range(E):
+        for (t, k) in buckets[e]:
+            perm[pos] = t
+            inv[t, k] = pos
+            pos += 1
+    return PermuteResult(counts, offsets, perm, inv)
+
+
+def bias_update(bias, counts, gamma: float, n_tokens: int, top_k: int) -> np.ndarray:
+    """b[e] -= gamma if expert e is overloaded, += gamma if underloaded [KY],
+    once per step [MH §1.2]. Load = tokens routed to e in this step; the
+    balanced load is T*K/E, compared exactly as counts[e]*E vs T*K. gamma is
+    applied in fp32."""
+    b = np.array(bias, dtype=F32, copy=True)
+    E = b.shape[0]
+    g32 = F32(gamma)
+    total = int(n_tokens) * int(top_k)
+    for e in range(E):
+        load = int(counts[e]) * E
+        if load > total:
+            b[e] = F32(b[e] - g32)
+        elif load < total:
+            b[e] = F32(b[e] + g32)
+    return b
+
+
+# ---------------------------------------------------------------------------
+# Experts (fp64)
+# ---------------------------------------------------------------------------
+def _silu64(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(X, w13, w2) -> np.ndarray:
+    """FFN expert [KY: experts are FFNs] in SwiGLU form, fp64:
+    W2 @ (silu(W1 v) * (W3 v)), with w13 = [W1; W3] stacked as [2I, d]
+    and w2 = [d, I]."""
+    X = np.asarray(X, dtype=F64)
+    w13 = np.asarray(w13, dtype=F64)
+    w2 = np.asarray(w2, dtype=F64)
+    inter = w13.shape[0] // 2
+    a = X @ w13[:inter].T
+    b = X @ w13[inter:].T
+    return (_silu64(a) * b) @ w2.T
+
+
+def layer_output(x, topk_idx, topk_gate, w13, w2, ws13=None, ws2=None) -> np.ndarray:
+    """y_t = FFN_shared(x_t) + sum_k g[t,k] * FFN_{idx[t,k]}(x_t), in fp64.
+
+    The shared expert processes every token, ungated [MH §1.1]. ``w13[e]`` and
+    ``w2[e]`` may be any indexable container (arrays, lazy loaders)."""
+    x = np.asarray(x, dtype=F64)
+    idx = np.asarray(topk_idx)
+    g = np.asarray(topk_gate, dtype=F64)
+    T = x.shape[0]
+    y = np.zeros((T, x.shape[1]), F64)
+    if ws13 is not None:
+        y += swiglu_expert(x, ws13, ws2)
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        ye = swiglu_expert(x[rows], w13[int(e)], w2[int(e)])
+        for i in range(rows.shape[0]):
+            y[rows[i]] += g[rows[i], slots[i]] * ye[i]
+    return y
+
+
+def forward(x, w_router, bias, w13, w2, ws13, ws2, top_k, n_groups=1,
+            topk_groups=1, group_topn=2, logits=None, eps=1e-6):
+    """Whole layer: routing (from ``logits`` when given, else from the fp64
+    router product), counting sort and fp64 outputs. Returns
+    (y fp64, RouteResult, PermuteResult). The bias is not updated here."""
+    u = router_logits(x, w_router) if logits is None else np.asarray(logits, F32)
+    rr = route(u, bias, top_k, n_groups, topk_groups, group_topn, eps)
+    pr = permute(rr.idx, u.shape[1])
+    y = layer_output(x, rr.idx, rr.gate, w13, w2, ws13, ws2)
+    return y, rr, pr
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+def round_bf16(v) -> np.ndarray:
+    """Round to bfloat16 (8 significant bits), nearest-even, returned as fp32.
+    Normal range only (outputs here are far from over/underflow)."""
+    v = np.asarray(v, dtype=F64)
+    m, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0) / 256.0          # keep 8 significant bits
+    return np.ldexp(q, e).astype(F32)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """OCP E4M3FN (the forward-pass FP8 format): 1 sign, 4 exponent (bias 7),
+    3 mantissa bits; no infinities; S.1111.111 is NaN; max 448."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    mant = c & 0x7
+    val = np.where(ex == 0, mant / 8.0 * 2.0 ** -6,
+                   (1.0 + mant / 8.0) * np.exp2(ex - 7.0))
+    val = np.where((ex == 15) & (mant == 7), np.nan, val)
+    return (sign * val).astype(F32)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0, 127, dtype=np.uint8)).astype(F64)  # codes 0..126, ascending
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3FN code, ties to the even code (mantissa LSB 0); magnitudes
+    beyond 448 saturate to 448; the sign bit follows the input's sign."""
+    v = np.asarray(v, dtype=F32)
+    a = np.abs(v).astype(F64)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= _E4M3_POS[126], 126, code)           # saturate
+    code = np.where(a == _E4M3_POS[hi], hi, code)              # exact hits
+    code = code.astype(np.uint8)
+    code = np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+    return code
+
+
+def _quant_block(vals: np.ndarray):
+    """One scaling group: online max-abs [MH §4.1]; scale = amax/448; codes of
+    fl32(v * fl32(448/amax)). An all-zero group gets scale 1 and code 0."""
+    amax = F32(np.max(np.abs(vals))) if vals.size else F32(0.0)
+    if amax == F32(0.0):
+        return np.zeros(vals.shape, np.uint8), F32(1.0)
+    inv = F32(F32(448.0) / amax)
+    q = e4m3_encode((vals.astype(F32) * inv).astype(F32))
+    return q, F32(amax / F32(448.0))
+
+
+def quantize_rows_1x128(X):
+    """Activation tiles: 1 x 128 per token along the channel axis [GK Q8;
+    MH §4.1]. X [n, D] with D % 128 == 0 -> (codes uint8 [n, D],
+    scales fp32 [n, D/128])."""
+    X = np.asarray(X, dtype=F32)
+    n, D = X.shape
+    q = np.empty((n, D), np.uint8)
+    s = np.empty((n, D // 128), F32)
+    for i in range(n):
+        for j in range(D // 128):
+            q[i, j * 128:(j + 1) * 128], s[i, j] = _quant_block(X[i, j * 128:(j + 1) * 128])
+    return q, s
+
+
+def quantize_blocks_128(W):
+    """Weight blocks: 128 output rows x 128 input columns [GK Q8; MH §4.1].
+    W [R, C] with R, C % 128 == 0 -> (codes [R, C], scales [R/128, C/128])."""
+    W = np.asarray(W, dtype=F32)
+    R, C = W.shape
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((R // 128, C // 128), F32)
+    for i in range(R // 128):
+        for j in range(C // 128):
+            blk = W[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], s[i, j] = _quant_block(blk)
+    return q, s
+
+
+def dequant_rows_1x128(q, s) -> np.ndarray:
+    v = e4m3_decode(q).astype(F64)
+    return v * np.repeat(np.asarray(s, F64), 128, axis=1)
+
+
+def dequant_blocks_128(q, s) -> np.ndarray:
+    v = e4m3_decode(q).astype(F64)
+    sc = np.repeat(np.repeat(np.asarray(s, F64), 128, axis=0), 128, axis=1)
+    return v * sc
+
+
+def _fp8_expert(Xd, w13q, w13s, w2q, w2s):
+    """One expert in the FP8 scheme: fp64 products of dequantized e4m3 values
+    (fp32 accumulation in place of the 14-bit tensor-core sum [MH §4.1; KY]);
+    H rounded to fp32 and re-quantized in 1x128 tiles before the down GEMM."""
+    W13 = dequant_blocks_128(w13q, w13s)
+    W2 = dequant_blocks_128(w2q, w2s)
+    inter = W13.shape[0] // 2
+    H = (_silu64(Xd @ W13[:inter].T) * (Xd @ W13[inter:].T)).astype(F32)
+    hq, hs = quantize_rows_1x128(H)
+    return dequant_rows_1x128(hq, hs) @ W2.T
+
+
+def layer_output_fp8(x, topk_idx, topk_gate, w13q, w13s, w2q, w2s,
+                     ws13q=None, ws13s=None, ws2q=None, ws2s=None) -> np.ndarray:
+    """FP8 forward of the layer outputs, fp64 result (round to bf16 after)."""
+    xq, xs = quantize_rows_1x128(np.asarray(x, F32))
+    Xd = dequant_rows_1x128(xq, xs)
+    idx = np.asarray(topk_idx)
+    g = np.asarray(topk_gate, dtype=F64)
+    y = np.zeros(Xd.shape, F64)
+    if ws13q is not None:
+        y += _fp8_expert(Xd, ws13q, ws13s, ws2q, ws2s)
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        e = int(e)
+        ye = _fp8_expert(Xd[rows], w13q[e], w13s[e], w2q[e], w2s[e])
+        for i in range(rows.shape[0]):
+            y[rows[i]] += g[rows[i], slots[i]] * ye[i]
+    return y
