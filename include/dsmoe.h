@@ -1,0 +1,223 @@
+/*
+ * dsmoe.h - C ABI of the DeepSeekMoE feed-forward layer for one MI355X (gfx950).
+ *
+ * The layer (sources are cited by page title and section):
+ *   - affinity s = sigmoid(x . Wr^T) per token and routed expert
+ *     (kaiyunto.com DeepSeek-V3 walkthrough, DeepSeekMoE paragraph);
+ *   - a per-expert bias b is added to s for SELECTION ONLY, never to the gate
+ *     values (gkm0120.cn DeepSeek-V3 notes, Q3; mhpq.cn "DeepSeek-V3 高效训练
+ *     关键技术全景解析" §1.2);
+ *   - optional group limit: experts form G groups (one per EP node), a token
+ *     may use only its best M groups (same article, §3.1: at most 4 nodes);
+ *   - top-K of (s + b) among eligible experts; gates = the selected s divided
+ *     by their sum (kaiyunto.com walkthrough);
+ *   - y = FFN_shared(x) + sum_k gate_k * FFN_{idx_k}(x), one always-on shared
+ *     expert plus K routed experts (mhpq.cn article §1.1); experts are SwiGLU
+ *     FFNs without biases;
+ *   - after each step, b[e] -= gamma for overloaded experts and += gamma for
+ *     underloaded ones (kaiyunto.com walkthrough; mhpq.cn §1.2);
+ *   - FP8 variant: E4M3 codes with max-abs scales per 1x128 activation tile
+ *     and per 128x128 weight block, fp32 accumulation (gkm0120.cn Q8;
+ *     mhpq.cn §4.1).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `desc`, `w` and `bytes` is a DEVICE
+ *     pointer. The caller owns every buffer. The library never allocates,
+ *     frees or synchronizes, and keeps no pointer after it returns.
+ *   - All work is enqueued on `stream` (NULL = the default stream) and runs
+ *     asynchronously. Outputs are fully overwritten, never accumulated into.
+ *   - Arguments are validated on the host BEFORE anything is enqueued; on an
+ *     error nothing is launched, outputs are untouched and a status other
+ *     than MOE_OK is returned; moe_last_error() then holds a message
+ *     (thread-local). No C++ exception crosses this boundary. Faults inside
+ *     kernels surface at the caller's next synchronization.
+ *   - Row-major layouts throughout; base pointers 16-byte aligned.
+ *   - Entry points are reentrant; calls that share output or workspace
+ *     buffers must not overlap in time.
+ */
+#ifndef DSMOE_H
+#define DSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSMOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size or relation      */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid but outside what the kernels do   */
+  MOE_ERR_MISALIGNED = 3,         /* a pointer is not 16-byte aligned        */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4,
+  MOE_ERR_HIP = 5                 /* a HIP launch or query failed            */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_DT_F32 = 0,
+  MOE_DT_BF16 = 1,
+  MOE_DT_FP8_E4M3 = 2             /* OCP E4M3FN: bias 7, max 448, no inf     */
+} moe_dtype;
+
+/* Shape and precision of one layer call.
+ *   T            tokens in the call (>= 0; 0 is a no-op)
+ *   d            hidden size
+ *   n_experts    E routed experts, 1..512
+ *   top_k        K routed experts per token, 1..min(E, 64)
+ *   n_groups     G expert groups (1 = no group limit); E % G == 0, G <= 64
+ *   topk_groups  M groups a token may use, 1..G; M*E/G >= K
+ *   group_topn   a group's score is the sum of its group_topn best biased
+ *                scores, 1..min(E/G, 8) (ignored when G == 1)
+ *   inter        I, intermediate size of every routed expert
+ *   shared_inter Is, intermediate size of the shared expert (0 = none)
+ *   act_dtype    dtype of x and y: MOE_DT_F32 or MOE_DT_BF16
+ *   w_dtype      expert weights: MOE_DT_F32 (with act F32), MOE_DT_BF16 or
+ *                MOE_DT_FP8_E4M3 (both with act BF16)
+ *   near_tie_eps a token counts as a near tie when the K-th and (K+1)-th
+ *                biased scores of eligible experts differ by <= eps, or the
+ *                M-th and (M+1)-th group scores do (fp32 difference).
+ * Divisibility: d, I, Is multiples of 64 for BF16/F32 weights and of 128 for
+ * FP8 weights. The router weights and bias are always fp32. */
+typedef struct moe_layer_desc {
+  int64_t T;
+  int32_t d;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_groups;
+  int32_t topk_groups;
+  int32_t group_topn;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t act_dtype;
+  int32_t w_dtype;
+  float near_tie_eps;
+} moe_layer_desc;
+
+/* Expert weights (device pointers, w_dtype elements, row-major):
+ *   w13  [E, 2I, d]  rows 0..I-1 gate projection W1, rows I..2I-1 up W3
+ *   w2   [E, d, I]   down projection
+ *   ws13 [2Is, d], ws2 [d, Is]  shared expert (NULL when Is == 0)
+ * FP8 only, fp32 scales of the 128x128 blocks (128 output rows x 128 input
+ * columns), as written by moe_quantize_fp8_blocks:
+ *   w13_scale [E, 2I/128, d/128], w2_scale [E, d/128, I/128],
+ *   ws13_scale [2Is/128, d/128], ws2_scale [d/128, Is/128]. */
+typedef struct moe_weights {
+  const void* w13;
+  const void* w2;
+  const void* ws13;
+  const void* ws2;
+  const float* w13_scale;
+  const float* w2_scale;
+  const float* ws13_scale;
+  const float* ws2_scale;
+} moe_weights;
+
+/* Bytes of workspace that deepseek_moe_forward needs for `desc`; this also
+ * covers moe_gate, moe_route_from_logits and moe_expert_ffn. Host only. */
+moe_status moe_workspace_size(const moe_layer_desc* desc, size_t* bytes);
+
+/* Router and routing, steps affinity -> bias -> group limit -> top-K -> gates
+ * -> per-expert counts (sources above).
+ *   x          [T, d] act_dtype
+ *   w_router   [E, d] fp32;  bias [E] fp32
+ *   logits     [T, E] fp32 OUT, optional (NULL = kept in the workspace). The
+ *              router product is exact-input fp32 accumulation; the routing
+ *              that follows is a fixed sequence of IEEE fp32 operations, so
+ *              it is reproducible bit for bit from these logits.
+ *   topk_idx   [T, K] int32 OUT, slot order = biased score descending, ties
+ *              to the lower expert id
+ *   topk_gate  [T, K] fp32 OUT, gates in slot order (sum to 1)
+ *   counts     [E] int32 OUT, tokens routed to each expert
+ *   near_tie   [1] int32 OUT, optional: number of near-tie tokens
+ *   ws         workspace of >= moe_workspace_size bytes */
+moe_status moe_gate(const moe_layer_desc* desc, const void* x, const float* w_router,
+                    const float* bias, float* logits, int32_t* topk_idx, float* topk_gate,
+                    int32_t* counts, int32_t* near_tie, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* The routing half of moe_gate on caller-supplied fp32 logits [T, E]. */
+moe_status moe_route_from_logits(const moe_layer_desc* desc, const float* logits,
+                                 const float* bias, int32_t* topk_idx, float* topk_gate,
+                                 int32_t* counts, int32_t* near_tie, hipStream_t stream);
+
+/* Per-expert token segments sized to the routed data (mhpq.cn §3.1: memory
+ * opened for the data actually sent), by a stable counting sort.
+ *   topk_idx [T, K], counts [E] IN (from moe_gate)
+ *   offsets  [E+1] int32 OUT, exclusive prefix sum of counts
+ *   perm     [T*K] int32 OUT, token ids, expert-major, ascending token order
+ *            inside each expert
+ *   inv      [T, K] int32 OUT, position of pair (t, k) in perm
+ *   x        [T, d] act_dtype IN, only read when x_perm != NULL
+ *   x_perm   [T*K, d] OUT, optional: gathered rows x[perm]; with FP8 weights
+ *            these are E4M3 codes of 1x128 tiles and x_perm_scale [T*K, d/128]
+ *            fp32 receives their scales. */
+moe_status moe_permute(const moe_layer_desc* desc, const int32_t* topk_idx,
+                       const int32_t* counts, const void* x, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* x_perm, float* x_perm_scale, hipStream_t stream);
+
+/* Grouped expert FFNs: for every expert e, rows offsets[e]..offsets[e+1]-1
+ *   y_perm[r] = W2_e (silu(W1_e a_r) * (W3_e a_r)),
+ * with a_r = x_perm[r] when x_perm != NULL, else x[perm[r]]; and for every
+ * token y_shared[t] = the shared expert applied to x[t].
+ *   y_perm [T*K, d], y_shared [T, d] OUT: fp32 with F32 weights, else bf16.
+ *   With FP8 weights, x is quantized in 1x128 tiles, H in 1x128 tiles of the
+ *   intermediate axis; fp32 accumulation with the block scales applied per
+ *   128-wide slice of the contraction. */
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* w, const void* x,
+                          const int32_t* perm, const void* x_perm, const float* x_perm_scale,
+                          const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Gated combine: y[t] = y_shared[t] + sum_k topk_gate[t,k] * y_perm[inv[t,k]],
+ * fp32 accumulation in slot order, y in act_dtype. y_shared may be NULL
+ * (no shared expert). */
+moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int32_t* inv,
+                       const float* topk_gate, const void* y_shared, void* y,
+                       hipStream_t stream);
+
+/* Bias update from this step's loads (in place): with balanced load T*K/E,
+ * b[e] -= gamma if counts[e]*E > T*K, b[e] += gamma if counts[e]*E < T*K,
+ * unchanged otherwise; fp32 arithmetic. The only call that mutates an input. */
+moe_status moe_bias_update(const moe_layer_desc* desc, const int32_t* counts, float gamma,
+                           float* bias, hipStream_t stream);
+
+/* The whole layer: moe_gate, the counting sort, moe_expert_ffn (rows gathered
+ * from x inside the GEMM) and moe_combine, enqueued back to back. It does NOT
+ * update the bias: call moe_bias_update with `counts` afterwards.
+ *   y [T, d] act_dtype OUT; topk_idx, topk_gate, counts OUT as in moe_gate;
+ *   near_tie and logits optional OUT. */
+moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
+                                const float* w_router, const float* bias, const moe_weights* w,
+                                void* y, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                                int32_t* near_tie, float* logits, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* FP8 weight preparation, once per weight set: n_mats matrices [rows, cols]
+ * of `src_dtype` (MOE_DT_F32 or MOE_DT_BF16) -> E4M3 codes q (same shape) and
+ * fp32 scales [n_mats, rows/128, cols/128]. Per 128x128 block: amax = max|w|;
+ * amax == 0 gives scale 1 and zero codes; else scale = amax/448 and
+ * q = e4m3(w * (448/amax)), round to nearest even, saturating at 448
+ * (gkm0120.cn Q8; mhpq.cn §4.1). rows, cols multiples of 128. */
+moe_status moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t n_mats,
+                                   int32_t rows, int32_t cols, uint8_t* q, float* scale,
+                                   hipStream_t stream);
+
+/* The same rule on 1x128 tiles of each row: src [n, cols] -> q [n, cols],
+ * scale [n, cols/128]. cols a multiple of 128. */
+moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, int32_t cols,
+                                 uint8_t* q, float* scale, hipStream_t stream);
+
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSMOE_H */

@@ -1,0 +1,59 @@
+// Device helpers shared by the HIP kernels of the library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsmoe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// silu(z) = z * sigmoid(z) for the expert activations (tolerance-checked).
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// One E4M3FN code from an fp32 value already scaled into [-448, 448]: clamp
+// (saturation), then the hardware conversion, which rounds to nearest even.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Maps a physical workgroup id to a logical one so that logically adjacent
+// workgroups run on the same XCD (workgroups are dealt round-robin over the
+// 8 XCDs, each with its own L2). Requires gridDim.x % 8 == 0.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+  return (b & 7) * (nblocks >> 3) + (b >> 3);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace dsmoe

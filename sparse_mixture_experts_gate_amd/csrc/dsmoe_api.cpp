@@ -1,0 +1,586 @@
+// C ABI of the DeepSeekMoE layer: argument validation (host only, before any
+// launch), workspace carving and launch sequencing on the caller's stream.
+// The library never allocates, frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "dsmoe.h"
+#include "internal.h"
+
+using namespace dsmoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                     \
+  do {                                          \
+    hipError_t _e = (expr);                     \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+moe_status validate_desc(const moe_layer_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)d->T);
+  if (d->d <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "d = %d <= 0", d->d);
+  if (d->n_experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "n_experts = %d < 1", d->n_experts);
+  if (d->n_experts > 512)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts = %d > 512", d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "top_k = %d outside 1..n_experts", d->top_k);
+  if (d->top_k > 64) return fail(MOE_ERR_UNSUPPORTED, "top_k = %d > 64", d->top_k);
+  if (d->n_groups < 1 || d->n_experts % d->n_groups != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "n_groups = %d must divide n_experts = %d",
+                d->n_groups, d->n_experts);
+  if (d->n_groups > 64) return fail(MOE_ERR_UNSUPPORTED, "n_groups = %d > 64", d->n_groups);
+  if (d->topk_groups < 1 || d->topk_groups > d->n_groups)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "topk_groups = %d outside 1..n_groups",
+                d->topk_groups);
+  const int gs = d->n_experts / d->n_groups;
+  if (d->topk_groups * gs < d->top_k)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "topk_groups * group size = %d < top_k = %d",
+                d->topk_groups * gs, d->top_k);
+  if (d->n_groups > 1 && (d->group_topn < 1 || d->group_topn > gs || d->group_topn > 8))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "group_topn = %d outside 1..min(group size, 8)",
+                d->group_topn);
+  if (d->inter < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "inter = %d < 1", d->inter);
+  if (d->shared_inter < 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_inter = %d < 0", d->shared_inter);
+  if (!(d->near_tie_eps >= 0.0f) || !std::isfinite(d->near_tie_eps))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "near_tie_eps must be finite and >= 0");
+  const bool f32 = d->act_dtype == MOE_DT_F32 && d->w_dtype == MOE_DT_F32;
+  const bool bf16 = d->act_dtype == MOE_DT_BF16 && d->w_dtype == MOE_DT_BF16;
+  const bool fp8 = d->act_dtype == MOE_DT_BF16 && d->w_dtype == MOE_DT_FP8_E4M3;
+  if (!(f32 || bf16 || fp8))
+    return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", d->act_dtype,
+                d->w_dtype);
+  const int mult = fp8 ? 128 : 64;
+  if (d->d % mult || d->inter % mult || d->shared_inter % mult)
+    return fail(MOE_ERR_UNSUPPORTED, "d, inter, shared_inter must be multiples of %d", mult);
+  if (d->T * static_cast<int64_t>(d->top_k) + d->T >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1) must be < 2^31");
+  return MOE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  }
+};
+
+int io_bytes(const moe_layer_desc* d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
+int h_bytes(const moe_layer_desc* d) {
+  return d->w_dtype == MOE_DT_F32 ? 4 : d->w_dtype == MOE_DT_BF16 ? 2 : 1;
+}
+
+struct GateLayout {
+  int splits;
+  size_t partial, wsplit, ntie, bytes;
+};
+
+GateLayout gate_layout(const moe_layer_desc* d) {
+  GateLayout L{};
+  const int E = d->n_experts;
+  L.splits = router_splits(d->T, d->d, E, d->act_dtype);
+  Carver c;
+  L.partial = c.take(sizeof(float) * size_t(L.splits) * size_t(d->T) * E);
+  L.wsplit = c.take(d->act_dtype == MOE_DT_BF16 ? size_t(E) * 3 * d->d * 2 : 0);
+  L.ntie = c.take(sizeof(int32_t));
+  L.bytes = c.off;
+  return L;
+}
+
+struct FfnLayout {
+  GemmTiling tiling;
+  int ldh;
+  int64_t max_tiles1, max_tiles2;
+  size_t tiles1, tiles2, tmap1, tmap2, xq, xs, H, Hs, bytes;
+};
+
+FfnLayout ffn_layout(const moe_layer_desc* d) {
+  FfnLayout L{};
+  const int64_t T = d->T, TK = d->T * d->top_k;
+  const int E = d->n_experts;
+  L.tiling = choose_tiling(T, d->top_k, E, d->w_dtype);
+  L.ldh = std::max(d->inter, d->shared_inter);
+  const GemmTiling& t = L.tiling;
+  const int64_t nt1 = (d->inter + t.bnh1 - 1) / t.bnh1;
+  const int64_t nts1 = (d->shared_inter + t.bnh1 - 1) / t.bnh1;
+  const int64_t nt2 = (d->d + t.bn2 - 1) / t.bn2;
+  // sum_e ceil(c_e / bm) <= TK / bm + E (rounded up)
+  L.max_tiles1 = ((TK + t.bm1 - 1) / t.bm1 + E) * nt1 + ((T + t.bm1 - 1) / t.bm1) * nts1;
+  L.max_tiles2 = ((TK + t.bm2 - 1) / t.bm2 + E) * nt2 +
+                 (d->shared_inter > 0 ? ((T + t.bm2 - 1) / t.bm2) * nt2 : 0);
+  Carver c;
+  L.tiles1 = c.take(sizeof(int32_t) * (E + 2));
+  L.tiles2 = c.take(sizeof(int32_t) * (E + 2));
+  L.tmap1 = c.take(sizeof(int32_t) * size_t(L.max_tiles1));
+  L.tmap2 = c.take(sizeof(int32_t) * size_t(L.max_tiles2));
+  const bool fp8 = d->w_dtype == MOE_DT_FP8_E4M3;
+  L.xq = c.take(fp8 ? size_t(T) * d->d : 0);
+  L.xs = c.take(fp8 ? sizeof(float) * size_t(T) * (d->d / 128) : 0);
+  const int64_t hrows = TK + (d->shared_inter > 0 ? T : 0);
+  L.Hs = c.take(fp8 ? sizeof(float) * size_t(hrows) * (L.ldh / 128) : 0);
+  L.H = c.take(size_t(hrows) * L.ldh * h_bytes(d));
+  L.bytes = c.off;
+  return L;
+}
+
+struct FwdLayout {
+  GateLayout gate;
+  FfnLayout ffn;
+  size_t gate_base, ffn_base, offsets, perm, inv, yperm, yshared, bytes;
+};
+
+FwdLayout fwd_layout(const moe_layer_desc* d) {
+  FwdLayout L{};
+  L.gate = gate_layout(d);
+  L.ffn = ffn_layout(d);
+  const int64_t T = d->T, TK = d->T * d->top_k;
+  Carver c;
+  L.gate_base = c.take(L.gate.bytes);
+  L.ffn_base = c.take(L.ffn.bytes);
+  L.offsets = c.take(sizeof(int32_t) * (d->n_experts + 1));
+  L.perm = c.take(sizeof(int32_t) * size_t(TK));
+  L.inv = c.take(sizeof(int32_t) * size_t(TK));
+  L.yperm = c.take(size_t(TK) * d->d * io_bytes(d));
+  L.yshared = c.take(d->shared_inter > 0 ? size_t(T) * d->d * io_bytes(d) : 0);
+  L.bytes = c.off;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> req) {
+  for (auto& p : req) {
+    if (!p.first) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", p.second);
+    if (misaligned(p.first)) return fail(MOE_ERR_MISALIGNED, "%s is not 16-byte aligned", p.second);
+  }
+  return MOE_OK;
+}
+
+moe_status check_opt(std::initializer_list<std::pair<const void*, const char*>> opt) {
+  for (auto& p : opt)
+    if (p.first && misaligned(p.first))
+      return fail(MOE_ERR_MISALIGNED, "%s is not 16-byte aligned", p.second);
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_layer_desc* d, const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
+  moe_status st = check_ptrs({{w->w13, "w13"}, {w->w2, "w2"}});
+  if (st) return st;
+  if (d->shared_inter > 0) {
+    st = check_ptrs({{w->ws13, "ws13"}, {w->ws2, "ws2"}});
+    if (st) return st;
+  }
+  if (d->w_dtype == MOE_DT_FP8_E4M3) {
+    st = check_ptrs({{w->w13_scale, "w13_scale"}, {w->w2_scale, "w2_scale"}});
+    if (st) return st;
+    if (d->shared_inter > 0) {
+      st = check_ptrs({{w->ws13_scale, "ws13_scale"}, {w->ws2_scale, "ws2_scale"}});
+      if (st) return st;
+    }
+  }
+  return MOE_OK;
+}
+
+// T == 0: the only outputs are the per-expert counts (all zero) and the
+// near-tie count (zero); T-sized pointers may be NULL.
+moe_status zero_counts(const moe_layer_desc* d, int32_t* counts, int32_t* near_tie,
+                       hipStream_t s) {
+  moe_status st = check_ptrs({{counts, "counts"}});
+  if (st) return st;
+  st = check_opt({{near_tie, "near_tie"}});
+  if (st) return st;
+  HIP_TRY(launch_fill_i32(counts, d->n_experts, 0, s), "zero counts");
+  if (near_tie) HIP_TRY(launch_fill_i32(near_tie, 1, 0, s), "zero near_tie");
+  return MOE_OK;
+}
+
+RouteParams route_params(const moe_layer_desc* d) {
+  RouteParams p;
+  p.T = d->T;
+  p.E = d->n_experts;
+  p.K = d->top_k;
+  p.G = d->n_groups;
+  p.M = d->n_groups > 1 ? d->topk_groups : 1;
+  p.topn = d->n_groups > 1 ? d->group_topn : 1;
+  p.eps = d->near_tie_eps;
+  return p;
+}
+
+PlanParams plan_params(const moe_layer_desc* d, const GemmTiling& t) {
+  PlanParams p;
+  p.T = d->T;
+  p.E = d->n_experts;
+  p.K = d->top_k;
+  p.d = d->d;
+  p.I = d->inter;
+  p.Is = d->shared_inter;
+  p.bm1 = t.bm1;
+  p.bnh1 = t.bnh1;
+  p.bm2 = t.bm2;
+  p.bn2 = t.bn2;
+  return p;
+}
+
+// Router + routing on a validated call; ws points at a GateLayout region.
+moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_router,
+                    const float* bias, float* logits, int32_t* idx, float* gate, int32_t* counts,
+                    int32_t* near_tie, void* ws, const GateLayout& L, hipStream_t s) {
+  int32_t* ntie = near_tie ? near_tie : at<int32_t>(ws, L.ntie);
+  HIP_TRY(launch_fill_i32(counts, d->n_experts, 0, s), "zero counts");
+  HIP_TRY(launch_fill_i32(ntie, 1, 0, s), "zero near_tie");
+  if (d->T == 0) return MOE_OK;
+  float* partial = at<float>(ws, L.partial);
+  if (d->act_dtype == MOE_DT_F32)
+    HIP_TRY(launch_router_f32(static_cast<const float*>(x), w_router, d->T, d->d, d->n_experts,
+                              partial, s),
+            "router (fp32)");
+  else
+    HIP_TRY(launch_router_logits_bf16(x, w_router, d->T, d->d, d->n_experts, L.splits,
+                                      at<uint16_t>(ws, L.wsplit), partial, s),
+            "router (bf16)");
+  HIP_TRY(launch_route(partial, L.splits, logits, bias, route_params(d), idx, gate, counts, ntie,
+                       s),
+          "route");
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
+                   const int32_t* perm, const void* x_perm, const float* x_perm_scale,
+                   const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
+                   const FfnLayout& L, bool offsets_ready_tiles, hipStream_t s) {
+  (void)offsets_ready_tiles;
+  if (d->T == 0) return MOE_OK;
+  int32_t* tiles1 = at<int32_t>(ws, L.tiles1);
+  int32_t* tiles2 = at<int32_t>(ws, L.tiles2);
+  int32_t* tmap1 = at<int32_t>(ws, L.tmap1);
+  int32_t* tmap2 = at<int32_t>(ws, L.tmap2);
+  FfnArgs a{};
+  a.offsets = offsets;
+  a.tiles1 = tiles1;
+  a.tiles2 = tiles2;
+  a.tmap1 = tmap1;
+  a.tmap2 = tmap2;
+  a.T = d->T;
+  a.TK = d->T * d->top_k;
+  a.E = d->n_experts;
+  a.d = d->d;
+  a.I = d->inter;
+  a.Is = d->shared_inter;
+  a.ldh = L.ldh;
+  a.perm = x_perm ? nullptr : perm;
+  a.xperm = x_perm;
+  a.xperm_scale = x_perm_scale;
+  a.w13 = w->w13;
+  a.ws13 = w->ws13;
+  a.w13_scale = w->w13_scale;
+  a.ws13_scale = w->ws13_scale;
+  a.w2 = w->w2;
+  a.ws2 = w->ws2;
+  a.w2_scale = w->w2_scale;
+  a.ws2_scale = w->ws2_scale;
+  a.H = at<void>(ws, L.H);
+  a.H_scale = at<float>(ws, L.Hs);
+  a.yperm = y_perm;
+  a.yshared = y_shared;
+  HIP_TRY(launch_plan(nullptr, offsets, nullptr, tiles1, tiles2, tmap1, tmap2,
+                      plan_params(d, L.tiling), s),
+          "plan");
+  if (d->w_dtype == MOE_DT_FP8_E4M3) {
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    float* xs = at<float>(ws, L.xs);
+    HIP_TRY(launch_quant_rows(x, MOE_DT_BF16, nullptr, d->T, d->d, xq, xs, s), "quantize x");
+    a.x = xq;
+    a.x_scale = xs;
+    HIP_TRY(launch_ffn_fp8(a, L.tiling, s), "expert ffn (fp8)");
+  } else {
+    a.x = x;
+    if (d->w_dtype == MOE_DT_BF16)
+      HIP_TRY(launch_ffn_bf16(a, L.tiling, s), "expert ffn (bf16)");
+    else
+      HIP_TRY(launch_ffn_f32(a, s), "expert ffn (fp32)");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return DSMOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_workspace_size(const moe_layer_desc* desc, size_t* bytes) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = fwd_layout(desc).bytes;
+  return MOE_OK;
+}
+
+moe_status moe_gate(const moe_layer_desc* desc, const void* x, const float* w_router,
+                    const float* bias, float* logits, int32_t* topk_idx, float* topk_gate,
+                    int32_t* counts, int32_t* near_tie, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  if (desc->T == 0) return zero_counts(desc, counts, near_tie, stream);
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {bias, "bias"}, {topk_idx, "topk_idx"},
+                   {topk_gate, "topk_gate"}, {counts, "counts"}, {ws, "ws"}});
+  if (st) return st;
+  st = check_opt({{logits, "logits"}, {near_tie, "near_tie"}});
+  if (st) return st;
+  const GateLayout L = gate_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_gate needs %zu workspace bytes, got %zu",
+                L.bytes, ws_bytes);
+  return run_gate(desc, x, w_router, bias, logits, topk_idx, topk_gate, counts, near_tie, ws, L,
+                  stream);
+}
+
+moe_status moe_route_from_logits(const moe_layer_desc* desc, const float* logits,
+                                 const float* bias, int32_t* topk_idx, float* topk_gate,
+                                 int32_t* counts, int32_t* near_tie, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  if (desc->T == 0) return zero_counts(desc, counts, near_tie, stream);
+  st = check_ptrs({{logits, "logits"}, {bias, "bias"}, {topk_idx, "topk_idx"},
+                   {topk_gate, "topk_gate"}, {counts, "counts"}, {near_tie, "near_tie"}});
+  if (st) return st;
+  HIP_TRY(launch_fill_i32(counts, desc->n_experts, 0, stream), "zero counts");
+  HIP_TRY(launch_fill_i32(near_tie, 1, 0, stream), "zero near_tie");
+  if (desc->T == 0) return MOE_OK;
+  HIP_TRY(launch_route(logits, 1, nullptr, bias, route_params(desc), topk_idx, topk_gate, counts,
+                       near_tie, stream),
+          "route");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_layer_desc* desc, const int32_t* topk_idx,
+                       const int32_t* counts, const void* x, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* x_perm, float* x_perm_scale, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  if (desc->T == 0) {
+    st = check_ptrs({{offsets, "offsets"}});
+    if (st) return st;
+    HIP_TRY(launch_fill_i32(offsets, desc->n_experts + 1, 0, stream), "zero offsets");
+    return MOE_OK;
+  }
+  st = check_ptrs({{topk_idx, "topk_idx"}, {counts, "counts"}, {offsets, "offsets"},
+                   {perm, "perm"}, {inv, "inv"}});
+  if (st) return st;
+  if (x_perm) {
+    st = check_ptrs({{x, "x"}});
+    if (st) return st;
+    if (desc->w_dtype == MOE_DT_FP8_E4M3) {
+      st = check_ptrs({{x_perm_scale, "x_perm_scale"}});
+      if (st) return st;
+    }
+    st = check_opt({{x_perm, "x_perm"}});
+    if (st) return st;
+  }
+  PlanParams pp = plan_params(desc, choose_tiling(desc->T, desc->top_k, desc->n_experts,
+                                                  desc->w_dtype));
+  HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, nullptr, nullptr, pp, stream),
+          "offsets");
+  if (desc->T == 0) return MOE_OK;
+  HIP_TRY(launch_permute(topk_idx, offsets, desc->T, desc->top_k, desc->n_experts, perm, inv,
+                         stream),
+          "permute");
+  if (x_perm) {
+    const int64_t TK = desc->T * desc->top_k;
+    if (desc->w_dtype == MOE_DT_FP8_E4M3)
+      HIP_TRY(launch_quant_rows(x, MOE_DT_BF16, perm, TK, desc->d,
+                                static_cast<uint8_t*>(x_perm), x_perm_scale, stream),
+              "quantize gathered rows");
+    else
+      HIP_TRY(launch_gather_rows(x, desc->T, perm, TK, int64_t(desc->d) * io_bytes(desc), x_perm,
+                                 stream),
+              "gather rows");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* w, const void* x,
+                          const int32_t* perm, const void* x_perm, const float* x_perm_scale,
+                          const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (desc->T == 0) return MOE_OK;
+  st = check_ptrs({{x, "x"}, {offsets, "offsets"}, {y_perm, "y_perm"}, {ws, "ws"}});
+  if (st) return st;
+  if (!x_perm) {
+    st = check_ptrs({{perm, "perm"}});
+    if (st) return st;
+  } else if (desc->w_dtype == MOE_DT_FP8_E4M3) {
+    st = check_ptrs({{x_perm, "x_perm"}, {x_perm_scale, "x_perm_scale"}});
+    if (st) return st;
+  } else {
+    st = check_ptrs({{x_perm, "x_perm"}});
+    if (st) return st;
+  }
+  if (desc->shared_inter > 0) {
+    st = check_ptrs({{y_shared, "y_shared"}});
+    if (st) return st;
+  }
+  const FfnLayout L = ffn_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_expert_ffn needs %zu workspace bytes, got %zu",
+                L.bytes, ws_bytes);
+  return run_ffn(desc, w, x, perm, x_perm, x_perm_scale, offsets, y_perm, y_shared, ws, L, false,
+                 stream);
+}
+
+moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int32_t* inv,
+                       const float* topk_gate, const void* y_shared, void* y,
+                       hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  if (desc->T == 0) return MOE_OK;
+  st = check_ptrs({{y_perm, "y_perm"}, {inv, "inv"}, {topk_gate, "topk_gate"}, {y, "y"}});
+  if (st) return st;
+  st = check_opt({{y_shared, "y_shared"}});
+  if (st) return st;
+  HIP_TRY(launch_combine(y_perm, inv, topk_gate, desc->shared_inter > 0 ? y_shared : nullptr, y,
+                         desc->T, desc->top_k, desc->d, desc->act_dtype, stream),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_bias_update(const moe_layer_desc* desc, const int32_t* counts, float gamma,
+                           float* bias, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  st = check_ptrs({{counts, "counts"}, {bias, "bias"}});
+  if (st) return st;
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARGUMENT, "gamma must be finite");
+  HIP_TRY(launch_bias_update(counts, gamma, bias, desc->n_experts, desc->T, desc->top_k, stream),
+          "bias update");
+  return MOE_OK;
+}
+
+moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
+                                const float* w_router, const float* bias, const moe_weights* w,
+                                void* y, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                                int32_t* near_tie, float* logits, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (desc->T == 0) return zero_counts(desc, counts, near_tie, stream);
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {bias, "bias"}, {y, "y"},
+                   {topk_idx, "topk_idx"}, {topk_gate, "topk_gate"}, {counts, "counts"},
+                   {ws, "ws"}});
+  if (st) return st;
+  st = check_opt({{near_tie, "near_tie"}, {logits, "logits"}});
+  if (st) return st;
+  const FwdLayout L = fwd_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "deepseek_moe_forward needs %zu workspace bytes, got %zu", L.bytes, ws_bytes);
+  void* gws = at<void>(ws, L.gate_base);
+  void* fws = at<void>(ws, L.ffn_base);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  void* yperm = at<void>(ws, L.yperm);
+  void* yshared = desc->shared_inter > 0 ? at<void>(ws, L.yshared) : nullptr;
+  st = run_gate(desc, x, w_router, bias, logits, topk_idx, topk_gate, counts, near_tie, gws,
+                L.gate, stream);
+  if (st) return st;
+  if (desc->T == 0) return MOE_OK;
+  HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, nullptr, nullptr,
+                      plan_params(desc, L.ffn.tiling), stream),
+          "offsets");
+  HIP_TRY(launch_permute(topk_idx, offsets, desc->T, desc->top_k, desc->n_experts, perm, inv,
+                         stream),
+          "permute");
+  st = run_ffn(desc, w, x, perm, nullptr, nullptr, offsets, yperm, yshared, fws, L.ffn, true,
+               stream);
+  if (st) return st;
+  HIP_TRY(launch_combine(yperm, inv, topk_gate, yshared, y, desc->T, desc->top_k, desc->d,
+                         desc->act_dtype, stream),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t n_mats,
+                                   int32_t rows, int32_t cols, uint8_t* q, float* scale,
+                                   hipStream_t stream) {
+  if (src_dtype != MOE_DT_F32 && src_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "src_dtype %d not supported", src_dtype);
+  if (n_mats < 0 || rows < 0 || cols < 0 || rows % 128 || cols % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "rows and cols must be non-negative multiples of 128");
+  if (n_mats * (rows / 128) * int64_t(cols / 128) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  moe_status st = check_ptrs({{src, "src"}, {q, "q"}, {scale, "scale"}});
+  if (st) return st;
+  HIP_TRY(launch_quant_blocks(src, src_dtype, n_mats, rows, cols, q, scale, stream),
+          "quantize blocks");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, int32_t cols,
+                                 uint8_t* q, float* scale, hipStream_t stream) {
+  if (src_dtype != MOE_DT_F32 && src_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "src_dtype %d not supported", src_dtype);
+  if (n < 0 || cols < 0 || cols % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "cols must be a non-negative multiple of 128");
+  if ((n * (cols / 128) + 3) / 4 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "too many tiles");
+  moe_status st = check_ptrs({{src, "src"}, {q, "q"}, {scale, "scale"}});
+  if (st) return st;
+  HIP_TRY(launch_quant_rows(src, src_dtype, nullptr, n, cols, q, scale, stream), "quantize rows");
+  return MOE_OK;
+}
+
+}  // extern "C"

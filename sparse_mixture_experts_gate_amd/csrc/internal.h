@@ -1,0 +1,111 @@
+// Host-side interface between the C-ABI layer (dsmoe_api.cpp) and the HIP
+// kernel translation units. Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsmoe {
+
+// ---- routing (router.hip) --------------------------------------------------
+struct RouteParams {
+  int64_t T;
+  int E, K, G, M, topn;
+  float eps;
+};
+
+// Split of the router's contraction for the bf16 path (partials are summed
+// in a fixed order by the routing kernel). 1 for fp32 activations.
+int router_splits(int64_t T, int d, int E, int act_dtype);
+// fp32 activations: partial[0] = x . Wr^T with fp32 FMA accumulation.
+hipError_t launch_router_f32(const float* x, const float* w, int64_t T, int d, int E, float* out,
+                             hipStream_t s);
+// bf16 activations: Wr split into bf16 hi + mid + lo (wsplit [E, 3d]), then
+// `splits` partial sums [splits, T, E] of the exact products.
+hipError_t launch_router_logits_bf16(const void* x, const float* w_router, int64_t T, int d, int E,
+                                     int splits, uint16_t* wsplit, float* partial, hipStream_t s);
+hipError_t launch_route(const float* partial, int splits, float* logits_out, const float* bias,
+                        const RouteParams& p, int32_t* idx, float* gate, int32_t* counts,
+                        int32_t* near_tie, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// ---- planning and permutation (permute.hip) --------------------------------
+// Tile tables for the persistent grouped GEMMs: group g in [0, E) is routed
+// expert g, group E the shared expert; tiles[g] = first tile of group g.
+struct PlanParams {
+  int64_t T;
+  int E, K;
+  int d, I, Is;
+  int bm1, bnh1;  // GEMM1 rows per tile, intermediate columns per tile
+  int bm2, bn2;   // GEMM2 rows per tile, output columns per tile
+};
+// counts != NULL: offsets_out = exclusive scan of counts. Else offsets_in is
+// used. tiles1/tiles2 may be NULL.
+// tmap1/tmap2 receive the group of every tile (may be NULL).
+hipError_t launch_plan(const int32_t* counts, const int32_t* offsets_in, int32_t* offsets_out,
+                       int32_t* tiles1, int32_t* tiles2, int32_t* tmap1, int32_t* tmap2,
+                       const PlanParams& p, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, const int32_t* offsets, int64_t T, int K, int E,
+                          int32_t* perm, int32_t* inv, hipStream_t s);
+// dst[i, :] = src[perm[i], :] for i < n, rows of `row_bytes` bytes (multiple of
+// 16); ids outside [0, n_src) give zero rows.
+hipError_t launch_gather_rows(const void* src, int64_t n_src, const int32_t* perm, int64_t n,
+                              int64_t row_bytes, void* dst, hipStream_t s);
+
+// ---- grouped expert GEMMs ---------------------------------------------------
+struct FfnArgs {
+  const int32_t* offsets;  // [E+1]
+  const int32_t* tiles1;   // [E+2]
+  const int32_t* tiles2;   // [E+2]
+  const int32_t* tmap1;    // group of every GEMM1 tile
+  const int32_t* tmap2;    // group of every GEMM2 tile
+  int64_t T, TK;
+  int E, d, I, Is, ldh;
+  // GEMM1 inputs
+  const void* x;           // [T, d]; fp8: E4M3 codes
+  const float* x_scale;    // fp8: [T, d/128]
+  const int32_t* perm;     // gather rows of x for routed groups (NULL -> xperm)
+  const void* xperm;       // [TK, d] contiguous routed rows (used when perm == NULL)
+  const float* xperm_scale;
+  const void* w13;
+  const void* ws13;
+  const float* w13_scale;
+  const float* ws13_scale;
+  void* H;                 // [TK + T, ldh]
+  float* H_scale;          // fp8: [TK + T, ldh/128]
+  // GEMM2
+  const void* w2;
+  const void* ws2;
+  const float* w2_scale;
+  const float* ws2_scale;
+  void* yperm;             // [TK, d]
+  void* yshared;           // [T, d]
+};
+
+struct GemmTiling {
+  int bm1, bnh1, bm2, bn2;
+  int variant;  // kernel variant id, see gemm_bf16.hip / gemm_fp8.hip
+};
+
+GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype);
+hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s);
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s);
+
+// ---- elementwise (elementwise.hip) -----------------------------------------
+hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,
+                          const void* yshared, void* y, int64_t T, int K, int d, int io_dtype,
+                          hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, float gamma, float* bias, int E,
+                              int64_t T, int K, hipStream_t s);
+hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, int rows,
+                               int cols, uint8_t* q, float* scale, hipStream_t s);
+// Row i of the output quantizes source row perm[i] (perm == NULL: row i).
+hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm, int64_t n,
+                             int cols, uint8_t* q, float* scale, hipStream_t s);
+
+// number of compute units of the current device (cached per device)
+int device_cu_count();
+
+}  // namespace dsmoe

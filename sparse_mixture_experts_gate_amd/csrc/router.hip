@@ -1,0 +1,276 @@
+// Routing: sigmoid affinities, selection bias, group limit, top-K, gates,
+// per-expert counts and near-tie count (kaiyunto.com DeepSeek-V3 walkthrough,
+// DeepSeekMoE paragraph; gkm0120.cn notes Q3; mhpq.cn "DeepSeek-V3 高效训练
+// 关键技术全景解析" §1.2 and §3.1).
+//
+// Every routing decision is a fixed sequence of IEEE fp32 operations with no
+// contraction, so the result is reproducible bit for bit from the logits.
+// This file is compiled with -ffp-contract=off in addition to the pragma.
+#pragma clang fp contract(off)
+
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace dsmoe {
+
+namespace {
+
+// exp(v) = 2^n exp(r), n = rint(v log2 e), r = v - n ln2 in two pieces
+// (Cody-Waite; ln2_hi = 355/512 has 9 significant bits so n*ln2_hi is exact),
+// exp(r) from the degree-7 Taylor polynomial, Horner form.
+constexpr float kLog2e = 0x1.715476p+0f;
+constexpr float kLn2Hi = 0x1.63p-1f;
+constexpr float kLn2Lo = -0x1.bd0106p-13f;
+constexpr float kC0 = 1.0f, kC1 = 1.0f, kC2 = 0x1p-1f, kC3 = 0x1.555556p-3f,
+                kC4 = 0x1.555556p-5f, kC5 = 0x1.111112p-7f, kC6 = 0x1.6c16c2p-10f,
+                kC7 = 0x1.a01a02p-13f;
+
+__device__ __forceinline__ float sigmoid_ieee(float u) {
+  const float v = -u;
+  if (v > 87.0f) return 0.0f;   // exp(v) would leave the normal range
+  if (v < -20.0f) return 1.0f;  // 1 + exp(v) rounds to 1
+  const float n = __builtin_rintf(v * kLog2e);
+  const float r = (v - n * kLn2Hi) - n * kLn2Lo;
+  float p = kC7;
+  p = p * r; p = p + kC6;
+  p = p * r; p = p + kC5;
+  p = p * r; p = p + kC4;
+  p = p * r; p = p + kC3;
+  p = p * r; p = p + kC2;
+  p = p * r; p = p + kC1;
+  p = p * r; p = p + kC0;
+  const float e = __builtin_ldexpf(p, static_cast<int>(n));
+  return 1.0f / (1.0f + e);
+}
+
+// (value desc, index asc) total order; the best candidate wins.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(v, m, kWave);
+    const int oi = __shfl_xor(i, m, kWave);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+constexpr int kTokPerBlock = 4;  // one wave per token
+constexpr int kMaxE = 512;
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ partial, int splits,
+                                                    float* __restrict__ logits_out,
+                                                    const float* __restrict__ bias, RouteParams p,
+                                                    int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ gate_out,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ near_tie) {
+  __shared__ float c_lds[kTokPerBlock][kMaxE];
+  __shared__ float s_lds[kTokPerBlock][kMaxE];
+  __shared__ int hist[kMaxE];
+  __shared__ int ntie;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int E = p.E, K = p.K, G = p.G, M = p.M;
+  const int GS = E / G;
+  for (int e = tid; e < E; e += blockDim.x) hist[e] = 0;
+  if (tid == 0) ntie = 0;
+  __syncthreads();
+
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kTokPerBlock; base < p.T;
+       base += static_cast<int64_t>(gridDim.x) * kTokPerBlock) {
+    const int64_t t = base + wave;
+    const bool active = t < p.T;
+    float s[EPL], c[EPL];
+    bool taken[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + kWave * j;
+      taken[j] = false;
+      s[j] = 0.0f;
+      c[j] = -INFINITY;
+      if (active && e < E) {
+        const size_t off = static_cast<size_t>(t) * E + e;
+        float u = partial[off];
+        for (int q = 1; q < splits; ++q) u = u + partial[static_cast<size_t>(q) * p.T * E + off];
+        if (logits_out) logits_out[off] = u;
+        s[j] = sigmoid_ieee(u);
+        c[j] = s[j] + bias[e];
+        c_lds[wave][e] = c[j];
+        s_lds[wave][e] = s[j];
+      }
+    }
+    __syncthreads();
+
+    bool tie = false;
+    uint64_t allowed = ~0ull;  // bit g: group g eligible
+    if (G > 1 && active) {
+      // group score: fp32 sum of the group's topn best biased scores, largest first
+      float gsc = -INFINITY;
+      if (lane < G) {
+        float top[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) top[q] = -INFINITY;
+        for (int i = 0; i < GS; ++i) {
+          float v = c_lds[wave][lane * GS + i];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (q < p.topn && v > top[q]) { const float tmp = top[q]; top[q] = v; v = tmp; }
+          }
+        }
+        gsc = top[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q)
+          if (q < p.topn) gsc = gsc + top[q];
+      }
+      allowed = 0;
+      bool picked = false;
+      float last = 0.0f;
+      for (int q = 0; q < M; ++q) {
+        float bv = (lane < G && !picked) ? gsc : -INFINITY;
+        int bi = (lane < G && !picked) ? lane : 0x7fffffff;
+        wave_argmax(bv, bi);
+        allowed |= 1ull << bi;
+        if (lane == bi) picked = true;
+        last = bv;
+      }
+      if (G > M) {
+        float bv = (lane < G && !picked) ? gsc : -INFINITY;
+        int bi = (lane < G && !picked) ? lane : 0x7fffffff;
+        wave_argmax(bv, bi);
+        if (last - bv <= p.eps) tie = true;
+      }
+    }
+
+    bool elig[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + kWave * j;
+      elig[j] = e < E && ((allowed >> (e / GS)) & 1ull);
+    }
+
+    // top-K of the biased scores among eligible experts
+    int my_e = 0;
+    float my_s = 0.0f;
+    float ssum = 0.0f, last_c = 0.0f;
+    for (int k = 0; k <= K; ++k) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + kWave * j;
+        const bool ok = elig[j] && !taken[j];
+        if (ok && better(c[j], e, bv, bi)) { bv = c[j]; bi = e; }
+      }
+      wave_argmax(bv, bi);
+      if (k == K) {  // the (K+1)-th best, for the near-tie flag only
+        if (bi != 0x7fffffff && last_c - bv <= p.eps) tie = true;
+        break;
+      }
+      if (active) {
+        const float sw = s_lds[wave][bi];
+        ssum = (k == 0) ? sw : ssum + sw;
+        if (lane == k) { my_e = bi; my_s = sw; }
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (lane + kWave * j == bi) taken[j] = true;
+      last_c = bv;
+    }
+    if (active && lane < K) {
+      const float g = (ssum == 0.0f) ? 1.0f / static_cast<float>(K) : my_s / ssum;
+      idx_out[t * K + lane] = my_e;
+      gate_out[t * K + lane] = g;
+      atomicAdd(&hist[my_e], 1);
+    }
+    if (active && lane == 0 && tie) atomicAdd(&ntie, 1);
+    __syncthreads();
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  if (tid == 0 && ntie && near_tie) atomicAdd(near_tie, ntie);
+}
+
+// fp32 activations: plain fp32 dot products, one thread per (token, expert).
+__global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ w, int64_t T,
+                                                         int d, int E, float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = static_cast<int>(i % E);
+  const float* xr = x + t * d;
+  const float* wr = w + static_cast<int64_t>(e) * d;
+  float acc = 0.0f;
+  for (int k = 0; k < d; ++k) acc = __builtin_fmaf(xr[k], wr[k], acc);
+  out[i] = acc;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n,
+                     v);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const float* x, const float* w, int64_t T, int d, int E, float* out,
+                             hipStream_t s) {
+  const int64_t n = T * E;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     s, x, w, T, d, E, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const float* partial, int splits, float* logits_out, const float* bias,
+                        const RouteParams& p, int32_t* idx, float* gate, int32_t* counts,
+                        int32_t* near_tie, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  int64_t blocks = (p.T + kTokPerBlock - 1) / kTokPerBlock;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  if (blocks > cap) blocks = cap;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const int epl = (p.E + kWave - 1) / kWave;
+  if (epl <= 1)
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, partial, splits, logits_out, bias, p,
+                       idx, gate, counts, near_tie);
+  else if (epl <= 2)
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, partial, splits, logits_out, bias, p,
+                       idx, gate, counts, near_tie);
+  else if (epl <= 4)
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, partial, splits, logits_out, bias, p,
+                       idx, gate, counts, near_tie);
+  else
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, partial, splits, logits_out, bias, p,
+                       idx, gate, counts, near_tie);
+  return hipGetLastError();
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace dsmoe

@@ -1,0 +1,83 @@
+"""A DeepSeekMoE layer object over the C ABI: it owns the device weights (and
+their FP8 copies), allocates outputs and the workspace with torch, and calls
+the library. No arithmetic of the layer happens here."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+from .workloads import Workload
+
+_ACT = {"f32": L.MOE_DT_F32, "bf16": L.MOE_DT_BF16}
+_W = {"f32": L.MOE_DT_F32, "bf16": L.MOE_DT_BF16, "fp8": L.MOE_DT_FP8_E4M3}
+
+
+def make_desc(wl: Workload, T: int, near_tie_eps: float = 1e-6) -> L.MoeLayerDesc:
+    return L.MoeLayerDesc(T=T, d=wl.d, n_experts=wl.E, top_k=wl.K, n_groups=wl.G,
+                          topk_groups=wl.M, group_topn=wl.topn, inter=wl.I, shared_inter=wl.Is,
+                          act_dtype=_ACT[wl.act], w_dtype=_W[wl.w], near_tie_eps=near_tie_eps)
+
+
+def quantize_fp8_blocks(w: torch.Tensor):
+    """E4M3 codes and 128x128 block scales of w [n, rows, cols] (library)."""
+    shp = w.shape if w.dim() == 3 else (1, *w.shape)
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    s = torch.empty(shp[0], shp[1] // 128, shp[2] // 128, dtype=torch.float32, device=w.device)
+    L.moe_quantize_fp8_blocks(w.contiguous(), q, s)
+    if w.dim() == 2:
+        s = s[0]
+    return q, s
+
+
+class MoELayer:
+    def __init__(self, wl: Workload, params: dict):
+        self.wl = wl
+        self.w_router = params["w_router"]
+        self.bias = params["bias"].clone()
+        dev = self.w_router.device
+        if wl.w == "fp8":
+            self.w13, self.w13_scale = quantize_fp8_blocks(params["w13"])
+            self.w2, self.w2_scale = quantize_fp8_blocks(params["w2"])
+            self.ws13, self.ws13_scale = (quantize_fp8_blocks(params["ws13"]) if wl.Is else (None, None))
+            self.ws2, self.ws2_scale = (quantize_fp8_blocks(params["ws2"]) if wl.Is else (None, None))
+        else:
+            self.w13, self.w2 = params["w13"], params["w2"]
+            self.ws13, self.ws2 = params["ws13"], params["ws2"]
+            self.w13_scale = self.w2_scale = self.ws13_scale = self.ws2_scale = None
+        self.weights = L.make_weights(self.w13, self.w2, self.ws13, self.ws2, self.w13_scale,
+                                      self.w2_scale, self.ws13_scale, self.ws2_scale)
+        self._ws = torch.empty(0, dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def desc(self, T: int) -> L.MoeLayerDesc:
+        return make_desc(self.wl, T)
+
+    def workspace(self, T: int) -> torch.Tensor:
+        need = L.moe_workspace_size(self.desc(T))
+        if self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def alloc_outputs(self, T: int) -> dict:
+        wl, dev = self.wl, self.device
+        ydt = torch.float32 if wl.act == "f32" else torch.bfloat16
+        return {"y": torch.empty(T, wl.d, dtype=ydt, device=dev),
+                "topk_idx": torch.empty(T, wl.K, dtype=torch.int32, device=dev),
+                "topk_gate": torch.empty(T, wl.K, dtype=torch.float32, device=dev),
+                "counts": torch.empty(wl.E, dtype=torch.int32, device=dev),
+                "near_tie": torch.empty(1, dtype=torch.int32, device=dev),
+                "logits": torch.empty(T, wl.E, dtype=torch.float32, device=dev)}
+
+    def forward(self, x: torch.Tensor, out: dict | None = None, with_logits: bool = True,
+                stream=None) -> dict:
+        T = x.shape[0]
+        out = self.alloc_outputs(T) if out is None else out
+        ws = self.workspace(T)
+        L.deepseek_moe_forward(self.desc(T), x, self.w_router, self.bias, self.weights, out["y"],
+                               out["topk_idx"], out["topk_gate"], out["counts"], out["near_tie"],
+                               out["logits"] if with_logits else None, ws, stream)
+        return out
+
+    def bias_update(self, counts: torch.Tensor, T: int, gamma: float | None = None, stream=None):
+        L.moe_bias_update(self.desc(T), counts, self.wl.gamma if gamma is None else gamma,
+                          self.bias, stream)

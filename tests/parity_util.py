@@ -1,0 +1,40 @@
+"""Helpers shared by the GPU parity tests: host copies, the row-max relative
+error metric, lazy per-expert host views for the oracle."""
+import numpy as np
+import torch
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype in (torch.bfloat16, torch.float16, torch.float32, torch.float64):
+        return t.detach().float().cpu().numpy()
+    return t.detach().cpu().numpy()
+
+
+def row_rel_err(y, ref) -> float:
+    """max over rows of max|y - ref| / max|ref| (row-max-normalized)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(y - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((num / den).max())
+
+
+class LazyHost:
+    """Indexable host view of a device tensor [E, ...]: expert e is copied to
+    the host (as fp32) only when the oracle asks for it."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = host(self.t[e])
+        return self.cache[e]
+
+
+def route_args(wl):
+    return dict(top_k=wl.K, n_groups=wl.G, topk_groups=wl.M, group_topn=wl.topn)

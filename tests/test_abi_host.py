@@ -1,0 +1,124 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/dsmoe.h declares, and rejects bad arguments with the documented status
+before anything reaches a GPU (validation runs on the host first)."""
+import ctypes
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "libdsmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdsmoe.so not built")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_mixture_experts_gate_amd import _lib
+    return _lib
+
+
+def test_exports_every_declared_symbol(L):
+    names = L.header_symbols()
+    assert set(names) == {
+        "moe_workspace_size", "moe_gate", "moe_route_from_logits", "moe_permute",
+        "moe_expert_ffn", "moe_combine", "moe_bias_update", "deepseek_moe_forward",
+        "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
+        "moe_last_error", "moe_abi_version"}
+    so = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(so, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_abi_version_and_strings(L):
+    assert L.moe_abi_version() == 1
+    assert L.lib().moe_status_string(4) == b"workspace too small"
+
+
+def _desc(L, **kw):
+    base = dict(T=64, d=256, n_experts=16, top_k=2, n_groups=1, topk_groups=1, group_topn=2,
+                inter=128, shared_inter=128, act_dtype=L.MOE_DT_BF16, w_dtype=L.MOE_DT_BF16,
+                near_tie_eps=1e-6)
+    base.update(kw)
+    return L.MoeLayerDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), 1), (dict(d=0), 1), (dict(n_experts=0), 1), (dict(n_experts=600), 2),
+    (dict(top_k=0), 1), (dict(top_k=17), 1), (dict(n_groups=3), 1),
+    (dict(n_groups=4, topk_groups=5), 1), (dict(n_groups=8, topk_groups=1, top_k=3), 1),
+    (dict(n_groups=4, topk_groups=2, group_topn=5), 1), (dict(inter=0), 1),
+    (dict(shared_inter=-1), 1), (dict(act_dtype=0), 2), (dict(w_dtype=2, d=192), 2),
+    (dict(d=200), 2), (dict(inter=96), 2), (dict(near_tie_eps=float("nan")), 1),
+])
+def test_descriptor_validation(L, kw, status):
+    n = ctypes.c_size_t(0)
+    st = L.lib().moe_workspace_size(ctypes.byref(_desc(L, **kw)), ctypes.byref(n))
+    assert st == status, L.lib().moe_last_error()
+    assert L.lib().moe_last_error()
+
+
+def test_valid_descriptor_sizes(L):
+    n = ctypes.c_size_t(0)
+    d = _desc(L)
+    assert L.lib().moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # at least H and y_perm live in the workspace
+    assert n.value >= 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2
+    d0 = _desc(L, T=0)
+    assert L.lib().moe_workspace_size(ctypes.byref(d0), ctypes.byref(n)) == 0
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch(L):
+    lib = L.lib()
+    d = _desc(L)
+    P = ctypes.c_void_p
+    good = P(4096)
+    # moe_gate with a NULL x
+    st = lib.moe_gate(ctypes.byref(d), None, good, good, None, good, good, good, None, good, 1 << 30, None)
+    assert st == 1 and b"x is NULL" in lib.moe_last_error()
+    # misaligned topk_idx
+    st = lib.moe_gate(ctypes.byref(d), good, good, good, None, P(4100), good, good, None, good, 1 << 30, None)
+    assert st == 3
+    # permute without offsets
+    st = lib.moe_permute(ctypes.byref(d), good, good, None, None, good, good, None, None, None)
+    assert st == 1
+    # combine with NULL y
+    st = lib.moe_combine(ctypes.byref(d), good, good, good, None, None, None)
+    assert st == 1
+    # bias update with non-finite gamma
+    st = lib.moe_bias_update(ctypes.byref(d), good, ctypes.c_float(float("inf")), good, None)
+    assert st == 1
+    # expert ffn: missing weights struct
+    st = lib.moe_expert_ffn(ctypes.byref(d), None, good, good, None, None, good, good, good, good, 1 << 30, None)
+    assert st == 1
+    # quantizers: bad shapes / dtypes
+    assert lib.moe_quantize_fp8_blocks(good, 1, 1, 100, 128, good, good, None) == 1
+    assert lib.moe_quantize_fp8_blocks(good, 2, 1, 128, 128, good, good, None) == 2
+    assert lib.moe_quantize_fp8_rows(good, 1, 4, 130, good, good, None) == 1
+
+
+def test_workspace_too_small_rejected(L):
+    lib = L.lib()
+    d = _desc(L)
+    good = ctypes.c_void_p(4096)
+    w = L.MoeWeights(4096, 4096, 4096, 4096, None, None, None, None)
+    st = lib.deepseek_moe_forward(ctypes.byref(d), good, good, good, ctypes.byref(w), good, good,
+                                  good, good, None, None, good, 16, None)
+    assert st == 4 and b"workspace" in lib.moe_last_error()
+
+
+def test_product_path_has_no_oracle_import():
+    """The package must not reach the CPU oracle: no module under it imports it."""
+    pkg = os.path.join(ROOT, "sparse_mixture_experts_gate_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn
+    code = ("import sys; import sparse_mixture_experts_gate_amd as m; "
+            "assert 'oracle' not in sys.modules and not any(k.startswith('oracle.') for k in sys.modules)")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
