@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer on one MI355X.
+
+A step is one deepseek_moe_forward over one batch (router, routing, counting
+sort, grouped SwiGLU experts + shared expert, combine) plus the bias update,
+with the inputs resident in HBM. The default workload is the DeepSeek-V3-shaped
+prefill layer in bf16 (T=8192, d=7168, 256 routed experts, top-8 in 8 groups of
+32 with 4 groups per token, shared expert, intermediate 2048).
+
+Prints ONE JSON line on stdout (progress goes to stderr). Besides the contract
+fields it carries:
+  roofline      the dominant kernel (gate/up grouped GEMM): algorithmic bytes
+                and flops per launch over its mean duration, timed live with
+                HIP events recorded by the library on its own stream;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  extra         decode-sized batches (T = 16/64/256, HBM GB/s), the fp8 layer
+                and the stage breakdown.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12}
+STAGES = ["gate", "permute", "gemm_gate_up", "gemm_down", "combine"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def wsize(wl) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0}[wl.w]
+
+
+def algorithmic(wl, T: int, n_touched: int) -> dict:
+    """Algorithmic work per call: top-K sparse flops; every touched expert's
+    weights, the router weights, x in and y out once (no intermediates)."""
+    sw, sa = wsize(wl), (4.0 if wl.act == "f32" else 2.0)
+    TK = T * wl.K
+    w_routed = n_touched * 3.0 * wl.d * wl.I * sw
+    w_shared = 3.0 * wl.d * wl.Is * sw
+    layer_bytes = w_routed + w_shared + wl.E * wl.d * 4.0 + 2.0 * T * wl.d * sa
+    layer_flops = T * wl.flops_per_token
+    # gate/up grouped GEMM: its weights, x rows once, H written once
+    g1_flops = 4.0 * wl.d * (TK * wl.I + T * wl.Is)
+    g1_bytes = (n_touched * 2.0 * wl.I * wl.d + 2.0 * wl.Is * wl.d) * sw + T * wl.d * sa + \
+        (TK + T) * wl.I * (1.0 if wl.w == "fp8" else sa)
+    return {"layer_bytes": layer_bytes, "layer_flops": layer_flops,
+            "g1_bytes": g1_bytes, "g1_flops": g1_flops}
+
+
+def time_layer(layer, x, steps: int, warmup: int, bias_update: bool = True, stages: bool = True):
+    import torch
+    import sparse_mixture_experts_gate_amd as M
+    T = x.shape[0]
+    out = layer.alloc_outputs(T)
+    layer.workspace(T)
+    for _ in range(warmup):
+        layer.forward(x, out, with_logits=False)
+        if bias_update:
+            layer.bias_update(out["counts"], T)
+    torch.cuda.synchronize()
+    evs = []
+    if stages:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for row in evs:
+            for e in row:
+                e.record()  # materialize the underlying hipEvent
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        if stages:
+            M.moe_profile_events(evs[i])
+        layer.forward(x, out, with_logits=False)
+        if bias_update:
+            layer.bias_update(out["counts"], T)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if stages:
+        M.moe_profile_events(None)
+    res = {"wall_ms_per_step": wall * 1e3 / steps,
+           "gpu_ms_per_step": start.elapsed_time(end) / steps, "out": out}
+    if stages:
+        st = [[row[j].elapsed_time(row[j + 1]) for j in range(5)] for row in evs]
+        res["stage_ms"] = {name: sum(s[j] for s in st) / steps for j, name in enumerate(STAGES)}
+    return res
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM traffic measured by rocprofv3 counters for `kernel`, valid only while
+    the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(wl, P, n_tokens: int) -> dict:
+    """The CPU oracle, unchanged, on the first n_tokens tokens of the batch:
+    router product, routing and the fp64 experts. Weights of the experts those
+    tokens use are copied to the host before the clock starts."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    x = P["x"][:n_tokens].float().cpu().numpy()
+    wr = P["w_router"].cpu().numpy()
+    b = P["bias"].cpu().numpy()
+    u = O.router_logits(x, wr)
+    rr = O.route(u, b, wl.K, wl.G, wl.M, wl.topn)
+    need = np.unique(rr.idx)
+    w13 = {int(e): P["w13"][int(e)].float().cpu().numpy() for e in need}
+    w2 = {int(e): P["w2"][int(e)].float().cpu().numpy() for e in need}
+    ws13 = P["ws13"].float().cpu().numpy() if wl.Is else None
+    ws2 = P["ws2"].float().cpu().numpy() if wl.Is else None
+    t0 = time.perf_counter()
+    O.forward(x, wr, b, w13, w2, ws13, ws2, wl.K, wl.G, wl.M, wl.topn)
+    secs = time.perf_counter() - t0
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"value": n_tokens / secs, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle",
+            "sample": f"{n_tokens} tokens of {wl.name} (T={wl.T}), full oracle forward "
+                      f"(fp64 router product, routing, fp64 SwiGLU experts over the "
+                      f"{len(need)} experts they use + shared), {secs:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
+              "not part of this build (see DESIGN.md on sharding).", file=sys.stderr)
+        return 2
+
+    import torch
+    import sparse_mixture_experts_gate_amd as M
+    from sparse_mixture_experts_gate_amd.workloads import CONFIGS, make_inputs, make_tokens
+
+    wl = CONFIGS[args.workload]
+    dev = "cuda"
+    log(f"generating {wl.name} inputs")
+    P = make_inputs(wl, dev)
+    layer = M.MoELayer(wl, P)
+    log(f"timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    r = time_layer(layer, P["x"], args.steps, args.warmup)
+    counts = r["out"]["counts"].cpu()
+    n_touched = int((counts > 0).sum())
+    near = int(r["out"]["near_tie"].item())
+    ms = r["wall_ms_per_step"]
+    tok_s = wl.T / (ms / 1e3)
+    alg = algorithmic(wl, wl.T, n_touched)
+    g1_ms = r["stage_ms"]["gemm_gate_up"]
+    g1_bw = alg["g1_bytes"] / (g1_ms / 1e3)
+    g1_fl = alg["g1_flops"] / (g1_ms / 1e3)
+    bound = "hbm" if alg["g1_bytes"] / HBM_PEAK >= alg["g1_flops"] / MFMA_PEAK[wl.w] else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": g1_bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": g1_bw / HBM_PEAK}
+    else:
+        roof = {"bound": "mfma", "achieved": g1_fl / 1e12, "peak": MFMA_PEAK[wl.w] / 1e12,
+                "unit": "TFLOP/s", "frac": g1_fl / MFMA_PEAK[wl.w]}
+    roof.update({"kernel": "ffn1_bf16_kernel (grouped gate/up GEMM + SwiGLU)",
+                 "traffic": traffic_record("ffn1_bf16", wl.name),
+                 "ms_per_launch": g1_ms, "alg_bytes_per_launch": alg["g1_bytes"],
+                 "alg_flops_per_launch": alg["g1_flops"],
+                 "mfma_frac": g1_fl / MFMA_PEAK[wl.w], "hbm_frac": g1_bw / HBM_PEAK})
+    layer_mfma = alg["layer_flops"] / (ms / 1e3) / MFMA_PEAK[wl.w]
+    layer_hbm = alg["layer_bytes"] / (ms / 1e3) / HBM_PEAK
+    log(f"{wl.name}: {ms:.3f} ms/step, {tok_s/1e6:.3f} M tok/s, layer MFMA {layer_mfma:.1%}, "
+        f"HBM {layer_hbm:.1%}; stages {json.dumps({k: round(v, 3) for k, v in r['stage_ms'].items()})}")
+
+    extra = {"stage_ms": r["stage_ms"], "gpu_ms_per_step": r["gpu_ms_per_step"],
+             "layer_mfma_frac": layer_mfma, "layer_hbm_frac": layer_hbm,
+             "n_touched_experts": n_touched, "near_tie_tokens": near,
+             "near_tie_frac": near / wl.T, "max_over_mean_load": float(counts.max()) / (wl.T * wl.K / wl.E)}
+    if not args.no_extra and wl.name == "v3_prefill_bf16":
+        dec = {}
+        for T in (16, 64, 256):
+            x = make_tokens(CONFIGS["v3_decode_bf16"], T, 3, dev)
+            rd = time_layer(layer, x, 20, 3, bias_update=False)
+            nt = int((rd["out"]["counts"] > 0).sum())
+            a = algorithmic(wl, T, nt)
+            dms = rd["wall_ms_per_step"]
+            dec[str(T)] = {"ms": dms, "tokens_per_s": T / (dms / 1e3),
+                           "hbm_GBps": a["layer_bytes"] / (dms / 1e3) / 1e9,
+                           "hbm_frac": a["layer_bytes"] / (dms / 1e3) / HBM_PEAK,
+                           "n_touched": nt, "stage_ms": rd["stage_ms"]}
+            log(f"decode T={T}: {dms:.3f} ms, {dec[str(T)]['hbm_GBps']:.0f} GB/s, {nt} experts")
+        extra["decode_bf16"] = dec
+        try:
+            wl8 = CONFIGS["v3_fp8"]
+            layer8 = M.MoELayer(wl8, P)
+            r8 = time_layer(layer8, P["x"], 10, 3)
+            ms8 = r8["wall_ms_per_step"]
+            a8 = algorithmic(wl8, wl8.T, int((r8["out"]["counts"] > 0).sum()))
+            extra["fp8"] = {"ms": ms8, "tokens_per_s": wl8.T / (ms8 / 1e3),
+                            "mfma_frac_fp8": a8["layer_flops"] / (ms8 / 1e3) / MFMA_PEAK["fp8"],
+                            "hbm_frac": a8["layer_bytes"] / (ms8 / 1e3) / HBM_PEAK,
+                            "stage_ms": r8["stage_ms"]}
+            log(f"fp8: {ms8:.3f} ms, {wl8.T / ms8 * 1e3 / 1e6:.3f} M tok/s")
+            del layer8
+        except M.MoeError as e:
+            extra["fp8"] = {"error": str(e)}
+            log(f"fp8: {e}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu oracle baseline on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(wl, P, args.cpu_tokens)
+        log(f"cpu oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} BLAS threads")
+
+    line = {"metric": "MoE-layer tokens/s at V3 shape (bf16, fp8) + % of MFMA/HBM roofline",
+            "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": wl.w, "data": "synthetic",
+            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "n_experts": wl.E,
+                       "top_k": wl.K, "groups": wl.G, "topk_groups": wl.M, "inter": wl.I,
+                       "shared_inter": wl.Is, "parallelism": "single GPU"},
+            "roofline": roof, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

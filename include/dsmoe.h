@@ -212,6 +212,13 @@ moe_status moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t n
 moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, int32_t cols,
                                  uint8_t* q, float* scale, hipStream_t stream);
 
+/* Timing hook for benchmarks (thread-local setting). With n_events >= 6,
+ * deepseek_moe_forward records events[0..5] on its stream: before the router,
+ * after routing, right before the gate/up GEMM, after it, after the down GEMM
+ * and after the combine. events == NULL or n_events == 0 turns it off. The
+ * events stay owned by the caller. */
+moe_status moe_profile_events(const hipEvent_t* events, int32_t n_events);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 int moe_abi_version(void);

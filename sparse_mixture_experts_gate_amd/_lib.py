@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "deepseek_moe_forward": [D, P, P, P, W, P, P, P, P, P, P, P, ctypes.c_size_t, P],
             "moe_quantize_fp8_blocks": [P, I32, I64, I32, I32, P, P, P],
             "moe_quantize_fp8_rows": [P, I32, I64, I32, P, P, P],
+            "moe_profile_events": [ctypes.POINTER(ctypes.c_void_p), I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -181,6 +182,16 @@ def moe_quantize_fp8_blocks(src, q, scale, stream=None):
     shp = src.shape if src.dim() == 3 else (1, *src.shape)
     _check(lib().moe_quantize_fp8_blocks(_p(src), _dt(src), shp[0], shp[1], shp[2], _p(q),
                                          _p(scale), _stream(stream)), "moe_quantize_fp8_blocks")
+
+
+def moe_profile_events(events) -> None:
+    """events: six torch.cuda.Event(enable_timing=True) already recorded once
+    (so that they exist), or None to switch the hook off."""
+    if events is None:
+        _check(lib().moe_profile_events(None, 0), "moe_profile_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check(lib().moe_profile_events(arr, len(events)), "moe_profile_events")
 
 
 def moe_quantize_fp8_rows(src, q, scale, stream=None):

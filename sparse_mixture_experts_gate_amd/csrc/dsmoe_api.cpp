@@ -16,6 +16,12 @@ using namespace dsmoe;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_prof[6] = {};
+thread_local bool g_prof_on = false;
+
+hipError_t prof_record(int i, hipStream_t s) {
+  return g_prof_on ? hipEventRecord(g_prof[i], s) : hipSuccess;
+}
 
 moe_status fail(moe_status st, const char* fmt, ...) {
   char buf[512];
@@ -279,8 +285,7 @@ moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_route
 moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
                    const int32_t* perm, const void* x_perm, const float* x_perm_scale,
                    const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
-                   const FfnLayout& L, bool offsets_ready_tiles, hipStream_t s) {
-  (void)offsets_ready_tiles;
+                   const FfnLayout& L, bool profile, hipStream_t s) {
   if (d->T == 0) return MOE_OK;
   int32_t* tiles1 = at<int32_t>(ws, L.tiles1);
   int32_t* tiles2 = at<int32_t>(ws, L.tiles2);
@@ -323,14 +328,21 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
     HIP_TRY(launch_quant_rows(x, MOE_DT_BF16, nullptr, d->T, d->d, xq, xs, s), "quantize x");
     a.x = xq;
     a.x_scale = xs;
-    HIP_TRY(launch_ffn_fp8(a, L.tiling, s), "expert ffn (fp8)");
   } else {
     a.x = x;
-    if (d->w_dtype == MOE_DT_BF16)
-      HIP_TRY(launch_ffn_bf16(a, L.tiling, s), "expert ffn (bf16)");
-    else
-      HIP_TRY(launch_ffn_f32(a, s), "expert ffn (fp32)");
   }
+  hipEvent_t mid = nullptr;
+  if (profile) {
+    HIP_TRY(prof_record(2, s), "profile event");
+    mid = g_prof_on ? g_prof[3] : nullptr;
+  }
+  if (d->w_dtype == MOE_DT_FP8_E4M3)
+    HIP_TRY(launch_ffn_fp8(a, L.tiling, s, mid), "expert ffn (fp8)");
+  else if (d->w_dtype == MOE_DT_BF16)
+    HIP_TRY(launch_ffn_bf16(a, L.tiling, s, mid), "expert ffn (bf16)");
+  else
+    HIP_TRY(launch_ffn_f32(a, s, mid), "expert ffn (fp32)");
+  if (profile) HIP_TRY(prof_record(4, s), "profile event");
   return MOE_OK;
 }
 
@@ -534,10 +546,11 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
   int32_t* inv = at<int32_t>(ws, L.inv);
   void* yperm = at<void>(ws, L.yperm);
   void* yshared = desc->shared_inter > 0 ? at<void>(ws, L.yshared) : nullptr;
+  HIP_TRY(prof_record(0, stream), "profile event");
   st = run_gate(desc, x, w_router, bias, logits, topk_idx, topk_gate, counts, near_tie, gws,
                 L.gate, stream);
   if (st) return st;
-  if (desc->T == 0) return MOE_OK;
+  HIP_TRY(prof_record(1, stream), "profile event");
   HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, nullptr, nullptr,
                       plan_params(desc, L.ffn.tiling), stream),
           "offsets");
@@ -550,6 +563,21 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
   HIP_TRY(launch_combine(yperm, inv, topk_gate, yshared, y, desc->T, desc->top_k, desc->d,
                          desc->act_dtype, stream),
           "combine");
+  HIP_TRY(prof_record(5, stream), "profile event");
+  return MOE_OK;
+}
+
+moe_status moe_profile_events(const hipEvent_t* events, int32_t n_events) {
+  if (!events || n_events == 0) {
+    g_prof_on = false;
+    return MOE_OK;
+  }
+  if (n_events < 6) return fail(MOE_ERR_INVALID_ARGUMENT, "need 6 events, got %d", n_events);
+  for (int i = 0; i < 6; ++i) {
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARGUMENT, "event %d is NULL", i);
+    g_prof[i] = events[i];
+  }
+  g_prof_on = true;
   return MOE_OK;
 }
 

@@ -354,7 +354,7 @@ int occupancy_blocks(K kernel, int threads) {
 }
 
 template <class C>
-hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
   if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C>, C::NT);
   if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C>, C::NT);
@@ -365,6 +365,7 @@ hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(ffn1_bf16_kernel<C>, dim3(g1), dim3(C::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
   hipLaunchKernelGGL(ffn2_bf16_kernel<C>, dim3(g2), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }
@@ -392,9 +393,9 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
   return t;
 }
 
-hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s) {
-  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode>(a, s);
-  return launch_ffn_bf16_cfg<TilePrefill>(a, s);
+hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
+  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode>(a, s, mid);
+  return launch_ffn_bf16_cfg<TilePrefill>(a, s, mid);
 }
 
 int router_splits(int64_t T, int d, int E, int act_dtype) {

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(FfnArgs a) {
 
 }  // namespace
 
-hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   const int64_t rows = a.TK + (a.Is > 0 ? a.T : 0);
   if (rows == 0) return hipSuccess;
   const int64_t n1 = rows * a.ldh, n2 = rows * a.d;
@@ -90,6 +90,7 @@ hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
                      s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
   hipLaunchKernelGGL(ffn2_f32_kernel, dim3(static_cast<unsigned>((n2 + 255) / 256)), dim3(256), 0,
                      s, a);
   return hipGetLastError();

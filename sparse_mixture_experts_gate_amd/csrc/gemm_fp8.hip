@@ -4,7 +4,7 @@
 
 namespace dsmoe {
 
-hipError_t launch_ffn_fp8(const FfnArgs&, const GemmTiling&, hipStream_t) {
+hipError_t launch_ffn_fp8(const FfnArgs&, const GemmTiling&, hipStream_t, hipEvent_t) {
   return hipErrorNotSupported;
 }
 

@@ -89,9 +89,10 @@ struct GemmTiling {
 };
 
 GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype);
-hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s);
-hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
-hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s);
+// `mid` (may be NULL) is recorded between the gate/up and the down GEMM.
+hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s, hipEvent_t mid);
+hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
 
 // ---- elementwise (elementwise.hip) -----------------------------------------
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,

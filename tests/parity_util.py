@@ -23,17 +23,13 @@ def row_rel_err(y, ref) -> float:
 
 class LazyHost:
     """Indexable host view of a device tensor [E, ...]: expert e is copied to
-    the host (as fp32) only when the oracle asks for it."""
+    the host (as fp32) when the oracle asks for it, and not kept."""
 
     def __init__(self, t: torch.Tensor):
         self.t = t
-        self.cache = {}
 
     def __getitem__(self, e):
-        e = int(e)
-        if e not in self.cache:
-            self.cache[e] = host(self.t[e])
-        return self.cache[e]
+        return host(self.t[int(e)])
 
 
 def route_args(wl):

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(L):
         "moe_workspace_size", "moe_gate", "moe_route_from_logits", "moe_permute",
         "moe_expert_ffn", "moe_combine", "moe_bias_update", "deepseek_moe_forward",
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
-        "moe_last_error", "moe_abi_version"}
+        "moe_last_error", "moe_abi_version", "moe_profile_events"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
