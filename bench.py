@@ -147,7 +147,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy three times, so that HBM byte "
+                         "counters can be scaled against a kernel of known traffic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     args = ap.parse_args()
@@ -162,6 +165,13 @@ def main() -> int:
 
     wl = CONFIGS[args.workload]
     dev = "cuda"
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"generating {wl.name} inputs")
     P = make_inputs(wl, dev)
     layer = M.MoELayer(wl, P)

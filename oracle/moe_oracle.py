@@ -48,7 +48,7 @@ F64 = np.float64
 __all__ = [
     "sigmoid_f32", "router_logits", "route", "permute", "bias_update",
     "swiglu_expert", "layer_output", "forward", "round_bf16",
-    "e4m3_decode", "e4m3_encode", "quantize_rows_1x128", "quantize_blocks_128",
+    "e4m3_decode", "e4m3_encode", "e4m3_encode_table", "quantize_rows_1x128", "quantize_blocks_128",
     "dequant_rows_1x128", "dequant_blocks_128", "layer_output_fp8",
     "RouteResult", "PermuteResult",
 ]
@@ -322,7 +322,28 @@ _E4M3_POS = e4m3_decode(np.arange(0, 127, dtype=np.uint8)).astype(F64)  # codes 
 
 def e4m3_encode(v) -> np.ndarray:
     """Nearest E4M3FN code, ties to the even code (mantissa LSB 0); magnitudes
-    beyond 448 saturate to 448; the sign bit follows the input's sign."""
+    beyond 448 saturate to 448; the sign bit follows the input's sign.
+
+    From the format: with |v| = 1.f * 2^E, a normal code (E >= -6) counts steps
+    of 2^(E-3) (3 mantissa bits), a subnormal one steps of 2^-9. The magnitude
+    divided by its step is rounded to the nearest integer, ties to even (exact
+    in fp64); code = (E + 7) * 8 + (steps - 8) for normals (steps == 16 rolls
+    into the next binade by itself), code = steps for subnormals."""
+    v = np.asarray(v, dtype=F32)
+    a = np.minimum(np.abs(v).astype(F64), 448.0)
+    _, e = np.frexp(a)
+    E = e - 1
+    sub = E < -6
+    step_exp = np.where(sub, -9, E - 3)
+    steps = np.rint(np.ldexp(a, -step_exp)).astype(np.int64)
+    code = np.where(sub, steps, (E + 7) * 8 + (steps - 8))
+    code = np.where(a == 0.0, 0, code).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_encode_table(v) -> np.ndarray:
+    """Reference for e4m3_encode: nearest of the 127 non-negative finite code
+    values by table search, ties to the even code, saturating at 448."""
     v = np.asarray(v, dtype=F32)
     a = np.abs(v).astype(F64)
     hi = np.searchsorted(_E4M3_POS, a, side="left")          # first value >= a
@@ -366,16 +387,20 @@ def quantize_rows_1x128(X):
 
 def quantize_blocks_128(W):
     """Weight blocks: 128 output rows x 128 input columns [GK Q8; MH §4.1].
-    W [R, C] with R, C % 128 == 0 -> (codes [R, C], scales [R/128, C/128])."""
+    W [R, C] with R, C % 128 == 0 -> (codes [R, C], scales [R/128, C/128]).
+    The rule of _quant_block, applied to every block at once."""
     W = np.asarray(W, dtype=F32)
     R, C = W.shape
-    q = np.empty((R, C), np.uint8)
-    s = np.empty((R // 128, C // 128), F32)
-    for i in range(R // 128):
-        for j in range(C // 128):
-            blk = W[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
-            q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], s[i, j] = _quant_block(blk)
-    return q, s
+    blk = W.reshape(R // 128, 128, C // 128, 128)
+    amax = np.abs(blk).max(axis=(1, 3)).astype(F32)               # [R/128, C/128]
+    zero = amax == F32(0.0)
+    safe = np.where(zero, F32(1.0), amax).astype(F32)
+    inv = (F32(448.0) / safe).astype(F32)
+    scaled = (blk * inv[:, None, :, None]).astype(F32)
+    q = e4m3_encode(scaled)
+    q = np.where(zero[:, None, :, None], np.uint8(0), q).astype(np.uint8)
+    s = np.where(zero, F32(1.0), (safe / F32(448.0)).astype(F32)).astype(F32)
+    return q.reshape(R, C), s
 
 
 def dequant_rows_1x128(q, s) -> np.ndarray:

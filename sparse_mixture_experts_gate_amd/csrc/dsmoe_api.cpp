@@ -282,10 +282,13 @@ moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_route
   return MOE_OK;
 }
 
+// Expert FFNs on a validated call; ws points at an FfnLayout region. With
+// planned == true the tile tables were already written (by the forward's
+// single planning launch).
 moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
                    const int32_t* perm, const void* x_perm, const float* x_perm_scale,
                    const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
-                   const FfnLayout& L, bool profile, hipStream_t s) {
+                   const FfnLayout& L, bool profile, bool planned, hipStream_t s) {
   if (d->T == 0) return MOE_OK;
   int32_t* tiles1 = at<int32_t>(ws, L.tiles1);
   int32_t* tiles2 = at<int32_t>(ws, L.tiles2);
@@ -319,9 +322,10 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   a.H_scale = at<float>(ws, L.Hs);
   a.yperm = y_perm;
   a.yshared = y_shared;
-  HIP_TRY(launch_plan(nullptr, offsets, nullptr, tiles1, tiles2, tmap1, tmap2,
-                      plan_params(d, L.tiling), s),
-          "plan");
+  if (!planned)
+    HIP_TRY(launch_plan(nullptr, offsets, nullptr, tiles1, tiles2, tmap1, tmap2,
+                        plan_params(d, L.tiling), s),
+            "plan");
   if (d->w_dtype == MOE_DT_FP8_E4M3) {
     uint8_t* xq = at<uint8_t>(ws, L.xq);
     float* xs = at<float>(ws, L.xs);
@@ -488,7 +492,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* w, cons
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_expert_ffn needs %zu workspace bytes, got %zu",
                 L.bytes, ws_bytes);
   return run_ffn(desc, w, x, perm, x_perm, x_perm_scale, offsets, y_perm, y_shared, ws, L, false,
-                 stream);
+                 false, stream);
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int32_t* inv,
@@ -551,14 +555,15 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
                 L.gate, stream);
   if (st) return st;
   HIP_TRY(prof_record(1, stream), "profile event");
-  HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, nullptr, nullptr,
-                      plan_params(desc, L.ffn.tiling), stream),
-          "offsets");
+  HIP_TRY(launch_plan(counts, nullptr, offsets, at<int32_t>(fws, L.ffn.tiles1),
+                      at<int32_t>(fws, L.ffn.tiles2), at<int32_t>(fws, L.ffn.tmap1),
+                      at<int32_t>(fws, L.ffn.tmap2), plan_params(desc, L.ffn.tiling), stream),
+          "plan");
   HIP_TRY(launch_permute(topk_idx, offsets, desc->T, desc->top_k, desc->n_experts, perm, inv,
                          stream),
           "permute");
   st = run_ffn(desc, w, x, perm, nullptr, nullptr, offsets, yperm, yshared, fws, L.ffn, true,
-               stream);
+               true, stream);
   if (st) return st;
   HIP_TRY(launch_combine(yperm, inv, topk_gate, yshared, y, desc->T, desc->top_k, desc->d,
                          desc->act_dtype, stream),

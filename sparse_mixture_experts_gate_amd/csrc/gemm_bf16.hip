@@ -375,11 +375,11 @@ hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) 
 GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
   GemmTiling t{};
   const double rows_per_expert = static_cast<double>(T) * K / E;
-  if (w_dtype == 2) {  // FP8: fixed 128-wide k blocks; see gemm_fp8.hip
+  if (w_dtype == 2) {  // FP8: 128 intermediate columns per gate/up tile; see gemm_fp8.hip
     if (rows_per_expert < 48.0) {
-      t.bm1 = 32; t.bnh1 = 64; t.bm2 = 32; t.bn2 = 128; t.variant = 1;
+      t.bm1 = 32; t.bnh1 = 128; t.bm2 = 32; t.bn2 = 128; t.variant = 1;
     } else {
-      t.bm1 = 128; t.bnh1 = 64; t.bm2 = 128; t.bn2 = 128; t.variant = 0;
+      t.bm1 = 128; t.bnh1 = 128; t.bm2 = 128; t.bn2 = 128; t.variant = 0;
     }
     return t;
   }

@@ -1,11 +1,385 @@
-// FP8 (E4M3) grouped expert GEMMs: placeholder until the MFMA kernel lands.
+// FP8 (E4M3) grouped expert GEMMs on gfx950.
+//
+// GEMMs in FP8 with fine-grained scaling: activations carry one fp32 scale per
+// 1x128 tile (per token, 128 channels), weights one per 128x128 block, and
+// partial products are promoted to fp32 at every 128-wide slice of the
+// contraction (mhpq.cn "DeepSeek-V3 高效训练关键技术全景解析" §4.1; gkm0120.cn
+// DeepSeek-V3 notes, Q8). Here one LDS stage holds exactly one 128-wide slice,
+// so a single v_mfma_scale_f32_16x16x128_f8f6f4 (unit hardware scales) yields
+// the slice's exact-product partial sum for a 16x16 sub-tile; the fp32 scale
+// product s_a(row) * s_b(block) is applied on the VALU as it is accumulated.
+//
+// The gate/up GEMM covers 128 intermediate columns per tile, i.e. exactly one
+// 1x128 quantization tile of H: its epilogue computes silu(gate) * up, the
+// row max-abs across the tile's waves, and writes E4M3 codes plus the fp32
+// scale that the down GEMM consumes.
+#pragma clang fp contract(off)
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace dsmoe {
 
-hipError_t launch_ffn_fp8(const FfnArgs&, const GemmTiling&, hipStream_t, hipEvent_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int BK8 = 128;  // E4M3 elements (bytes) per row per stage = one scale block
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile8 {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int MI = WM / 16, NJ = WN / 16;
+  static constexpr int RPP = NT / 8;
+  static constexpr int A_LOADS = BM / RPP;
+  static constexpr int B_LOADS = BN / RPP;
+  static constexpr int STAGE = (BM + BN) * BK8;  // bytes
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
+  static_assert(BM <= NT, "one thread per row loads the activation scales");
+};
+
+using T8Gate = Tile8<128, 256, 64, 64>;     // 8 waves, H tile 128 x 128, 96 KB LDS
+using T8Down = Tile8<128, 128, 64, 64>;     // 4 waves, 64 KB LDS
+using T8GateDec = Tile8<32, 256, 32, 64>;   // 4 waves
+using T8DownDec = Tile8<32, 128, 32, 64>;   // 2 waves
+
+__device__ __forceinline__ int lds_off8(int r, int ch) { return r * BK8 + ((ch ^ (r & 7)) << 4); }
+
+template <class C, bool SWIGLU>
+__device__ __forceinline__ int b_row8(int wn, int nj) {
+  if constexpr (SWIGLU) {
+    constexpr int half = C::BN / 2, hw = C::WN / 2, njh = C::NJ / 2;
+    return nj < njh ? wn * hw + nj * 16 : half + wn * hw + (nj - njh) * 16;
+  } else {
+    return wn * C::WN + nj * 16;
+  }
+}
+
+__device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_off8(r, 2 * kg));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_off8(r, 2 * kg + 1));
+  i32x8_t v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// acc[mi][nj] += sum over 128-wide k blocks kb of
+//   (A_kb B_kb^T) * s_a[row][kb] * s_b[kb]   (s_b: sb_lo for the first half of
+// the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
+// sa_row: this thread's row scale pointer when threadIdx.x < BM (else unused).
+template <class C, bool SWIGLU>
+__device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
+                                           const uint8_t* const (&arow)[C::A_LOADS],
+                                           const float* sa_row,
+                                           const uint8_t* const (&brow)[C::B_LOADS],
+                                           const float* sb_lo, const float* sb_hi, int K,
+                                           f32x4_t (&acc)[C::MI][C::NJ]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int ch = tid & 7, r0 = tid >> 3;
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[C::A_LOADS], rb[C::B_LOADS];
+  float rsa = 0.0f;
+  auto gload = [&](int kb) {
+    const int off = kb * BK8 + ch * 16;
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p)
+      ra[p] = arow[p] ? *reinterpret_cast<const uint4*>(arow[p] + off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p)
+      rb[p] = brow[p] ? *reinterpret_cast<const uint4*>(brow[p] + off) : make_uint4(0, 0, 0, 0);
+    if (tid < C::BM) rsa = sa_row ? sa_row[kb] : 0.0f;
+  };
+  auto sstore = [&](int st) {
+    uint8_t* As = lds + st * C::STAGE;
+    uint8_t* Bs = As + C::BM * BK8;
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p)
+      *reinterpret_cast<uint4*>(As + lds_off8(r0 + p * C::RPP, ch)) = ra[p];
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p)
+      *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = rb[p];
+    if (tid < C::BM) lds_sa[st * C::BM + tid] = rsa;
+  };
+
+  const int nkb = K / BK8;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  int st = 0;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) gload(kb + 1);
+    const float s_lo = sb_lo[kb];
+    const float s_hi = SWIGLU ? sb_hi[kb] : s_lo;
+    const uint8_t* As = lds + st * C::STAGE;
+    const uint8_t* Bs = As + C::BM * BK8;
+    const int kg = lane >> 4;
+    i32x8_t bfr[C::NJ];
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int rbase = wm * C::WM + mi * 16;
+      const i32x8_t af = frag8(As, rbase + (lane & 15), kg);
+      const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::BM + rbase + 4 * kg);
+      f32x4_t s_l, s_h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s_l[r] = sa[r] * s_lo;
+        s_h[r] = sa[r] * s_hi;
+      }
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        const f32x4_t p =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[nj], zero, 0, 0, 0, 127, 0, 127);
+        const bool lo = !SWIGLU || nj < C::NJ / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][nj][r] = __builtin_fmaf(p[r], lo ? s_l[r] : s_h[r], acc[mi][nj][r]);
+      }
+    }
+    if (more) sstore(st ^ 1);
+    __syncthreads();
+    st ^= 1;
+  }
+}
+
+struct TileCoord8 {
+  int g, rows, rbase, m, n;
+  bool shared;
+};
+
+__device__ __forceinline__ TileCoord8 tile_coord8(const FfnArgs& a, const int32_t* tiles,
+                                                  const int32_t* tmap, int tile, int bm) {
+  TileCoord8 c;
+  c.g = tmap[tile];
+  c.shared = c.g == a.E;
+  c.rbase = c.shared ? 0 : a.offsets[c.g];
+  c.rows = c.shared ? static_cast<int>(a.T) : a.offsets[c.g + 1] - c.rbase;
+  const int mt = (c.rows + bm - 1) / bm;
+  const int local = tile - tiles[c.g];
+  c.n = local / mt;
+  c.m = local % mt;
+  return c;
+}
+
+// H (E4M3 + 1x128 scales) = quant(silu(A W1^T) * (A W3^T)); tile = 128 H columns.
+template <class C>
+__global__ __launch_bounds__(C::NT) void ffn1_fp8_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
+  __shared__ float red[C::WAVES_N][C::BM];
+  constexpr int HALF = C::BN / 2;  // 128 H columns
+  static_assert(HALF == 128, "one 1x128 quantization tile of H per tile");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r0 = tid >> 3;
+  const int total = a.tiles1[a.E + 1];
+  const int nb = gridDim.x;
+  const int dkb = a.d / 128;
+  const int hkb = a.ldh / 128;
+  const uint8_t* X = static_cast<const uint8_t*>(a.perm ? a.x : a.xperm);
+  const float* XS = a.perm ? a.x_scale : a.xperm_scale;
+  const uint8_t* Xsh = static_cast<const uint8_t*>(a.x);
+  uint8_t* H = static_cast<uint8_t*>(a.H);
+  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
+    const TileCoord8 tc = tile_coord8(a, a.tiles1, a.tmap1, tile, C::BM);
+    const int Ig = tc.shared ? a.Is : a.I;
+    auto src_row = [&](int r, const uint8_t** p, const float** s) {
+      *p = nullptr;
+      *s = nullptr;
+      if (r >= tc.rows) return;
+      int64_t row;
+      const uint8_t* base;
+      const float* sbase;
+      if (tc.shared) {
+        row = r; base = Xsh; sbase = a.x_scale;
+      } else if (a.perm) {
+        row = a.perm[tc.rbase + r];
+        if (row < 0 || row >= a.T) return;
+        base = X; sbase = XS;
+      } else {
+        row = tc.rbase + r; base = X; sbase = XS;
+      }
+      *p = base + row * a.d;
+      *s = sbase + row * dkb;
+    };
+    const uint8_t* arow[C::A_LOADS];
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const float* dummy;
+      src_row(tc.m * C::BM + r0 + p * C::RPP, &arow[p], &dummy);
+    }
+    const float* sa_row = nullptr;
+    if (tid < C::BM) {
+      const uint8_t* dummy;
+      src_row(tc.m * C::BM + tid, &dummy, &sa_row);
+    }
+    const uint8_t* W = tc.shared ? static_cast<const uint8_t*>(a.ws13)
+                                 : static_cast<const uint8_t*>(a.w13) +
+                                       static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
+    const float* WS = tc.shared ? a.ws13_scale
+                                : a.w13_scale + static_cast<int64_t>(tc.g) * (2 * a.I / 128) * dkb;
+    const uint8_t* brow[C::B_LOADS];
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p) {
+      const int lr = r0 + p * C::RPP;
+      const bool up = lr >= HALF;
+      const int col = tc.n * HALF + (up ? lr - HALF : lr);
+      brow[p] = W + static_cast<int64_t>(up ? Ig + col : col) * a.d;
+    }
+    const float* sb_gate = WS + static_cast<int64_t>(tc.n) * dkb;
+    const float* sb_up = WS + static_cast<int64_t>(Ig / 128 + tc.n) * dkb;
+    f32x4_t acc[C::MI][C::NJ];
+    gemm8_tile<C, true>(lds, lds_sa, arow, sa_row, brow, sb_gate, sb_up, a.d, acc);
+
+    // SwiGLU, then the row max-abs over the 128 columns (across the wave's
+    // 16-lane groups and the tile's WAVES_N waves)
+    constexpr int NJH = C::NJ / 2;
+    float h[C::MI][NJH][4];
+    float pm[C::MI][4];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = 0.0f;
+#pragma unroll
+        for (int nj = 0; nj < NJH; ++nj) {
+          h[mi][nj][r] = silu_f32(acc[mi][nj][r]) * acc[mi][nj + NJH][r];
+          m = fmaxf(m, fabsf(h[mi][nj][r]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        pm[mi][r] = m;
+      }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wn][wm * C::WM + mi * 16 + 4 * (lane >> 4) + r] = pm[mi][r];
+    }
+    __syncthreads();
+    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    const int rows_left = tc.rows - tc.m * C::BM;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = wm * C::WM + mi * 16 + 4 * (lane >> 4) + r;
+        float amax = red[0][lr];
+#pragma unroll
+        for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
+        if (lr >= rows_left) continue;
+        const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
+        uint8_t* hrow = H + (hrow0 + lr) * a.ldh + tc.n * HALF;
+#pragma unroll
+        for (int nj = 0; nj < NJH; ++nj) {
+          const int col = wn * (C::WN / 2) + nj * 16 + (lane & 15);
+          const uint32_t q = amax == 0.0f ? 0u : e4m3_pack4(h[mi][nj][r] * inv, 0.f, 0.f, 0.f);
+          hrow[col] = static_cast<uint8_t>(q & 0xFFu);
+        }
+        if (wn == 0 && (lane & 15) == 0)
+          a.H_scale[(hrow0 + lr) * hkb + tc.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
+      }
+    __syncthreads();  // red[] is rewritten by the next tile
+  }
+}
+
+// y = dequant(H) dequant(W2)^T per group, bf16 out.
+template <class C>
+__global__ __launch_bounds__(C::NT) void ffn2_fp8_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r0 = tid >> 3;
+  const int total = a.tiles2[a.E + 1];
+  const int nb = gridDim.x;
+  const int hkb = a.ldh / 128;
+  const uint8_t* H = static_cast<const uint8_t*>(a.H);
+  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
+    const TileCoord8 tc = tile_coord8(a, a.tiles2, a.tmap2, tile, C::BM);
+    const int Ig = tc.shared ? a.Is : a.I;
+    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    const int rows_left = tc.rows - tc.m * C::BM;
+    const uint8_t* arow[C::A_LOADS];
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const int lr = r0 + p * C::RPP;
+      arow[p] = lr < rows_left ? H + (hrow0 + lr) * a.ldh : nullptr;
+    }
+    const float* sa_row = (tid < C::BM && tid < rows_left) ? a.H_scale + (hrow0 + tid) * hkb : nullptr;
+    const uint8_t* W = tc.shared ? static_cast<const uint8_t*>(a.ws2)
+                                 : static_cast<const uint8_t*>(a.w2) +
+                                       static_cast<int64_t>(tc.g) * a.d * a.I;
+    const int ikb = Ig / 128;
+    const float* WS = tc.shared ? a.ws2_scale
+                                : a.w2_scale + static_cast<int64_t>(tc.g) * (a.d / 128) * (a.I / 128);
+    const uint8_t* brow[C::B_LOADS];
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p) {
+      const int row = tc.n * C::BN + r0 + p * C::RPP;
+      brow[p] = row < a.d ? W + static_cast<int64_t>(row) * Ig : nullptr;
+    }
+    const float* sb = WS + static_cast<int64_t>((tc.n * C::BN) / 128) * ikb;
+    f32x4_t acc[C::MI][C::NJ];
+    gemm8_tile<C, false>(lds, lds_sa, arow, sa_row, brow, sb, sb, Ig, acc);
+
+    uint16_t* out = tc.shared ? static_cast<uint16_t*>(a.yshared) +
+                                    static_cast<int64_t>(tc.m) * C::BM * a.d
+                              : static_cast<uint16_t*>(a.yperm) +
+                                    (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        const int col = tc.n * C::BN + wn * C::WN + nj * 16 + (lane & 15);
+        if (col >= a.d) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = wm * C::WM + mi * 16 + 4 * (lane >> 4) + r;
+          if (lr < rows_left) out[static_cast<int64_t>(lr) * a.d + col] = f32_to_bf16(acc[mi][nj][r]);
+        }
+      }
+  }
+}
+
+template <class K>
+int occupancy8(K kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
+template <class C1, class C2>
+hipError_t launch_fp8_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
+  static int occ1 = 0, occ2 = 0;
+  if (!occ1) occ1 = occupancy8(ffn1_fp8_kernel<C1>, C1::NT);
+  if (!occ2) occ2 = occupancy8(ffn2_fp8_kernel<C2>, C2::NT);
+  const int cus = device_cu_count();
+  const int g1 = ((cus * occ1 + 7) / 8) * 8;
+  const int g2 = ((cus * occ2 + 7) / 8) * 8;
+  hipLaunchKernelGGL(ffn1_fp8_kernel<C1>, dim3(g1), dim3(C1::NT), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
+  hipLaunchKernelGGL(ffn2_fp8_kernel<C2>, dim3(g2), dim3(C2::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
+  if (t.variant == 1) return launch_fp8_pair<T8GateDec, T8DownDec>(a, s, mid);
+  return launch_fp8_pair<T8Gate, T8Down>(a, s, mid);
 }
 
 }  // namespace dsmoe

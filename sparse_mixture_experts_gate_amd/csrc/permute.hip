@@ -71,15 +71,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       if (tiles1) tiles1[tid + 1] = s1[tid];
       if (tiles2) tiles2[tid + 1] = s2[tid];
     }
-    // tile -> group maps
-    for (int g = tid; g < ng; g += kPlanThreads) {
-      const int b1 = g == 0 ? 0 : s1[g - 1];
-      const int b2 = g == 0 ? 0 : s2[g - 1];
-      if (tmap1)
-        for (int i = b1; i < s1[g]; ++i) tmap1[i] = g;
-      if (tmap2)
-        for (int i = b2; i < s2[g]; ++i) tmap2[i] = g;
-    }
+    // tile -> group maps: every thread takes tiles i, i + 1024, ... and finds
+    // the group g with s[g-1] <= i < s[g] (inclusive prefix) by binary search
+    auto fill = [&](const int* s, int32_t* tmap) {
+      const int total = s[ng - 1];
+      for (int i = tid; i < total; i += kPlanThreads) {
+        int lo = 0, hi = ng - 1;  // smallest g with s[g] > i
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s[mid] > i) hi = mid; else lo = mid + 1;
+        }
+        tmap[i] = lo;
+      }
+    };
+    if (tmap1) fill(s1, tmap1);
+    if (tmap2) fill(s2, tmap2);
   }
 }
 

@@ -1,0 +1,159 @@
+"""GPU parity of the FP8 (E4M3, 1x128 activation tiles, 128x128 weight blocks,
+fp32 accumulation) layer against the oracle's FP8 forward, and the
+load-balancing loop: forward + bias update on fresh Zipf-skewed batches with
+the bias trajectory bit-exact against the oracle's update rule."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_gate_amd as M
+from sparse_mixture_experts_gate_amd.workloads import CONFIGS, Workload, make_inputs, make_tokens
+from parity_util import TOL, host, route_args, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class LazyQuant:
+    """Oracle-side E4M3 block quantization of expert e's bf16 weights, made on
+    demand from the host copy (the oracle quantizes on its own)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.cache = {}
+
+    def get(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = O.quantize_blocks_128(host(self.t[e]))
+        return self.cache[e]
+
+
+class _Codes:
+    def __init__(self, lq): self.lq = lq
+    def __getitem__(self, e): return self.lq.get(e)[0]
+
+
+class _Scales:
+    def __init__(self, lq): self.lq = lq
+    def __getitem__(self, e): return self.lq.get(e)[1]
+
+
+def oracle_fp8(wl, P, x_rows, idx, gate):
+    q13, q2 = LazyQuant(P["w13"]), LazyQuant(P["w2"])
+    sh = {}
+    if wl.Is:
+        sh = dict(zip(("ws13q", "ws13s"), O.quantize_blocks_128(host(P["ws13"]))))
+        sh.update(zip(("ws2q", "ws2s"), O.quantize_blocks_128(host(P["ws2"]))))
+    y = O.layer_output_fp8(x_rows, idx, gate, _Codes(q13), _Scales(q13), _Codes(q2), _Scales(q2),
+                           **sh)
+    return O.round_bf16(y)
+
+
+def fp8_small(T):
+    return Workload("fp8_small", T=T, d=256, E=16, K=4, I=256, Is=256, G=4, M=2, topn=2,
+                    act="bf16", w="fp8", x_kind="normal", bias_kind="uniform", bias_amp=0.05,
+                    w_std=0.05, seed=21)
+
+
+@pytest.mark.parametrize("T", [300, 7, 1])
+def test_fp8_layer_parity_small(T):
+    """T=300 runs the 128-row tiles, T=7 and T=1 the decode tiles."""
+    wl = fp8_small(T)
+    print(f"fp8 small T={T}", flush=True)
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    g = {k: host(v) for k, v in layer.forward(P["x"]).items()}
+    torch.cuda.synchronize()
+    rr = O.route(g["logits"], host(P["bias"]), **route_args(wl))
+    assert np.array_equal(g["topk_idx"], rr.idx)
+    assert np.array_equal(g["topk_gate"].view(np.uint32), rr.gate.view(np.uint32))
+    ref = oracle_fp8(wl, P, host(P["x"]), rr.idx, rr.gate)
+    err = row_rel_err(g["y"], ref)
+    print(f"  fp8 max row-rel err {err:.3e}", flush=True)
+    assert err <= TOL["fp8"]
+
+
+def test_fp8_staged_matches_fused():
+    """moe_permute's quantized gathered rows through moe_expert_ffn give the
+    fused forward's output bit for bit."""
+    wl = fp8_small(300)
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    fused = layer.forward(P["x"])
+    T = wl.T
+    desc = M.make_desc(wl, T)
+    ws = torch.empty(M.moe_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    offsets = torch.empty(wl.E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * wl.K, dtype=torch.int32, device=DEV)
+    inv = torch.empty(T, wl.K, dtype=torch.int32, device=DEV)
+    xq = torch.empty(T * wl.K, wl.d, dtype=torch.uint8, device=DEV)
+    xs = torch.empty(T * wl.K, wl.d // 128, device=DEV)
+    M.moe_permute(desc, fused["topk_idx"], fused["counts"], P["x"], offsets, perm, inv, xq, xs)
+    yp = torch.empty(T * wl.K, wl.d, dtype=torch.bfloat16, device=DEV)
+    ysh = torch.empty(T, wl.d, dtype=torch.bfloat16, device=DEV)
+    M.moe_expert_ffn(desc, layer.weights, P["x"], perm, xq, xs, offsets, yp, ysh, ws)
+    y = torch.empty(T, wl.d, dtype=torch.bfloat16, device=DEV)
+    M.moe_combine(desc, yp, inv, fused["topk_gate"], ysh, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, fused["y"])
+    # the gathered codes are the 1x128 quantization of the gathered bf16 rows
+    rq, rs = O.quantize_rows_1x128(host(P["x"])[host(perm)])
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def v3fp8():
+    wl = CONFIGS["v3_fp8"]
+    print("generating v3 layer (bf16 weights, quantized by the library)", flush=True)
+    P = make_inputs(wl, DEV)
+    return wl, P, M.MoELayer(wl, P)
+
+
+def test_v3_fp8_sampled_tokens(v3fp8):
+    wl, P, layer = v3fp8
+    out = layer.forward(P["x"])
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    rr = O.route(g["logits"], host(layer.bias), **route_args(wl))
+    assert np.array_equal(g["topk_idx"], rr.idx)
+    assert np.array_equal(g["topk_gate"].view(np.uint32), rr.gate.view(np.uint32))
+    # tokens that share experts with token 0 keep the oracle's quantization work small
+    share = np.array([len(set(rr.idx[t]) & set(rr.idx[0])) for t in range(wl.T)])
+    rows = np.argsort(-share, kind="stable")[:8]
+    print(f"  fp8 v3: {len(np.unique(rr.idx[rows]))} experts for {len(rows)} tokens", flush=True)
+    ref = oracle_fp8(wl, P, host(P["x"])[rows], rr.idx[rows], rr.gate[rows])
+    err = row_rel_err(g["y"][rows], ref)
+    print(f"  fp8 v3 max row-rel err {err:.3e}", flush=True)
+    assert err <= TOL["fp8"]
+
+
+def test_v3_load_balancing_loop(v3fp8):
+    """100 steps of forward + bias update (gamma = 0.001) on fresh Zipf batches:
+    every step's counts equal the oracle's count of the kernel's selections and
+    the bias follows the oracle's update rule bit for bit; on steps 0, 50 and
+    99 the whole routing is re-derived by the oracle from the kernel's logits.
+    The max/mean load must fall."""
+    wl, P, layer = v3fp8
+    layer.bias.copy_(P["bias"])
+    ratios = []
+    b = host(layer.bias)
+    for s in range(100):
+        x = make_tokens(wl, wl.T, 1000 + s, DEV)
+        out = layer.forward(x, with_logits=s in (0, 50, 99))
+        layer.bias_update(out["counts"], wl.T)
+        torch.cuda.synchronize()
+        idx, counts = host(out["topk_idx"]), host(out["counts"])
+        assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=wl.E))
+        if s in (0, 50, 99):
+            rr = O.route(host(out["logits"]), b, **route_args(wl))
+            assert np.array_equal(idx, rr.idx), s
+        b = O.bias_update(b, counts, wl.gamma, wl.T, wl.K)
+        assert np.array_equal(host(layer.bias).view(np.uint32), b.view(np.uint32)), s
+        ratios.append(counts.max() / (wl.T * wl.K / wl.E))
+        if s % 20 == 0:
+            print(f"  step {s}: max/mean load {ratios[-1]:.3f}", flush=True)
+    print(f"  max/mean load: first {ratios[0]:.3f}, last {ratios[-1]:.3f}", flush=True)
+    assert np.mean(ratios[-10:]) < ratios[0]

@@ -397,3 +397,29 @@ def test_fp8_layer_lossless_when_values_are_on_the_grid():
     hq, hs = O.quantize_rows_1x128(h.astype(F32))
     ref = O.dequant_rows_1x128(hq, hs) @ w2.T.astype(np.float64)
     np.testing.assert_allclose(y8, ref, rtol=0, atol=0)
+
+
+def test_vectorized_block_quantizer_equals_per_block_rule():
+    """The all-blocks-at-once weight quantizer applies _quant_block's rule."""
+    rng = np.random.default_rng(16)
+    W = rng.normal(0, 0.02, (256, 384)).astype(F32)
+    W[:128, 128:256] = 0.0
+    W[200, 5] = 7.5
+    q, s = O.quantize_blocks_128(W)
+    for i in range(2):
+        for j in range(3):
+            rq, rs = O.moe_oracle._quant_block(W[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128])
+            assert np.array_equal(q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], rq)
+            assert s[i, j] == rs
+
+
+def test_e4m3_arithmetic_encoder_equals_table_search():
+    """The arithmetic encoder agrees with the nearest-code table search on
+    random values across every binade, the subnormals, exact midpoints and
+    saturation."""
+    rng = np.random.default_rng(17)
+    v = (rng.normal(size=300000) * np.exp2(rng.uniform(-14, 10, 300000))).astype(F32)
+    vals = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8)).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(F32)
+    v = np.concatenate([v, mids, -mids, np.float32([0.0, -0.0, 448.0, 464.0, 1e9, -1e9, 2.0 ** -10])])
+    assert np.array_equal(O.e4m3_encode(v), O.e4m3_encode_table(v))
