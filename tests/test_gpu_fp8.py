@@ -26,6 +26,7 @@ class LazyQuant:
     def get(self, e):
         e = int(e)
         if e not in self.cache:
+            print(f"    oracle quantizes expert {e}", flush=True)
             self.cache[e] = O.quantize_blocks_128(host(self.t[e]))
         return self.cache[e]
 
