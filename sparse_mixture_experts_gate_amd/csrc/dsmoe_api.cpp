@@ -85,6 +85,19 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_ERR_UNSUPPORTED, "d, inter, shared_inter must be multiples of %d", mult);
   if (d->T * static_cast<int64_t>(d->top_k) + d->T >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*(K+1) must be < 2^31");
+  // the GEMMs address x, H and each expert's weights with 32-bit byte offsets
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  const int64_t s_act = d->act_dtype == MOE_DT_F32 ? 4 : 2;
+  const int64_t s_w = d->w_dtype == MOE_DT_F32 ? 4 : d->w_dtype == MOE_DT_BF16 ? 2 : 1;
+  const int64_t ldh = std::max(d->inter, d->shared_inter);
+  if (d->T * d->d * s_act > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*d*sizeof(act) must be < 2^31 bytes");
+  if ((d->T * d->top_k + d->T) * ldh * s_w > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*max(I,Is)*sizeof(H) must be < 2^31 bytes");
+  if (int64_t(2) * ldh * d->d * s_w > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's weights must be < 2^31 bytes");
+  if (int64_t(d->n_experts) * 3 * d->d * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "E*3*d*2 must be < 2^31 bytes");
   return MOE_OK;
 }
 
@@ -124,8 +137,7 @@ GateLayout gate_layout(const moe_layer_desc* d) {
 struct FfnLayout {
   GemmTiling tiling;
   int ldh;
-  int64_t max_tiles1, max_tiles2;
-  size_t tiles1, tiles2, tmap1, tmap2, xq, xs, H, Hs, bytes;
+  size_t tiles1, tiles2, xq, xs, H, Hs, bytes;
 };
 
 FfnLayout ffn_layout(const moe_layer_desc* d) {
@@ -134,19 +146,9 @@ FfnLayout ffn_layout(const moe_layer_desc* d) {
   const int E = d->n_experts;
   L.tiling = choose_tiling(T, d->top_k, E, d->w_dtype);
   L.ldh = std::max(d->inter, d->shared_inter);
-  const GemmTiling& t = L.tiling;
-  const int64_t nt1 = (d->inter + t.bnh1 - 1) / t.bnh1;
-  const int64_t nts1 = (d->shared_inter + t.bnh1 - 1) / t.bnh1;
-  const int64_t nt2 = (d->d + t.bn2 - 1) / t.bn2;
-  // sum_e ceil(c_e / bm) <= TK / bm + E (rounded up)
-  L.max_tiles1 = ((TK + t.bm1 - 1) / t.bm1 + E) * nt1 + ((T + t.bm1 - 1) / t.bm1) * nts1;
-  L.max_tiles2 = ((TK + t.bm2 - 1) / t.bm2 + E) * nt2 +
-                 (d->shared_inter > 0 ? ((T + t.bm2 - 1) / t.bm2) * nt2 : 0);
   Carver c;
   L.tiles1 = c.take(sizeof(int32_t) * (E + 2));
   L.tiles2 = c.take(sizeof(int32_t) * (E + 2));
-  L.tmap1 = c.take(sizeof(int32_t) * size_t(L.max_tiles1));
-  L.tmap2 = c.take(sizeof(int32_t) * size_t(L.max_tiles2));
   const bool fp8 = d->w_dtype == MOE_DT_FP8_E4M3;
   L.xq = c.take(fp8 ? size_t(T) * d->d : 0);
   L.xs = c.take(fp8 ? sizeof(float) * size_t(T) * (d->d / 128) : 0);
@@ -292,14 +294,10 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   if (d->T == 0) return MOE_OK;
   int32_t* tiles1 = at<int32_t>(ws, L.tiles1);
   int32_t* tiles2 = at<int32_t>(ws, L.tiles2);
-  int32_t* tmap1 = at<int32_t>(ws, L.tmap1);
-  int32_t* tmap2 = at<int32_t>(ws, L.tmap2);
   FfnArgs a{};
   a.offsets = offsets;
   a.tiles1 = tiles1;
   a.tiles2 = tiles2;
-  a.tmap1 = tmap1;
-  a.tmap2 = tmap2;
   a.T = d->T;
   a.TK = d->T * d->top_k;
   a.E = d->n_experts;
@@ -323,8 +321,7 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   a.yperm = y_perm;
   a.yshared = y_shared;
   if (!planned)
-    HIP_TRY(launch_plan(nullptr, offsets, nullptr, tiles1, tiles2, tmap1, tmap2,
-                        plan_params(d, L.tiling), s),
+    HIP_TRY(launch_plan(nullptr, offsets, nullptr, tiles1, tiles2, plan_params(d, L.tiling), s),
             "plan");
   if (d->w_dtype == MOE_DT_FP8_E4M3) {
     uint8_t* xq = at<uint8_t>(ws, L.xq);
@@ -442,7 +439,7 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* topk_idx,
   }
   PlanParams pp = plan_params(desc, choose_tiling(desc->T, desc->top_k, desc->n_experts,
                                                   desc->w_dtype));
-  HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, nullptr, nullptr, pp, stream),
+  HIP_TRY(launch_plan(counts, nullptr, offsets, nullptr, nullptr, pp, stream),
           "offsets");
   if (desc->T == 0) return MOE_OK;
   HIP_TRY(launch_permute(topk_idx, offsets, desc->T, desc->top_k, desc->n_experts, perm, inv,
@@ -482,6 +479,11 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* w, cons
   } else {
     st = check_ptrs({{x_perm, "x_perm"}});
     if (st) return st;
+  }
+  if (x_perm) {
+    const int64_t s = desc->w_dtype == MOE_DT_FP8_E4M3 ? 1 : io_bytes(desc);
+    if (desc->T * desc->top_k * desc->d * s > (int64_t(1) << 31) - 1)
+      return fail(MOE_ERR_UNSUPPORTED, "T*K*d*sizeof(x_perm) must be < 2^31 bytes");
   }
   if (desc->shared_inter > 0) {
     st = check_ptrs({{y_shared, "y_shared"}});
@@ -556,8 +558,7 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
   if (st) return st;
   HIP_TRY(prof_record(1, stream), "profile event");
   HIP_TRY(launch_plan(counts, nullptr, offsets, at<int32_t>(fws, L.ffn.tiles1),
-                      at<int32_t>(fws, L.ffn.tiles2), at<int32_t>(fws, L.ffn.tmap1),
-                      at<int32_t>(fws, L.ffn.tmap2), plan_params(desc, L.ffn.tiling), stream),
+                      at<int32_t>(fws, L.ffn.tiles2), plan_params(desc, L.ffn.tiling), stream),
           "plan");
   HIP_TRY(launch_permute(topk_idx, offsets, desc->T, desc->top_k, desc->n_experts, perm, inv,
                          stream),

@@ -16,12 +16,15 @@
 // the same XCD and hit in its L2.
 #include "device_common.h"
 #include "internal.h"
+#include "tile_schedule.h"
 
 namespace dsmoe {
 
 namespace {
 
 constexpr int BK = 64;  // k elements per stage: 128 bytes per row
+
+constexpr int kPrefetch = 2;  // global loads run this many k-steps ahead
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
@@ -34,16 +37,24 @@ struct Tile {
   static constexpr int A_LOADS = BM / RPP;
   static constexpr int B_LOADS = BN / RPP;
   static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+  // waves per SIMD the register budget is sized for
+  static constexpr int MINW = (WM * WN >= 64 * 128) ? 1 : 2;
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA sub-tiles");
+  static_assert(BM * (BN + 8) <= LDS_ELEMS, "the output tile fits in the LDS stages");
 };
 
-using TilePrefill = Tile<128, 128, 64, 64>;  // 4 waves, 64 KB LDS
+using TilePrefill = Tile<128, 256, 64, 64>;  // 8 waves, 96 KB LDS
 using TileDecode = Tile<32, 128, 32, 64>;    // 2 waves, 40 KB LDS
 
-// LDS element offset of 16-byte chunk `ch` (0..7) of row `r`.
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * BK + ((ch ^ (r & 7)) << 3); }
+// LDS element offset of 16-byte chunk `ch` (0..7) of row `r`. The chunk is
+// XOR-swizzled with (r >> 1) & 7: the 16 lanes that one 128-bit LDS access
+// serves together read 16 consecutive rows at one logical chunk, and with two
+// 128-byte rows per 64-bank line this spreads them over all 64 banks.
+__device__ __forceinline__ int lds_off(int r, int ch) {
+  return r * BK + ((ch ^ ((r >> 1) & 7)) << 3);
+}
 
 template <class C, bool SWIGLU>
 __device__ __forceinline__ int b_local_row(int wn, int nj) {
@@ -55,16 +66,37 @@ __device__ __forceinline__ int b_local_row(int wn, int nj) {
   }
 }
 
-// acc[mi][nj] += A(rows of arow) * B(rows of brow)^T over k in [k_begin, k_end).
-// Row pointers are per thread (the rows this thread loads); nullptr rows read
-// as zeros. With a_kmod != 0 the A column is k mod a_kmod (router: the same
-// activations meet the three weight terms).
-template <class C, bool SWIGLU>
-__device__ __forceinline__ void gemm_tile(uint16_t* lds, const uint16_t* const (&arow)[C::A_LOADS],
-                                          const uint16_t* const (&brow)[C::B_LOADS], int k_begin,
-                                          int k_end, int a_kmod,
+// acc[mi][nj] += A * B^T over k in [k_begin, k_end) (multiples of 64).
+// Operands are read with buffer loads: one resource per operand and a 32-bit
+// byte offset per thread and row (the k = 0 element of the row). Offsets at
+// or beyond the resource size (kInvalidRow) read as zeros in hardware, so
+// padding rows cost no branches. With a_kmod != 0 the A column is k mod a_kmod
+// (router: the same activations meet the three weight terms). rows_valid is
+// informational: padded rows are multiplied as zeros, which keeps the tiles
+// that share a weight slab in step (skipping them lets those tiles drift apart
+// and lose the slab from L2).
+//
+// PD = 1: the next k-step's loads are in flight while this one computes.
+// PD = 2: two k-steps ahead, in two register sets (loop unrolled by two).
+// LDS is double buffered, one barrier per k-step; within a k-step the LDS
+// fragments of the next 16-wide sub-step are read while the current one
+// multiplies.
+
+template <class C>
+struct Stage {
+  uint4 a[C::A_LOADS];
+  uint4 b[C::B_LOADS];
+};
+
+template <class C, bool SWIGLU, int PD>
+__device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t ra,
+                                          const uint32_t (&aoff)[C::A_LOADS],
+                                          __amdgpu_buffer_rsrc_t rb,
+                                          const uint32_t (&boff)[C::B_LOADS], int k_begin,
+                                          int k_end, int a_kmod, int rows_valid,
                                           f32x16_t (&acc)[C::MI][C::NJ]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int ch = tid & 7, r0 = tid >> 3;
 #pragma unroll
@@ -73,66 +105,97 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, const uint16_t* const (
     for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+  (void)rows_valid;
 
-  uint4 ra[C::A_LOADS], rb[C::B_LOADS];
-  auto gload = [&](int k0) {
-    const int kc = k0 + ch * 8;
-    const bool kin = kc < k_end;
-    const int ka = a_kmod ? (k0 % a_kmod) + ch * 8 : kc;
+  auto gload = [&](Stage<C>& R, int k0) {
+    const uint32_t kb = static_cast<uint32_t>(k0 + ch * 8) * 2u;
+    const uint32_t ka = a_kmod ? static_cast<uint32_t>(k0 % a_kmod + ch * 8) * 2u : kb;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p)
-      ra[p] = (arow[p] && kin) ? *reinterpret_cast<const uint4*>(arow[p] + ka)
-                               : make_uint4(0, 0, 0, 0);
+      R.a[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[p] + ka, 0, 0));
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
-      rb[p] = (brow[p] && kin) ? *reinterpret_cast<const uint4*>(brow[p] + kc)
-                               : make_uint4(0, 0, 0, 0);
+      R.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[p] + kb, 0, 0));
   };
-  auto sstore = [&](int st) {
+  auto sstore = [&](const Stage<C>& R, int st) {
     uint16_t* As = lds + st * C::STAGE;
     uint16_t* Bs = As + C::BM * BK;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p)
-      *reinterpret_cast<uint4*>(As + lds_off(r0 + p * C::RPP, ch)) = ra[p];
+      *reinterpret_cast<uint4*>(As + lds_off(r0 + p * C::RPP, ch)) = R.a[p];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
-      *reinterpret_cast<uint4*>(Bs + lds_off(r0 + p * C::RPP, ch)) = rb[p];
+      *reinterpret_cast<uint4*>(Bs + lds_off(r0 + p * C::RPP, ch)) = R.b[p];
   };
-
-  gload(k_begin);
-  sstore(0);
-  __syncthreads();
-  int st = 0;
-  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
-    const bool more = k0 + BK < k_end;
-    if (more) gload(k0 + BK);
+  auto compute = [&](int st) {
     const uint16_t* As = lds + st * C::STAGE;
     const uint16_t* Bs = As + C::BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    // fragments of sub-step kk+1 are read from LDS while sub-step kk multiplies
+    bf16x8_t af[2][C::MI], bfr[2][C::NJ];
+    auto fetch = [&](int kk, int buf) {
       const int chk = kk * 2 + (lane >> 5);
-      bf16x8_t af[C::MI], bfr[C::NJ];
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) {
-        const int r = wm * C::WM + mi * 32 + (lane & 31);
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(r, chk));
-      }
-#pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) {
-        const int r = b_local_row<C, SWIGLU>(wn, nj) + (lane & 31);
-        bfr[nj] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(r, chk));
-      }
+      for (int nj = 0; nj < C::NJ; ++nj)
+        bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
+            Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
+        af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
+            As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
         for (int nj = 0; nj < C::NJ; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bfr[kk & 1][nj],
+                                                                acc[mi][nj], 0, 0, 0);
+      }
     }
-    if (more) sstore(st ^ 1);
+  };
+
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  if constexpr (PD == 1) {
+    Stage<C> s0;
+    gload(s0, k_begin);
+    sstore(s0, 0);
     __syncthreads();
-    st ^= 1;
+    for (int k = 0; k < nk; ++k) {
+      const bool more = k + 1 < nk;
+      if (more) gload(s0, k_begin + (k + 1) * BK);
+      compute(k & 1);
+      if (more) sstore(s0, (k + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    Stage<C> s0, s1;
+    gload(s0, k_begin);
+    if (nk > 1) gload(s1, k_begin + BK);
+    sstore(s0, 0);
+    __syncthreads();
+    int k = 0;
+    for (; k + 2 <= nk; k += 2) {
+      // LDS 0 holds step k, s1 step k+1 (arriving), s0 is free
+      if (k + 2 < nk) gload(s0, k_begin + (k + 2) * BK);
+      compute(0);
+      sstore(s1, 1);
+      __syncthreads();
+      // LDS 1 holds step k+1, s0 step k+2 (arriving), s1 is free
+      if (k + 3 < nk) gload(s1, k_begin + (k + 3) * BK);
+      compute(1);
+      if (k + 2 < nk) sstore(s0, 0);
+      __syncthreads();
+    }
+    if (k < nk) {  // odd number of steps: the last one sits in LDS 0
+      compute(0);
+      __syncthreads();
+    }
   }
 }
+
 
 // Row (within the tile) of accumulator element r of a 32x32 sub-tile, for
 // this lane; the lane's column is lane % 32.
@@ -140,153 +203,161 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Per tile: group g, row range and column tile n of a grouped GEMM.
-struct TileCoord {
-  int g, rows, rbase, m, n;
-  bool shared;
-};
-
-__device__ __forceinline__ TileCoord tile_coord(const FfnArgs& a, const int32_t* tiles,
-                                                const int32_t* tmap, int tile, int bm) {
-  TileCoord c;
-  c.g = tmap[tile];
-  c.shared = c.g == a.E;
-  c.rbase = c.shared ? 0 : a.offsets[c.g];
-  c.rows = c.shared ? static_cast<int>(a.T) : a.offsets[c.g + 1] - c.rbase;
-  const int mt = (c.rows + bm - 1) / bm;
-  const int local = tile - tiles[c.g];
-  c.n = local / mt;
-  c.m = local % mt;
-  return c;
-}
-
 // H = silu(A W1^T) * (A W3^T) per group.
-template <class C>
-__global__ __launch_bounds__(C::NT) void ffn1_bf16_kernel(FfnArgs a) {
+template <class C, int PD>
+__global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ int gtab[kMaxGroups + 1];
   constexpr int HALF = C::BN / 2;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  const int total = a.tiles1[a.E + 1];
+  load_group_table(gtab, a.tiles1, a.E);
+  const int total = gtab[a.E + 1];
   const int nb = gridDim.x;
-  const uint16_t* X = static_cast<const uint16_t*>(a.perm ? a.x : a.xperm);
-  const uint16_t* Xs = static_cast<const uint16_t*>(a.x);
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const __amdgpu_buffer_rsrc_t rx =
+      a.perm ? buf_rsrc(a.x, static_cast<uint32_t>(a.T) * row_bytes)
+             : buf_rsrc(a.xperm, static_cast<uint32_t>(a.TK) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rxs = buf_rsrc(a.x, static_cast<uint32_t>(a.T) * row_bytes);
   uint16_t* H = static_cast<uint16_t*>(a.H);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    const TileCoord tc = tile_coord(a, a.tiles1, a.tmap1, tile, C::BM);
-    const int Ig = tc.shared ? a.Is : a.I;
-    const uint16_t* arow[C::A_LOADS];
+    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
+    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
+    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
+    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
+    const bool shared = tc.g == a.E;
+    const int Ig = shared ? a.Is : a.I;
+    const int rows_left = tc.rows - tc.m * C::BM;
+    uint32_t aoff[C::A_LOADS];
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int r = tc.m * C::BM + r0 + p * C::RPP;
-      const uint16_t* ptr = nullptr;
+      uint32_t off = kInvalidRow;
       if (r < tc.rows) {
-        if (tc.shared) {
-          ptr = Xs + static_cast<int64_t>(r) * a.d;
+        if (shared) {
+          off = static_cast<uint32_t>(r) * row_bytes;
         } else if (a.perm) {
           const int tok = a.perm[tc.rbase + r];
-          ptr = (tok >= 0 && tok < a.T) ? X + static_cast<int64_t>(tok) * a.d : nullptr;
-        } else
-          ptr = X + static_cast<int64_t>(tc.rbase + r) * a.d;
+          if (tok >= 0 && tok < a.T) off = static_cast<uint32_t>(tok) * row_bytes;
+        } else {
+          off = static_cast<uint32_t>(tc.rbase + r) * row_bytes;
+        }
       }
-      arow[p] = ptr;
+      aoff[p] = off;
     }
-    const uint16_t* W = tc.shared ? static_cast<const uint16_t*>(a.ws13)
-                                  : static_cast<const uint16_t*>(a.w13) +
-                                        static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
-    const uint16_t* brow[C::B_LOADS];
+    const uint16_t* W = shared ? static_cast<const uint16_t*>(a.ws13)
+                               : static_cast<const uint16_t*>(a.w13) +
+                                     static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(2 * Ig) * row_bytes);
+    uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
       const bool up = lr >= HALF;
       const int col = tc.n * HALF + (up ? lr - HALF : lr);
-      brow[p] = col < Ig ? W + static_cast<int64_t>(up ? Ig + col : col) * a.d : nullptr;
+      boff[p] = col < Ig ? static_cast<uint32_t>(up ? Ig + col : col) * row_bytes : kInvalidRow;
     }
     f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, true>(lds, arow, brow, 0, a.d, 0, acc);
+    gemm_tile<C, true, PD>(lds, shared ? rxs : rx, aoff, rw, boff, 0, a.d, 0, rows_left, acc);
 
-    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
-    const int rows_left = tc.rows - tc.m * C::BM;
+    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < C::NJ / 2; ++nj) {
-        const int col = tc.n * HALF + wn * (C::WN / 2) + nj * 32 + (lane & 31);
-        if (col >= Ig) continue;
+        const int col = wn * (C::WN / 2) + nj * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = wm * C::WM + mi * 32 + acc_row(lane, r);
-          if (lr < rows_left) {
-            const float h = silu_f32(acc[mi][nj][r]) * acc[mi][nj + C::NJ / 2][r];
-            H[(hrow0 + lr) * a.ldh + col] = f32_to_bf16(h);
-          }
+          const float h = silu_f32(acc[mi][nj][r]) * acc[mi][nj + C::NJ / 2][r];
+          out_put<C, HALF>(lds, wm * C::WM + mi * 32 + acc_row(lane, r), col, h);
         }
       }
+    __syncthreads();
+    out_flush<C, HALF>(lds, H + hrow0 * a.ldh + tc.n * HALF, a.ldh, rows_left,
+                       Ig - tc.n * HALF);
+    __syncthreads();
   }
 }
 
 // y = H W2^T per group: routed rows to y_perm, shared rows to y_shared.
-template <class C>
-__global__ __launch_bounds__(C::NT) void ffn2_bf16_kernel(FfnArgs a) {
+template <class C, int PD>
+__global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int gtab[kMaxGroups + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  const int total = a.tiles2[a.E + 1];
+  load_group_table(gtab, a.tiles2, a.E);
+  const int total = gtab[a.E + 1];
   const int nb = gridDim.x;
-  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+  const uint32_t hrow_bytes = static_cast<uint32_t>(a.ldh) * 2u;
+  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.H, static_cast<uint32_t>(hrows) * hrow_bytes);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    const TileCoord tc = tile_coord(a, a.tiles2, a.tmap2, tile, C::BM);
-    const int Ig = tc.shared ? a.Is : a.I;
-    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
+    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
+    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
+    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
+    const bool shared = tc.g == a.E;
+    const int Ig = shared ? a.Is : a.I;
+    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
     const int rows_left = tc.rows - tc.m * C::BM;
-    const uint16_t* arow[C::A_LOADS];
+    uint32_t aoff[C::A_LOADS];
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      arow[p] = lr < rows_left ? H + (hrow0 + lr) * a.ldh : nullptr;
+      aoff[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * hrow_bytes : kInvalidRow;
     }
-    const uint16_t* W = tc.shared ? static_cast<const uint16_t*>(a.ws2)
-                                  : static_cast<const uint16_t*>(a.w2) +
-                                        static_cast<int64_t>(tc.g) * a.d * a.I;
-    const uint16_t* brow[C::B_LOADS];
+    const uint16_t* W = shared ? static_cast<const uint16_t*>(a.ws2)
+                               : static_cast<const uint16_t*>(a.w2) +
+                                     static_cast<int64_t>(tc.g) * a.d * a.I;
+    const uint32_t wrow_bytes = static_cast<uint32_t>(Ig) * 2u;
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(a.d) * wrow_bytes);
+    uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int row = tc.n * C::BN + r0 + p * C::RPP;
-      brow[p] = row < a.d ? W + static_cast<int64_t>(row) * Ig : nullptr;
+      boff[p] = row < a.d ? static_cast<uint32_t>(row) * wrow_bytes : kInvalidRow;
     }
     f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, false>(lds, arow, brow, 0, Ig, 0, acc);
+    gemm_tile<C, false, PD>(lds, rh, aoff, rw, boff, 0, Ig, 0, rows_left, acc);
 
-    uint16_t* out = tc.shared ? static_cast<uint16_t*>(a.yshared) +
-                                    static_cast<int64_t>(tc.m) * C::BM * a.d
-                              : static_cast<uint16_t*>(a.yperm) +
-                                    (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
+    uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
+                                 static_cast<int64_t>(tc.m) * C::BM * a.d
+                           : static_cast<uint16_t*>(a.yperm) +
+                                 (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
       for (int nj = 0; nj < C::NJ; ++nj) {
-        const int col = tc.n * C::BN + wn * C::WN + nj * 32 + (lane & 31);
-        if (col >= a.d) continue;
+        const int col = wn * C::WN + nj * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = wm * C::WM + mi * 32 + acc_row(lane, r);
-          if (lr < rows_left) out[static_cast<int64_t>(lr) * a.d + col] = f32_to_bf16(acc[mi][nj][r]);
-        }
+        for (int r = 0; r < 16; ++r)
+          out_put<C, C::BN>(lds, wm * C::WM + mi * 32 + acc_row(lane, r), col, acc[mi][nj][r]);
       }
+    __syncthreads();
+    out_flush<C, C::BN>(lds, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
+    __syncthreads();
   }
 }
 
 // Router: partial[s][t][e] = sum over k-split s of x[t, k mod d] * wsplit[e, k],
 // k in [0, 3d). Grid: (m-tiles * n-tiles, splits).
 template <class C>
-__global__ __launch_bounds__(C::NT) void router_bf16_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ wsplit,
-                                                            int64_t T, int d, int E, int kchunk,
-                                                            float* __restrict__ partial) {
+__global__ __launch_bounds__(C::NT, C::MINW) void router_bf16_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wsplit,
+                                                               int64_t T, int d, int E, int kchunk,
+                                                               float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
   const int ntn = (E + C::BN - 1) / C::BN;
@@ -295,20 +366,24 @@ __global__ __launch_bounds__(C::NT) void router_bf16_kernel(const uint16_t* __re
   const int split = blockIdx.y;
   const int k_begin = split * kchunk;
   const int k_end = min(3 * d, k_begin + kchunk);
-  const uint16_t* arow[C::A_LOADS];
+  const uint32_t row_bytes = static_cast<uint32_t>(d) * 2u;
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, static_cast<uint32_t>(T) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wsplit, static_cast<uint32_t>(E) * 3u * row_bytes);
+  uint32_t aoff[C::A_LOADS];
 #pragma unroll
   for (int p = 0; p < C::A_LOADS; ++p) {
     const int64_t t = m * C::BM + r0 + p * C::RPP;
-    arow[p] = t < T ? x + t * d : nullptr;
+    aoff[p] = t < T ? static_cast<uint32_t>(t) * row_bytes : kInvalidRow;
   }
-  const uint16_t* brow[C::B_LOADS];
+  uint32_t boff[C::B_LOADS];
 #pragma unroll
   for (int p = 0; p < C::B_LOADS; ++p) {
     const int e = n * C::BN + r0 + p * C::RPP;
-    brow[p] = e < E ? wsplit + static_cast<int64_t>(e) * 3 * d : nullptr;
+    boff[p] = e < E ? static_cast<uint32_t>(e) * 3u * row_bytes : kInvalidRow;
   }
   f32x16_t acc[C::MI][C::NJ];
-  gemm_tile<C, false>(lds, arow, brow, k_begin, k_end, d, acc);
+  gemm_tile<C, false, kPrefetch>(lds, rx, aoff, rw, boff, k_begin, k_end, d,
+                         static_cast<int>(min<int64_t>(T - m * C::BM, C::BM)), acc);
   float* out = partial + static_cast<int64_t>(split) * T * E;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
@@ -353,20 +428,20 @@ int occupancy_blocks(K kernel, int threads) {
   return nb;
 }
 
-template <class C>
+template <class C, int PD1, int PD2>
 hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
-  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C>, C::NT);
-  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C>, C::NT);
+  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C, PD1>, C::NT);
+  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C, PD2>, C::NT);
   const int cus = device_cu_count();
   // persistent grids, multiples of 8 for the XCD remap
   const int g1 = ((cus * occ1 + 7) / 8) * 8;
   const int g2 = ((cus * occ2 + 7) / 8) * 8;
-  hipLaunchKernelGGL(ffn1_bf16_kernel<C>, dim3(g1), dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn1_bf16_kernel<C, PD1>), dim3(g1), dim3(C::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL(ffn2_bf16_kernel<C>, dim3(g2), dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn2_bf16_kernel<C, PD2>), dim3(g2), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -394,8 +469,8 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
-  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode>(a, s, mid);
-  return launch_ffn_bf16_cfg<TilePrefill>(a, s, mid);
+  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, kPrefetch, kPrefetch>(a, s, mid);
+  return launch_ffn_bf16_cfg<TilePrefill, kPrefetch, kPrefetch>(a, s, mid);
 }
 
 int router_splits(int64_t T, int d, int E, int act_dtype) {

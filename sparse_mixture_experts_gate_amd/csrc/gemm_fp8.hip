@@ -17,6 +17,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "tile_schedule.h"
 
 namespace dsmoe {
 
@@ -44,7 +45,11 @@ using T8Down = Tile8<128, 128, 64, 64>;     // 4 waves, 64 KB LDS
 using T8GateDec = Tile8<32, 256, 32, 64>;   // 4 waves
 using T8DownDec = Tile8<32, 128, 32, 64>;   // 2 waves
 
-__device__ __forceinline__ int lds_off8(int r, int ch) { return r * BK8 + ((ch ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk `ch` of row `r`, swizzled with (r >> 1) & 7 so
+// that the 16 rows one 128-bit LDS access serves spread over all 64 banks.
+__device__ __forceinline__ int lds_off8(int r, int ch) {
+  return r * BK8 + ((ch ^ ((r >> 1) & 7)) << 4);
+}
 
 template <class C, bool SWIGLU>
 __device__ __forceinline__ int b_row8(int wn, int nj) {
@@ -69,54 +74,60 @@ __device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
 //   (A_kb B_kb^T) * s_a[row][kb] * s_b[kb]   (s_b: sb_lo for the first half of
 // the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
 // sa_row: this thread's row scale pointer when threadIdx.x < BM (else unused).
+// Operands come through buffer resources (padding rows read as zeros); global
+// loads run two k blocks ahead in two register sets; LDS is double buffered.
+template <class C>
+struct Stage8 {
+  uint4 a[C::A_LOADS];
+  uint4 b[C::B_LOADS];
+  float sa;
+};
+
 template <class C, bool SWIGLU>
 __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
-                                           const uint8_t* const (&arow)[C::A_LOADS],
-                                           const float* sa_row,
-                                           const uint8_t* const (&brow)[C::B_LOADS],
+                                           __amdgpu_buffer_rsrc_t ra,
+                                           const uint32_t (&aoff)[C::A_LOADS],
+                                           const float* sa_row, __amdgpu_buffer_rsrc_t rb,
+                                           const uint32_t (&boff)[C::B_LOADS],
                                            const float* sb_lo, const float* sb_hi, int K,
-                                           f32x4_t (&acc)[C::MI][C::NJ]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                           int rows_valid, f32x4_t (&acc)[C::MI][C::NJ]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int ch = tid & 7, r0 = tid >> 3;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // 16-row groups entirely beyond rows_valid skip their MFMAs; the branch also
+  // keeps the compiler from hoisting every row group's MFMAs at once
+  bool mi_on[C::MI];
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) mi_on[mi] = wm * C::WM + mi * 16 < rows_valid;
 
-  uint4 ra[C::A_LOADS], rb[C::B_LOADS];
-  float rsa = 0.0f;
-  auto gload = [&](int kb) {
-    const int off = kb * BK8 + ch * 16;
+  auto gload = [&](Stage8<C>& R, int kb) {
+    const uint32_t off = static_cast<uint32_t>(kb * BK8 + ch * 16);
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p)
-      ra[p] = arow[p] ? *reinterpret_cast<const uint4*>(arow[p] + off) : make_uint4(0, 0, 0, 0);
+      R.a[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[p] + off, 0, 0));
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
-      rb[p] = brow[p] ? *reinterpret_cast<const uint4*>(brow[p] + off) : make_uint4(0, 0, 0, 0);
-    if (tid < C::BM) rsa = sa_row ? sa_row[kb] : 0.0f;
+      R.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[p] + off, 0, 0));
+    R.sa = (tid < C::BM && sa_row) ? sa_row[kb] : 0.0f;
   };
-  auto sstore = [&](int st) {
+  auto sstore = [&](const Stage8<C>& R, int st) {
     uint8_t* As = lds + st * C::STAGE;
     uint8_t* Bs = As + C::BM * BK8;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p)
-      *reinterpret_cast<uint4*>(As + lds_off8(r0 + p * C::RPP, ch)) = ra[p];
+      *reinterpret_cast<uint4*>(As + lds_off8(r0 + p * C::RPP, ch)) = R.a[p];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
-      *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = rb[p];
-    if (tid < C::BM) lds_sa[st * C::BM + tid] = rsa;
+      *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = R.b[p];
+    if (tid < C::BM) lds_sa[st * C::BM + tid] = R.sa;
   };
-
-  const int nkb = K / BK8;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  int st = 0;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) gload(kb + 1);
+  auto compute = [&](int st, int kb) {
     const float s_lo = sb_lo[kb];
     const float s_hi = SWIGLU ? sb_hi[kb] : s_lo;
     const uint8_t* As = lds + st * C::STAGE;
@@ -127,6 +138,7 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
     for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
+      if (!mi_on[mi]) continue;
       const int rbase = wm * C::WM + mi * 16;
       const i32x8_t af = frag8(As, rbase + (lane & 15), kg);
       const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::BM + rbase + 4 * kg);
@@ -145,100 +157,106 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
         for (int r = 0; r < 4; ++r) acc[mi][nj][r] = __builtin_fmaf(p[r], lo ? s_l[r] : s_h[r], acc[mi][nj][r]);
       }
     }
-    if (more) sstore(st ^ 1);
+  };
+
+  const int nk = K / BK8;
+  Stage8<C> s0, s1;
+  gload(s0, 0);
+  if (nk > 1) gload(s1, 1);
+  sstore(s0, 0);
+  __syncthreads();
+  int k = 0;
+  for (; k + 2 <= nk; k += 2) {
+    if (k + 2 < nk) gload(s0, k + 2);
+    compute(0, k);
+    sstore(s1, 1);
     __syncthreads();
-    st ^= 1;
+    if (k + 3 < nk) gload(s1, k + 3);
+    compute(1, k + 1);
+    if (k + 2 < nk) sstore(s0, 0);
+    __syncthreads();
   }
-}
-
-struct TileCoord8 {
-  int g, rows, rbase, m, n;
-  bool shared;
-};
-
-__device__ __forceinline__ TileCoord8 tile_coord8(const FfnArgs& a, const int32_t* tiles,
-                                                  const int32_t* tmap, int tile, int bm) {
-  TileCoord8 c;
-  c.g = tmap[tile];
-  c.shared = c.g == a.E;
-  c.rbase = c.shared ? 0 : a.offsets[c.g];
-  c.rows = c.shared ? static_cast<int>(a.T) : a.offsets[c.g + 1] - c.rbase;
-  const int mt = (c.rows + bm - 1) / bm;
-  const int local = tile - tiles[c.g];
-  c.n = local / mt;
-  c.m = local % mt;
-  return c;
+  if (k < nk) {
+    compute(0, k);
+    __syncthreads();
+  }
 }
 
 // H (E4M3 + 1x128 scales) = quant(silu(A W1^T) * (A W3^T)); tile = 128 H columns.
 template <class C>
-__global__ __launch_bounds__(C::NT) void ffn1_fp8_kernel(FfnArgs a) {
+__global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
   __shared__ float red[C::WAVES_N][C::BM];
+  __shared__ int gtab[kMaxGroups + 1];
   constexpr int HALF = C::BN / 2;  // 128 H columns
   static_assert(HALF == 128, "one 1x128 quantization tile of H per tile");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  const int total = a.tiles1[a.E + 1];
+  load_group_table(gtab, a.tiles1, a.E);
+  const int total = gtab[a.E + 1];
   const int nb = gridDim.x;
   const int dkb = a.d / 128;
   const int hkb = a.ldh / 128;
-  const uint8_t* X = static_cast<const uint8_t*>(a.perm ? a.x : a.xperm);
   const float* XS = a.perm ? a.x_scale : a.xperm_scale;
-  const uint8_t* Xsh = static_cast<const uint8_t*>(a.x);
+  const __amdgpu_buffer_rsrc_t rx =
+      a.perm ? buf_rsrc(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d))
+             : buf_rsrc(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
+  const __amdgpu_buffer_rsrc_t rxs =
+      buf_rsrc(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
   uint8_t* H = static_cast<uint8_t*>(a.H);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    const TileCoord8 tc = tile_coord8(a, a.tiles1, a.tmap1, tile, C::BM);
-    const int Ig = tc.shared ? a.Is : a.I;
-    auto src_row = [&](int r, const uint8_t** p, const float** s) {
-      *p = nullptr;
-      *s = nullptr;
-      if (r >= tc.rows) return;
-      int64_t row;
-      const uint8_t* base;
-      const float* sbase;
-      if (tc.shared) {
-        row = r; base = Xsh; sbase = a.x_scale;
-      } else if (a.perm) {
-        row = a.perm[tc.rbase + r];
-        if (row < 0 || row >= a.T) return;
-        base = X; sbase = XS;
-      } else {
-        row = tc.rbase + r; base = X; sbase = XS;
+    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
+    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
+    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
+    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
+    const bool shared = tc.g == a.E;
+    const int Ig = shared ? a.Is : a.I;
+    // A rows: gathered token rows of the quantized x (or rows of x_perm); the
+    // shared expert reads x's rows in order
+    auto src_row = [&](int r) -> int64_t {
+      if (r >= tc.rows) return -1;
+      if (shared) return r;
+      if (a.perm) {
+        const int tok = a.perm[tc.rbase + r];
+        return (tok >= 0 && tok < a.T) ? tok : -1;
       }
-      *p = base + row * a.d;
-      *s = sbase + row * dkb;
+      return tc.rbase + r;
     };
-    const uint8_t* arow[C::A_LOADS];
+    uint32_t aoff[C::A_LOADS];
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
-      const float* dummy;
-      src_row(tc.m * C::BM + r0 + p * C::RPP, &arow[p], &dummy);
+      const int64_t row = src_row(tc.m * C::BM + r0 + p * C::RPP);
+      aoff[p] = row >= 0 ? static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) : kInvalidRow;
     }
     const float* sa_row = nullptr;
     if (tid < C::BM) {
-      const uint8_t* dummy;
-      src_row(tc.m * C::BM + tid, &dummy, &sa_row);
+      const int64_t row = src_row(tc.m * C::BM + tid);
+      if (row >= 0) sa_row = (shared ? a.x_scale : XS) + row * dkb;
     }
-    const uint8_t* W = tc.shared ? static_cast<const uint8_t*>(a.ws13)
-                                 : static_cast<const uint8_t*>(a.w13) +
-                                       static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
-    const float* WS = tc.shared ? a.ws13_scale
-                                : a.w13_scale + static_cast<int64_t>(tc.g) * (2 * a.I / 128) * dkb;
-    const uint8_t* brow[C::B_LOADS];
+    const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws13)
+                              : static_cast<const uint8_t*>(a.w13) +
+                                    static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
+    const float* WS = shared ? a.ws13_scale
+                             : a.w13_scale + static_cast<int64_t>(tc.g) * (2 * a.I / 128) * dkb;
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(2 * Ig) * a.d);
+    uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
       const bool up = lr >= HALF;
       const int col = tc.n * HALF + (up ? lr - HALF : lr);
-      brow[p] = W + static_cast<int64_t>(up ? Ig + col : col) * a.d;
+      boff[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
     }
     const float* sb_gate = WS + static_cast<int64_t>(tc.n) * dkb;
     const float* sb_up = WS + static_cast<int64_t>(Ig / 128 + tc.n) * dkb;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, true>(lds, lds_sa, arow, sa_row, brow, sb_gate, sb_up, a.d, acc);
+    gemm8_tile<C, true>(lds, lds_sa, shared ? rxs : rx, aoff, sa_row, rw, boff, sb_gate, sb_up,
+                        a.d, tc.rows - tc.m * C::BM, acc);
 
     // SwiGLU, then the row max-abs over the 128 columns (across the wave's
     // 16-lane groups and the tile's WAVES_N waves)
@@ -266,8 +284,12 @@ __global__ __launch_bounds__(C::NT) void ffn1_fp8_kernel(FfnArgs a) {
         for (int r = 0; r < 4; ++r) red[wn][wm * C::WM + mi * 16 + 4 * (lane >> 4) + r] = pm[mi][r];
     }
     __syncthreads();
-    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
     const int rows_left = tc.rows - tc.m * C::BM;
+    // E4M3 codes of the 128 x 128 H tile are staged in LDS (rows padded by 16
+    // bytes), then leave as 16-byte stores
+    constexpr int HSTR = HALF + 16;
+    static_assert(C::BM * HSTR <= 2 * C::STAGE, "the H tile fits in the LDS stages");
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -276,78 +298,97 @@ __global__ __launch_bounds__(C::NT) void ffn1_fp8_kernel(FfnArgs a) {
         float amax = red[0][lr];
 #pragma unroll
         for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
-        if (lr >= rows_left) continue;
         const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
-        uint8_t* hrow = H + (hrow0 + lr) * a.ldh + tc.n * HALF;
 #pragma unroll
         for (int nj = 0; nj < NJH; ++nj) {
           const int col = wn * (C::WN / 2) + nj * 16 + (lane & 15);
           const uint32_t q = amax == 0.0f ? 0u : e4m3_pack4(h[mi][nj][r] * inv, 0.f, 0.f, 0.f);
-          hrow[col] = static_cast<uint8_t>(q & 0xFFu);
+          lds[lr * HSTR + col] = static_cast<uint8_t>(q & 0xFFu);
         }
-        if (wn == 0 && (lane & 15) == 0)
+        if (wn == 0 && (lane & 15) == 0 && lr < rows_left)
           a.H_scale[(hrow0 + lr) * hkb + tc.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
       }
+    __syncthreads();
+    for (int i = tid; i < C::BM * (HALF / 16); i += C::NT) {
+      const int row = i / (HALF / 16), c = (i % (HALF / 16)) * 16;
+      if (row < rows_left)
+        *reinterpret_cast<uint4*>(H + (hrow0 + row) * a.ldh + tc.n * HALF + c) =
+            *reinterpret_cast<const uint4*>(lds + row * HSTR + c);
+    }
     __syncthreads();  // red[] is rewritten by the next tile
   }
 }
 
 // y = dequant(H) dequant(W2)^T per group, bf16 out.
 template <class C>
-__global__ __launch_bounds__(C::NT) void ffn2_fp8_kernel(FfnArgs a) {
+__global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int gtab[kMaxGroups + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  const int total = a.tiles2[a.E + 1];
+  load_group_table(gtab, a.tiles2, a.E);
+  const int total = gtab[a.E + 1];
   const int nb = gridDim.x;
   const int hkb = a.ldh / 128;
-  const uint8_t* H = static_cast<const uint8_t*>(a.H);
+  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
+  const __amdgpu_buffer_rsrc_t rh =
+      buf_rsrc(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    const TileCoord8 tc = tile_coord8(a, a.tiles2, a.tmap2, tile, C::BM);
-    const int Ig = tc.shared ? a.Is : a.I;
-    const int64_t hrow0 = (tc.shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
+    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
+    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
+    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
+    const bool shared = tc.g == a.E;
+    const int Ig = shared ? a.Is : a.I;
+    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
     const int rows_left = tc.rows - tc.m * C::BM;
-    const uint8_t* arow[C::A_LOADS];
+    uint32_t aoff[C::A_LOADS];
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      arow[p] = lr < rows_left ? H + (hrow0 + lr) * a.ldh : nullptr;
+      aoff[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * static_cast<uint32_t>(a.ldh)
+                               : kInvalidRow;
     }
     const float* sa_row = (tid < C::BM && tid < rows_left) ? a.H_scale + (hrow0 + tid) * hkb : nullptr;
-    const uint8_t* W = tc.shared ? static_cast<const uint8_t*>(a.ws2)
-                                 : static_cast<const uint8_t*>(a.w2) +
-                                       static_cast<int64_t>(tc.g) * a.d * a.I;
+    const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws2)
+                              : static_cast<const uint8_t*>(a.w2) +
+                                    static_cast<int64_t>(tc.g) * a.d * a.I;
     const int ikb = Ig / 128;
-    const float* WS = tc.shared ? a.ws2_scale
-                                : a.w2_scale + static_cast<int64_t>(tc.g) * (a.d / 128) * (a.I / 128);
-    const uint8_t* brow[C::B_LOADS];
+    const float* WS = shared ? a.ws2_scale
+                             : a.w2_scale + static_cast<int64_t>(tc.g) * (a.d / 128) * (a.I / 128);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(a.d) * static_cast<uint32_t>(Ig));
+    uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int row = tc.n * C::BN + r0 + p * C::RPP;
-      brow[p] = row < a.d ? W + static_cast<int64_t>(row) * Ig : nullptr;
+      boff[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
     }
     const float* sb = WS + static_cast<int64_t>((tc.n * C::BN) / 128) * ikb;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, false>(lds, lds_sa, arow, sa_row, brow, sb, sb, Ig, acc);
+    gemm8_tile<C, false>(lds, lds_sa, rh, aoff, sa_row, rw, boff, sb, sb, Ig, rows_left, acc);
 
-    uint16_t* out = tc.shared ? static_cast<uint16_t*>(a.yshared) +
-                                    static_cast<int64_t>(tc.m) * C::BM * a.d
-                              : static_cast<uint16_t*>(a.yperm) +
-                                    (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
+    uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
+                                 static_cast<int64_t>(tc.m) * C::BM * a.d
+                           : static_cast<uint16_t*>(a.yperm) +
+                                 (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
+    uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
+    static_assert(C::BM * (C::BN + 8) * 2 <= 2 * C::STAGE, "the output tile fits in the LDS stages");
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) {
-        const int col = tc.n * C::BN + wn * C::WN + nj * 16 + (lane & 15);
-        if (col >= a.d) continue;
+      for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = wm * C::WM + mi * 16 + 4 * (lane >> 4) + r;
-          if (lr < rows_left) out[static_cast<int64_t>(lr) * a.d + col] = f32_to_bf16(acc[mi][nj][r]);
-        }
-      }
+        for (int r = 0; r < 4; ++r)
+          out_put<C, C::BN>(ot, wm * C::WM + mi * 16 + 4 * (lane >> 4) + r,
+                            wn * C::WN + nj * 16 + (lane & 15), acc[mi][nj][r]);
+    __syncthreads();
+    out_flush<C, C::BN>(ot, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
+    __syncthreads();
   }
 }
 

@@ -41,11 +41,9 @@ struct PlanParams {
   int bm2, bn2;   // GEMM2 rows per tile, output columns per tile
 };
 // counts != NULL: offsets_out = exclusive scan of counts. Else offsets_in is
-// used. tiles1/tiles2 may be NULL.
-// tmap1/tmap2 receive the group of every tile (may be NULL).
+// used. tiles1/tiles2 (may be NULL) receive the tile prefix of each group.
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets_in, int32_t* offsets_out,
-                       int32_t* tiles1, int32_t* tiles2, int32_t* tmap1, int32_t* tmap2,
-                       const PlanParams& p, hipStream_t s);
+                       int32_t* tiles1, int32_t* tiles2, const PlanParams& p, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, const int32_t* offsets, int64_t T, int K, int E,
                           int32_t* perm, int32_t* inv, hipStream_t s);
 // dst[i, :] = src[perm[i], :] for i < n, rows of `row_bytes` bytes (multiple of
@@ -58,8 +56,6 @@ struct FfnArgs {
   const int32_t* offsets;  // [E+1]
   const int32_t* tiles1;   // [E+2]
   const int32_t* tiles2;   // [E+2]
-  const int32_t* tmap1;    // group of every GEMM1 tile
-  const int32_t* tmap2;    // group of every GEMM2 tile
   int64_t T, TK;
   int E, d, I, Is, ldh;
   // GEMM1 inputs

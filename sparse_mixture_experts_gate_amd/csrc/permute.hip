@@ -30,7 +30,7 @@ __device__ void block_inclusive_scan(int* v, int n, int* tmp) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets_in,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ tiles1, int32_t* __restrict__ tiles2,
-    int32_t* __restrict__ tmap1, int32_t* __restrict__ tmap2, PlanParams p) {
+    PlanParams p) {
   __shared__ int rows[kPlanThreads];
   __shared__ int s1[kPlanThreads];
   __shared__ int s2[kPlanThreads];
@@ -71,61 +71,68 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       if (tiles1) tiles1[tid + 1] = s1[tid];
       if (tiles2) tiles2[tid + 1] = s2[tid];
     }
-    // tile -> group maps: every thread takes tiles i, i + 1024, ... and finds
-    // the group g with s[g-1] <= i < s[g] (inclusive prefix) by binary search
-    auto fill = [&](const int* s, int32_t* tmap) {
-      const int total = s[ng - 1];
-      for (int i = tid; i < total; i += kPlanThreads) {
-        int lo = 0, hi = ng - 1;  // smallest g with s[g] > i
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (s[mid] > i) hi = mid; else lo = mid + 1;
-        }
-        tmap[i] = lo;
-      }
-    };
-    if (tmap1) fill(s1, tmap1);
-    if (tmap2) fill(s2, tmap2);
   }
 }
 
 // One workgroup per expert: scans every (t, k) pair in token order and gives
 // the matches consecutive positions, so the order inside an expert is the
-// ascending token order without depending on atomics.
-__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx,
-                                                     const int32_t* __restrict__ offsets,
-                                                     int64_t T, int K, int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ inv) {
-  __shared__ int wsum[4];
+// ascending token order without depending on atomics. Each thread owns
+// kPermTok consecutive tokens per pass; a workgroup-wide exclusive scan of the
+// per-thread match counts places them.
+constexpr int kPermThreads = 1024;
+constexpr int kPermTok = 4;
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int64_t T, int K,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ inv) {
+  __shared__ int wsum[kPermThreads / 64];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int base = offsets[e];
   if (offsets[e + 1] == base) return;
+  const int64_t TK = T * K;
   int running = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    const int64_t t = t0 + tid;
-    int slot = -1;
-    if (t < T) {
-      const int32_t* row = idx + t * K;
-      for (int k = 0; k < K; ++k)
-        if (row[k] == e) slot = k;
+  for (int64_t t0 = 0; t0 < T; t0 += static_cast<int64_t>(kPermThreads) * kPermTok) {
+    const int64_t tb = t0 + static_cast<int64_t>(tid) * kPermTok;
+    int slot[kPermTok];
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < kPermTok; ++q) {
+      slot[q] = -1;
+      const int64_t t = tb + q;
+      if (t < T) {
+        const int32_t* row = idx + t * K;
+        for (int k = 0; k < K; ++k)
+          if (row[k] == e) slot[q] = k;
+      }
+      mine += slot[q] >= 0;
     }
-    const bool hit = slot >= 0;
-    const uint64_t bal = __ballot(hit);
-    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[w] = __popcll(bal);
+    // inclusive scan of `mine` inside the wave
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
     int pre = 0, tot = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kPermThreads / 64; ++q) {
       pre += q < w ? wsum[q] : 0;
       tot += wsum[q];
     }
-    if (hit) {
-      const int pos = base + running + pre + rank;
-      if (pos < T * K) {  // guards counts that disagree with topk_idx
-        perm[pos] = static_cast<int32_t>(t);
-        inv[t * K + slot] = pos;
+    int pos = base + running + pre + incl - mine;
+#pragma unroll
+    for (int q = 0; q < kPermTok; ++q) {
+      if (slot[q] >= 0) {
+        if (pos < TK) {  // guards counts that disagree with topk_idx
+          perm[pos] = static_cast<int32_t>(tb + q);
+          inv[(tb + q) * K + slot[q]] = pos;
+        }
+        ++pos;
       }
     }
     running += tot;
@@ -152,17 +159,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 }  // namespace
 
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets_in, int32_t* offsets_out,
-                       int32_t* tiles1, int32_t* tiles2, int32_t* tmap1, int32_t* tmap2,
-                       const PlanParams& p, hipStream_t s) {
+                       int32_t* tiles1, int32_t* tiles2, const PlanParams& p, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, counts, offsets_in,
-                     offsets_out, tiles1, tiles2, tmap1, tmap2, p);
+                     offsets_out, tiles1, tiles2, p);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* idx, const int32_t* offsets, int64_t T, int K, int E,
                           int32_t* perm, int32_t* inv, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_kernel, dim3(E), dim3(256), 0, s, idx, offsets, T, K, perm, inv);
+  hipLaunchKernelGGL(permute_kernel, dim3(E), dim3(kPermThreads), 0, s, idx, offsets, T, K, perm,
+                     inv);
   return hipGetLastError();
 }
 
