@@ -24,7 +24,9 @@ namespace {
 
 constexpr int BK = 64;  // k elements per stage: 128 bytes per row
 
-constexpr int kPrefetch = 2;  // global loads run this many k-steps ahead
+// Global loads run this many k-steps ahead (2 measured best on the layer's
+// shapes; 3 and 4 only add register pressure).
+constexpr int kPrefetch = 2;
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
@@ -42,7 +44,6 @@ struct Tile {
   static constexpr int LDS_ELEMS = 2 * STAGE;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA sub-tiles");
-  static_assert(BM * (BN + 8) <= LDS_ELEMS, "the output tile fits in the LDS stages");
 };
 
 using TilePrefill = Tile<128, 256, 64, 64>;  // 8 waves, 96 KB LDS
@@ -76,8 +77,8 @@ __device__ __forceinline__ int b_local_row(int wn, int nj) {
 // that share a weight slab in step (skipping them lets those tiles drift apart
 // and lose the slab from L2).
 //
-// PD = 1: the next k-step's loads are in flight while this one computes.
-// PD = 2: two k-steps ahead, in two register sets (loop unrolled by two).
+// Global loads run PD k-steps ahead in PD register sets (loop unrolled by PD
+// so every set has fixed registers).
 // LDS is double buffered, one barrier per k-step; within a k-step the LDS
 // fragments of the next 16-wide sub-step are read while the current one
 // multiplies.
@@ -158,40 +159,24 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t 
   };
 
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  if constexpr (PD == 1) {
-    Stage<C> s0;
-    gload(s0, k_begin);
-    sstore(s0, 0);
-    __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      const bool more = k + 1 < nk;
-      if (more) gload(s0, k_begin + (k + 1) * BK);
-      compute(k & 1);
-      if (more) sstore(s0, (k + 1) & 1);
-      __syncthreads();
-    }
-  } else {
-    Stage<C> s0, s1;
-    gload(s0, k_begin);
-    if (nk > 1) gload(s1, k_begin + BK);
-    sstore(s0, 0);
-    __syncthreads();
-    int k = 0;
-    for (; k + 2 <= nk; k += 2) {
-      // LDS 0 holds step k, s1 step k+1 (arriving), s0 is free
-      if (k + 2 < nk) gload(s0, k_begin + (k + 2) * BK);
-      compute(0);
-      sstore(s1, 1);
-      __syncthreads();
-      // LDS 1 holds step k+1, s0 step k+2 (arriving), s1 is free
-      if (k + 3 < nk) gload(s1, k_begin + (k + 3) * BK);
-      compute(1);
-      if (k + 2 < nk) sstore(s0, 0);
-      __syncthreads();
-    }
-    if (k < nk) {  // odd number of steps: the last one sits in LDS 0
-      compute(0);
-      __syncthreads();
+  // PD register stages rotate: stage j of each unrolled group of PD k-steps is
+  // reloaded with step k+PD right after step k's LDS copy made it free.
+  Stage<C> S[PD];
+#pragma unroll
+  for (int j = 0; j < PD; ++j)
+    if (j < nk) gload(S[j], k_begin + j * BK);
+  sstore(S[0], 0);
+  __syncthreads();
+  for (int k0 = 0; k0 < nk; k0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int k = k0 + j;
+      if (k < nk) {
+        if (k + PD < nk) gload(S[j], k_begin + (k + PD) * BK);
+        compute(k & 1);
+        if (k + 1 < nk) sstore(S[(j + 1) % PD], (k + 1) & 1);
+        __syncthreads();
+      }
     }
   }
 }
@@ -209,6 +194,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int gtab[kMaxGroups + 1];
   constexpr int HALF = C::BN / 2;
+  static_assert(C::BM * (HALF + 8) <= C::LDS_ELEMS, "the H tile fits in the LDS stages");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -288,6 +274,7 @@ template <class C, int PD>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int gtab[kMaxGroups + 1];
+  static_assert(C::BM * (C::BN + 8) <= C::LDS_ELEMS, "the output tile fits in the LDS stages");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -428,20 +415,20 @@ int occupancy_blocks(K kernel, int threads) {
   return nb;
 }
 
-template <class C, int PD1, int PD2>
+template <class C1, class C2, int PD1, int PD2>
 hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
-  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C, PD1>, C::NT);
-  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C, PD2>, C::NT);
+  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C1, PD1>, C1::NT);
+  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C2, PD2>, C2::NT);
   const int cus = device_cu_count();
   // persistent grids, multiples of 8 for the XCD remap
   const int g1 = ((cus * occ1 + 7) / 8) * 8;
   const int g2 = ((cus * occ2 + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn1_bf16_kernel<C, PD1>), dim3(g1), dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn1_bf16_kernel<C1, PD1>), dim3(g1), dim3(C1::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((ffn2_bf16_kernel<C, PD2>), dim3(g2), dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn2_bf16_kernel<C2, PD2>), dim3(g2), dim3(C2::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -469,8 +456,8 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
-  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, kPrefetch, kPrefetch>(a, s, mid);
-  return launch_ffn_bf16_cfg<TilePrefill, kPrefetch, kPrefetch>(a, s, mid);
+  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode, kPrefetch, kPrefetch>(a, s, mid);
+  return launch_ffn_bf16_cfg<TilePrefill, TilePrefill, kPrefetch, kPrefetch>(a, s, mid);
 }
 
 int router_splits(int64_t T, int d, int E, int act_dtype) {

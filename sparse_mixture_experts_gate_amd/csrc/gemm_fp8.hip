@@ -24,6 +24,7 @@ namespace dsmoe {
 namespace {
 
 constexpr int BK8 = 128;  // E4M3 elements (bytes) per row per stage = one scale block
+constexpr int kPrefetch8 = 2;  // global loads run this many k blocks ahead
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile8 {
@@ -75,7 +76,8 @@ __device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
 // the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
 // sa_row: this thread's row scale pointer when threadIdx.x < BM (else unused).
 // Operands come through buffer resources (padding rows read as zeros); global
-// loads run two k blocks ahead in two register sets; LDS is double buffered.
+// loads run kPrefetch8 k blocks ahead in rotating register sets; LDS is
+// double buffered.
 template <class C>
 struct Stage8 {
   uint4 a[C::A_LOADS];
@@ -160,25 +162,23 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
   };
 
   const int nk = K / BK8;
-  Stage8<C> s0, s1;
-  gload(s0, 0);
-  if (nk > 1) gload(s1, 1);
-  sstore(s0, 0);
+  Stage8<C> S[kPrefetch8];
+#pragma unroll
+  for (int j = 0; j < kPrefetch8; ++j)
+    if (j < nk) gload(S[j], j);
+  sstore(S[0], 0);
   __syncthreads();
-  int k = 0;
-  for (; k + 2 <= nk; k += 2) {
-    if (k + 2 < nk) gload(s0, k + 2);
-    compute(0, k);
-    sstore(s1, 1);
-    __syncthreads();
-    if (k + 3 < nk) gload(s1, k + 3);
-    compute(1, k + 1);
-    if (k + 2 < nk) sstore(s0, 0);
-    __syncthreads();
-  }
-  if (k < nk) {
-    compute(0, k);
-    __syncthreads();
+  for (int k0 = 0; k0 < nk; k0 += kPrefetch8) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch8; ++j) {
+      const int k = k0 + j;
+      if (k < nk) {
+        if (k + kPrefetch8 < nk) gload(S[j], k + kPrefetch8);
+        compute(k & 1, k);
+        if (k + 1 < nk) sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
+        __syncthreads();
+      }
+    }
   }
 }
 
