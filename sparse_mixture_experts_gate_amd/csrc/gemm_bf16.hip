@@ -159,24 +159,42 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t 
   };
 
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  // PD register stages rotate: stage j of each unrolled group of PD k-steps is
-  // reloaded with step k+PD right after step k's LDS copy made it free.
+  if (nk <= 0) return;
+  // PD register stages rotate: stage j of each group of PD k-steps is reloaded
+  // with step k+PD right after step k-1's LDS copy made it free. The loads are
+  // unconditional, with the step clamped to the last one (in bounds, unused):
+  // a load under a branch makes the compiler's wait counts assume it may be
+  // missing, and it then waits for the loads just issued before every LDS
+  // store, which undoes the prefetch. Steps past the last full group of PD run
+  // in a tail that issues no loads.
+  auto kpos = [&](int k) { return k_begin + (k < nk ? k : nk - 1) * BK; };
   Stage<C> S[PD];
 #pragma unroll
-  for (int j = 0; j < PD; ++j)
-    if (j < nk) gload(S[j], k_begin + j * BK);
+  for (int j = 0; j < PD; ++j) gload(S[j], kpos(j));
   sstore(S[0], 0);
   __syncthreads();
-  for (int k0 = 0; k0 < nk; k0 += PD) {
+  const int nfull = nk - nk % PD;
+  for (int k0 = 0; k0 < nfull; k0 += PD) {
 #pragma unroll
     for (int j = 0; j < PD; ++j) {
       const int k = k0 + j;
-      if (k < nk) {
-        if (k + PD < nk) gload(S[j], k_begin + (k + PD) * BK);
-        compute(k & 1);
-        if (k + 1 < nk) sstore(S[(j + 1) % PD], (k + 1) & 1);
-        __syncthreads();
-      }
+      gload(S[j], kpos(k + PD));
+      // keep the loads at the top of the step (the scheduler would otherwise
+      // sink them towards their LDS store and shorten their latency slack)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(k & 1);
+      // at k = nk - 1 this fills the idle buffer with data nobody reads
+      sstore(S[(j + 1) % PD], (k + 1) & 1);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PD - 1; ++j) {
+    const int k = nfull + j;
+    if (k < nk) {
+      compute(k & 1);
+      if (k + 1 < nk) sstore(S[(j + 1) % PD], (k + 1) & 1);
+      __syncthreads();
     }
   }
 }

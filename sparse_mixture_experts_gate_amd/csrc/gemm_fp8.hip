@@ -74,25 +74,34 @@ __device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
 // acc[mi][nj] += sum over 128-wide k blocks kb of
 //   (A_kb B_kb^T) * s_a[row][kb] * s_b[kb]   (s_b: sb_lo for the first half of
 // the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
-// sa_row: this thread's row scale pointer when threadIdx.x < BM (else unused).
+// Scales come through buffer resources too: rsa + sa_off is the byte offset of
+// this thread's row of activation scales when threadIdx.x < BM (kInvalidRow
+// otherwise or for padding rows, which reads zeros); rsb + sb_lo / sb_hi are
+// byte offsets of the weight block scales of the tile's columns.
 // Operands come through buffer resources (padding rows read as zeros); global
-// loads run kPrefetch8 k blocks ahead in rotating register sets; LDS is
-// double buffered.
+// loads, scales included, run kPrefetch8 k blocks ahead in rotating register
+// sets; LDS is double buffered.
 template <class C>
 struct Stage8 {
   uint4 a[C::A_LOADS];
   uint4 b[C::B_LOADS];
-  float sa;
+  float sa, sbl, sbh;
 };
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
 template <class C, bool SWIGLU>
 __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
                                            __amdgpu_buffer_rsrc_t ra,
                                            const uint32_t (&aoff)[C::A_LOADS],
-                                           const float* sa_row, __amdgpu_buffer_rsrc_t rb,
+                                           __amdgpu_buffer_rsrc_t rsa, uint32_t sa_off,
+                                           __amdgpu_buffer_rsrc_t rb,
                                            const uint32_t (&boff)[C::B_LOADS],
-                                           const float* sb_lo, const float* sb_hi, int K,
-                                           int rows_valid, f32x4_t (&acc)[C::MI][C::NJ]) {
+                                           __amdgpu_buffer_rsrc_t rsb, uint32_t sb_lo,
+                                           uint32_t sb_hi, int K, int rows_valid,
+                                           f32x4_t (&acc)[C::MI][C::NJ]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -115,8 +124,12 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
       R.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[p] + off, 0, 0));
-    R.sa = (tid < C::BM && sa_row) ? sa_row[kb] : 0.0f;
+    R.sa = load_f32(rsa, sa_off + static_cast<uint32_t>(kb) * 4u);
+    R.sbl = load_f32(rsb, sb_lo + static_cast<uint32_t>(kb) * 4u);
+    R.sbh = SWIGLU ? load_f32(rsb, sb_hi + static_cast<uint32_t>(kb) * 4u) : R.sbl;
   };
+  // weight scales of the k block in LDS, copied from its stage with the tiles
+  float cur_sbl = 0.f, cur_sbh = 0.f;
   auto sstore = [&](const Stage8<C>& R, int st) {
     uint8_t* As = lds + st * C::STAGE;
     uint8_t* Bs = As + C::BM * BK8;
@@ -127,11 +140,13 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
     for (int p = 0; p < C::B_LOADS; ++p)
       *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = R.b[p];
     if (tid < C::BM) lds_sa[st * C::BM + tid] = R.sa;
+    cur_sbl = R.sbl;
+    cur_sbh = R.sbh;
   };
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int st, int kb) {
-    const float s_lo = sb_lo[kb];
-    const float s_hi = SWIGLU ? sb_hi[kb] : s_lo;
+  auto compute = [&](int st) {
+    const float s_lo = cur_sbl;
+    const float s_hi = cur_sbh;
     const uint8_t* As = lds + st * C::STAGE;
     const uint8_t* Bs = As + C::BM * BK8;
     const int kg = lane >> 4;
@@ -162,22 +177,36 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
   };
 
   const int nk = K / BK8;
+  if (nk <= 0) return;
+  // Unconditional loads with the block index clamped to the last one, a
+  // branch-free main loop over full groups of kPrefetch8 blocks and a tail
+  // without loads: a load under a branch makes the compiler wait for the
+  // loads just issued before every LDS store (same scheme as the bf16 GEMMs).
+  auto kpos = [&](int k) { return k < nk ? k : nk - 1; };
   Stage8<C> S[kPrefetch8];
 #pragma unroll
-  for (int j = 0; j < kPrefetch8; ++j)
-    if (j < nk) gload(S[j], j);
+  for (int j = 0; j < kPrefetch8; ++j) gload(S[j], kpos(j));
   sstore(S[0], 0);
   __syncthreads();
-  for (int k0 = 0; k0 < nk; k0 += kPrefetch8) {
+  const int nfull = nk - nk % kPrefetch8;
+  for (int k0 = 0; k0 < nfull; k0 += kPrefetch8) {
 #pragma unroll
     for (int j = 0; j < kPrefetch8; ++j) {
       const int k = k0 + j;
-      if (k < nk) {
-        if (k + kPrefetch8 < nk) gload(S[j], k + kPrefetch8);
-        compute(k & 1, k);
-        if (k + 1 < nk) sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
-        __syncthreads();
-      }
+      gload(S[j], kpos(k + kPrefetch8));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(k & 1);
+      sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPrefetch8 - 1; ++j) {
+    const int k = nfull + j;
+    if (k < nk) {
+      compute(k & 1);
+      if (k + 1 < nk) sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
+      __syncthreads();
     }
   }
 }
@@ -206,6 +235,11 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
              : buf_rsrc(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
   const __amdgpu_buffer_rsrc_t rxs =
       buf_rsrc(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
+  // activation scales: gathered rows (or x_perm rows) and the shared rows
+  const __amdgpu_buffer_rsrc_t rsxp =
+      buf_rsrc(XS, static_cast<uint32_t>(a.perm ? a.T : a.TK) * static_cast<uint32_t>(dkb) * 4u);
+  const __amdgpu_buffer_rsrc_t rsx =
+      buf_rsrc(a.x_scale, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(dkb) * 4u);
   uint8_t* H = static_cast<uint8_t*>(a.H);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
@@ -233,10 +267,10 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       const int64_t row = src_row(tc.m * C::BM + r0 + p * C::RPP);
       aoff[p] = row >= 0 ? static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) : kInvalidRow;
     }
-    const float* sa_row = nullptr;
+    uint32_t sa_off = kInvalidRow;
     if (tid < C::BM) {
       const int64_t row = src_row(tc.m * C::BM + tid);
-      if (row >= 0) sa_row = (shared ? a.x_scale : XS) + row * dkb;
+      if (row >= 0) sa_off = static_cast<uint32_t>(row * dkb) * 4u;
     }
     const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws13)
                               : static_cast<const uint8_t*>(a.w13) +
@@ -252,11 +286,13 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       const int col = tc.n * HALF + (up ? lr - HALF : lr);
       boff[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
     }
-    const float* sb_gate = WS + static_cast<int64_t>(tc.n) * dkb;
-    const float* sb_up = WS + static_cast<int64_t>(Ig / 128 + tc.n) * dkb;
+    const __amdgpu_buffer_rsrc_t rws =
+        buf_rsrc(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
+    const uint32_t sb_gate = static_cast<uint32_t>(tc.n * dkb) * 4u;
+    const uint32_t sb_up = static_cast<uint32_t>((Ig / 128 + tc.n) * dkb) * 4u;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, true>(lds, lds_sa, shared ? rxs : rx, aoff, sa_row, rw, boff, sb_gate, sb_up,
-                        a.d, tc.rows - tc.m * C::BM, acc);
+    gemm8_tile<C, true>(lds, lds_sa, shared ? rxs : rx, aoff, shared ? rsx : rsxp, sa_off, rw,
+                        boff, rws, sb_gate, sb_up, a.d, tc.rows - tc.m * C::BM, acc);
 
     // SwiGLU, then the row max-abs over the 128 columns (across the wave's
     // 16-lane groups and the tile's WAVES_N waves)
@@ -336,6 +372,8 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
   const __amdgpu_buffer_rsrc_t rh =
       buf_rsrc(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
+  const __amdgpu_buffer_rsrc_t rsh =
+      buf_rsrc(a.H_scale, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(hkb) * 4u);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
     tc.g = __builtin_amdgcn_readfirstlane(tc.g);
@@ -354,7 +392,9 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
       aoff[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * static_cast<uint32_t>(a.ldh)
                                : kInvalidRow;
     }
-    const float* sa_row = (tid < C::BM && tid < rows_left) ? a.H_scale + (hrow0 + tid) * hkb : nullptr;
+    const uint32_t sa_off = (tid < C::BM && tid < rows_left)
+                                ? static_cast<uint32_t>((hrow0 + tid) * hkb) * 4u
+                                : kInvalidRow;
     const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws2)
                               : static_cast<const uint8_t*>(a.w2) +
                                     static_cast<int64_t>(tc.g) * a.d * a.I;
@@ -368,9 +408,12 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
       const int row = tc.n * C::BN + r0 + p * C::RPP;
       boff[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
     }
-    const float* sb = WS + static_cast<int64_t>((tc.n * C::BN) / 128) * ikb;
+    const __amdgpu_buffer_rsrc_t rws =
+        buf_rsrc(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
+    const uint32_t sb = static_cast<uint32_t>(((tc.n * C::BN) / 128) * ikb) * 4u;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, false>(lds, lds_sa, rh, aoff, sa_row, rw, boff, sb, sb, Ig, rows_left, acc);
+    gemm8_tile<C, false>(lds, lds_sa, rh, aoff, rsh, sa_off, rw, boff, rws, sb, sb, Ig,
+                         rows_left, acc);
 
     uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
                                  static_cast<int64_t>(tc.m) * C::BM * a.d
