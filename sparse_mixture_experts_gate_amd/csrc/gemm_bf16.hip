@@ -148,6 +148,9 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t 
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+      // the reads above go out before this sub-step's MFMAs (the scheduler
+      // would otherwise reuse their registers and serialize read and multiply)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
