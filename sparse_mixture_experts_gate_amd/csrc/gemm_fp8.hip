@@ -24,7 +24,10 @@ namespace dsmoe {
 namespace {
 
 constexpr int BK8 = 128;  // E4M3 elements (bytes) per row per stage = one scale block
-constexpr int kPrefetch8 = 2;  // global loads run this many k blocks ahead
+// Global loads run this many k blocks ahead. One: the k block's MFMAs and
+// fp32 rescaling keep this kernel compute-bound, and a second register stage
+// does not fit beside the accumulators without spilling.
+constexpr int kPrefetch8 = 1;
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile8 {
@@ -110,11 +113,9 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // 16-row groups entirely beyond rows_valid skip their MFMAs; the branch also
-  // keeps the compiler from hoisting every row group's MFMAs at once
-  bool mi_on[C::MI];
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) mi_on[mi] = wm * C::WM + mi * 16 < rows_valid;
+  // padding rows hold zero codes and are multiplied like the others: a
+  // per-group skip becomes selects on every product and accumulator
+  (void)rows_valid;
 
   auto gload = [&](Stage8<C>& R, int kb) {
     const uint32_t off = static_cast<uint32_t>(kb * BK8 + ch * 16);
@@ -153,26 +154,53 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
     i32x8_t bfr[C::NJ];
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      if (!mi_on[mi]) continue;
-      const int rbase = wm * C::WM + mi * 16;
-      const i32x8_t af = frag8(As, rbase + (lane & 15), kg);
-      const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::BM + rbase + 4 * kg);
-      f32x4_t s_l, s_h;
+    auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
+    // row scale x block scale of the gate (lo) or up (hi) half, per 16-row group
+    auto row_scales = [&](int m, f32x4_t& s_l, f32x4_t& s_h) {
+      const f32x4_t sa =
+          *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::BM + wm * C::WM + m * 16 + 4 * kg);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         s_l[r] = sa[r] * s_lo;
         s_h[r] = sa[r] * s_hi;
       }
+    };
+    // Software pipeline over the MI x NJ products of the k block: MFMA t runs
+    // in the matrix core while the VALU folds product t-1 into its
+    // accumulator with the scales (4 FMAs, shorter than one MFMA).
+    constexpr int NP = C::MI * C::NJ;
+    f32x4_t p[2];
+    i32x8_t af[2];
+    f32x4_t sl[2], sh[2];
+    af[0] = a_frag(0);
+    row_scales(0, sl[0], sh[0]);
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) {
-        const f32x4_t p =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[nj], zero, 0, 0, 0, 127, 0, 127);
-        const bool lo = !SWIGLU || nj < C::NJ / 2;
+    for (int t = 0; t < NP; ++t) {
+      const int mi = t / C::NJ, nj = t % C::NJ;
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi & 1], bfr[nj], zero, 0, 0,
+                                                                  0, 127, 0, 127);
+      if (nj == 0 && mi + 1 < C::MI) af[(mi + 1) & 1] = a_frag(mi + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t > 0) {
+        const int pm = (t - 1) / C::NJ, pn = (t - 1) % C::NJ;
+        const bool lo = !SWIGLU || pn < C::NJ / 2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][nj][r] = __builtin_fmaf(p[r], lo ? s_l[r] : s_h[r], acc[mi][nj][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], lo ? sl[pm & 1][r] : sh[pm & 1][r],
+                                          acc[pm][pn][r]);
       }
+      // group mi+1's scales go to the slot of group mi-1, whose last product
+      // was folded in just above
+      if (nj == 0 && mi + 1 < C::MI) row_scales(mi + 1, sl[(mi + 1) & 1], sh[(mi + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      constexpr int pm = C::MI - 1, pn = C::NJ - 1;
+      constexpr bool lo = !SWIGLU || pn < C::NJ / 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], lo ? sl[pm & 1][r] : sh[pm & 1][r],
+                                        acc[pm][pn][r]);
     }
   };
 
