@@ -129,8 +129,9 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
     R.sbl = load_f32(rsb, sb_lo + static_cast<uint32_t>(kb) * 4u);
     R.sbh = SWIGLU ? load_f32(rsb, sb_hi + static_cast<uint32_t>(kb) * 4u) : R.sbl;
   };
-  // weight scales of the k block in LDS, copied from its stage with the tiles
-  float cur_sbl = 0.f, cur_sbh = 0.f;
+  // LDS scales per stage: row scale x weight block scale, for the gate half
+  // (then the up half with SWIGLU) of the tile's columns, one per row
+  constexpr int SA_STRIDE = SWIGLU ? 2 * C::BM : C::BM;
   auto sstore = [&](const Stage8<C>& R, int st) {
     uint8_t* As = lds + st * C::STAGE;
     uint8_t* Bs = As + C::BM * BK8;
@@ -140,14 +141,13 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p)
       *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = R.b[p];
-    if (tid < C::BM) lds_sa[st * C::BM + tid] = R.sa;
-    cur_sbl = R.sbl;
-    cur_sbh = R.sbh;
+    if (tid < C::BM) {
+      lds_sa[st * SA_STRIDE + tid] = R.sa * R.sbl;
+      if constexpr (SWIGLU) lds_sa[st * SA_STRIDE + C::BM + tid] = R.sa * R.sbh;
+    }
   };
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int st) {
-    const float s_lo = cur_sbl;
-    const float s_hi = cur_sbh;
     const uint8_t* As = lds + st * C::STAGE;
     const uint8_t* Bs = As + C::BM * BK8;
     const int kg = lane >> 4;
@@ -155,15 +155,11 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
     auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
-    // row scale x block scale of the gate (lo) or up (hi) half, per 16-row group
+    // combined scales of the lane's 4 rows in 16-row group m, gate (lo) and up (hi)
     auto row_scales = [&](int m, f32x4_t& s_l, f32x4_t& s_h) {
-      const f32x4_t sa =
-          *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::BM + wm * C::WM + m * 16 + 4 * kg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s_l[r] = sa[r] * s_lo;
-        s_h[r] = sa[r] * s_hi;
-      }
+      const float* base = lds_sa + st * SA_STRIDE + wm * C::WM + m * 16 + 4 * kg;
+      s_l = *reinterpret_cast<const f32x4_t*>(base);
+      s_h = SWIGLU ? *reinterpret_cast<const f32x4_t*>(base + C::BM) : s_l;
     };
     // Software pipeline over the MI x NJ products of the k block: MFMA t runs
     // in the matrix core while the VALU folds product t-1 into its
@@ -243,7 +239,7 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2 * 2 * C::BM];  // 2 stages x gate, up
   __shared__ float red[C::WAVES_N][C::BM];
   __shared__ int gtab[kMaxGroups + 1];
   constexpr int HALF = C::BN / 2;  // 128 H columns
