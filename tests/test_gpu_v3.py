@@ -55,8 +55,9 @@ def test_v3_prefill_full_size(v3):
     assert np.all(ro.near_tie[differ] | rr.near_tie[differ])
     print(f"  near ties {ro.near_tie.mean():.2e}, differing {differ.sum()}", flush=True)
     assert ro.near_tie.mean() < 1e-3
-    # outputs on a seeded sample of tokens
-    rows = np.random.default_rng(0).choice(wl.T, 32, replace=False)
+    # outputs on a seeded sample of 1024 tokens (the oracle streams each
+    # touched expert's weights once, so its cost saturates at all experts)
+    rows = np.sort(np.random.default_rng(0).choice(wl.T, 1024, replace=False))
     _check_rows(wl, P, P["x"], rows, g, TOL["bf16"])
     # permutation and bias update at full size
     desc = M.make_desc(wl, wl.T)
@@ -95,5 +96,4 @@ def test_v3_decode(v3, T):
     assert np.array_equal(g["topk_idx"], rr.idx)
     assert np.array_equal(g["topk_gate"].view(np.uint32), rr.gate.view(np.uint32))
     assert np.array_equal(g["counts"], O.permute(rr.idx, wl.E).counts)
-    rows = np.arange(T) if T <= 16 else np.random.default_rng(T).choice(T, 16, replace=False)
-    _check_rows(wl, P, x, rows, g, TOL["bf16"])
+    _check_rows(wl, P, x, np.arange(T), g, TOL["bf16"])
