@@ -89,11 +89,6 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float gam
   else if (load < total) bias[e] = bias[e] + gamma;
 }
 
-__device__ __forceinline__ float load_src(const void* src, int dtype, int64_t i) {
-  return dtype == 1 ? bf16_to_f32(static_cast<const uint16_t*>(src)[i])
-                    : static_cast<const float*>(src)[i];
-}
-
 // Max-abs scaling of one group (mhpq.cn §4.1, online max-abs; gkm0120.cn
 // notes Q8, 1x128 tiles / 128x128 blocks): scale = amax/448 and codes of
 // v * (448/amax); an all-zero group gets scale 1 and zero codes.
@@ -107,7 +102,34 @@ __device__ __forceinline__ void quant_params(float amax, float& inv, float& scal
   }
 }
 
-// One workgroup (256 threads) per 128x128 block; each thread 64 elements.
+// Eight consecutive elements src[i .. i+8) as fp32 (i a multiple of 8; one
+// 16-byte load for bf16, two for fp32).
+__device__ __forceinline__ void load8(const void* src, int dtype, int64_t i, float (&v)[8]) {
+  if (dtype == 1) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Codes of v * inv for eight values (all zero when the group is all zero).
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float amax, float inv) {
+  if (amax == 0.0f) return make_uint2(0u, 0u);
+  return make_uint2(e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                    e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
+}
+
+// One workgroup (256 threads) per 128x128 block: 16 lanes cover one block row
+// with 8 elements each (coalesced 16-byte loads), 8 rows per thread.
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const void* __restrict__ src,
                                                            int dtype, int rows, int cols,
                                                            uint8_t* __restrict__ q,
@@ -118,16 +140,16 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const void* __restric
   const int64_t mat = blk / (static_cast<int64_t>(rb) * cb);
   const int bi = static_cast<int>((blk / cb) % rb), bj = static_cast<int>(blk % cb);
   const int tid = threadIdx.x;
-  // thread -> (row, 64-column half) of the block, rows tid/2
-  const int r = tid >> 1, c0 = (tid & 1) * 64;
+  const int c = tid & 15, r0 = tid >> 4;
   const int64_t base = mat * rows * static_cast<int64_t>(cols) +
-                       static_cast<int64_t>(bi * 128 + r) * cols + bj * 128 + c0;
-  float v[64];
+                       static_cast<int64_t>(bi * 128 + r0) * cols + bj * 128 + c * 8;
+  float v[8][8];
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    v[j] = load_src(src, dtype, base + j);
-    amax = fmaxf(amax, fabsf(v[j]));
+  for (int i = 0; i < 8; ++i) {
+    load8(src, dtype, base + static_cast<int64_t>(16 * i) * cols, v[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
   }
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
@@ -136,38 +158,42 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const void* __restric
   float inv, sc;
   quant_params(amax, inv, sc);
 #pragma unroll
-  for (int j = 0; j < 64; j += 4) {
-    const uint32_t w = amax == 0.0f ? 0u
-                                    : e4m3_pack4(v[j] * inv, v[j + 1] * inv, v[j + 2] * inv,
-                                                 v[j + 3] * inv);
-    *reinterpret_cast<uint32_t*>(q + base + j) = w;
-  }
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(q + base + static_cast<int64_t>(16 * i) * cols) =
+        encode8(v[i], amax, inv);
   if (tid == 0) scale[blk] = sc;
 }
 
-// One wave per 1x128 tile; each lane 2 elements.
+// 16 lanes per 1x128 tile (8 elements each, 16-byte loads), 16 tiles per
+// workgroup; rows gathered through perm when given.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int dtype,
                                                          const int32_t* __restrict__ perm,
                                                          int64_t n, int cols,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int l16 = threadIdx.x & 15;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int tpr = cols / 128;
-  if (tile >= n * tpr) return;
-  const int64_t row = tile / tpr;
-  const int tc = static_cast<int>(tile % tpr);
-  const int64_t srow = perm ? static_cast<int64_t>(perm[row]) : row;
-  const int64_t base = row * cols + tc * 128 + lane * 2;
-  const int64_t sbase = srow * cols + tc * 128 + lane * 2;
-  const float a = load_src(src, dtype, sbase), b = load_src(src, dtype, sbase + 1);
-  float amax = fmaxf(fabsf(a), fabsf(b));
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const bool valid = tile < n * tpr;  // lanes stay for the shuffles
+  float v[8];
+  float amax = 0.0f;
+  int64_t base = 0;
+  if (valid) {
+    const int64_t row = tile / tpr;
+    const int tc = static_cast<int>(tile % tpr);
+    const int64_t srow = perm ? static_cast<int64_t>(perm[row]) : row;
+    base = row * cols + tc * 128 + l16 * 8;
+    load8(src, dtype, srow * cols + tc * 128 + l16 * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  }
+  // max over the tile's 16 lanes (xor of the low four lane bits)
+  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (!valid) return;
   float inv, sc;
   quant_params(amax, inv, sc);
-  const uint32_t w = amax == 0.0f ? 0u : e4m3_pack4(a * inv, b * inv, 0.0f, 0.0f);
-  *reinterpret_cast<uint16_t*>(q + base) = static_cast<uint16_t>(w & 0xFFFFu);
-  if (lane == 0) scale[tile] = sc;
+  *reinterpret_cast<uint2*>(q + base) = encode8(v, amax, inv);
+  if (l16 == 0) scale[tile] = sc;
 }
 
 }  // namespace
@@ -207,8 +233,8 @@ hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm
                              int cols, uint8_t* q, float* scale, hipStream_t s) {
   const int64_t tiles = n * (cols / 128);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4)), dim3(256), 0,
-                     s, src, src_dtype, perm, n, cols, q, scale);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(static_cast<unsigned>((tiles + 15) / 16)), dim3(256),
+                     0, s, src, src_dtype, perm, n, cols, q, scale);
   return hipGetLastError();
 }
 
