@@ -278,8 +278,12 @@ moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_route
     HIP_TRY(launch_router_logits_bf16(x, w_router, d->T, d->d, d->n_experts, L.splits,
                                       at<uint16_t>(ws, L.wsplit), partial, s),
             "router (bf16)");
-  HIP_TRY(launch_route(partial, L.splits, logits, bias, route_params(d), idx, gate, counts, ntie,
-                       s),
+  int splits = L.splits;
+  if (splits >= 8) {  // small T: many partials, summed by a wide kernel first
+    HIP_TRY(launch_sum_partials(partial, splits, d->T * d->n_experts, s), "router partial sums");
+    splits = 1;
+  }
+  HIP_TRY(launch_route(partial, splits, logits, bias, route_params(d), idx, gate, counts, ntie, s),
           "route");
   return MOE_OK;
 }

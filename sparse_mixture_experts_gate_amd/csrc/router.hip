@@ -59,6 +59,29 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// partial[i] = ((partial[i] + partial[n + i]) + ...) + partial[(S-1) n + i]:
+// the split-K partial sums of the router product added in split order, one
+// thread per logit. Used when there are many splits (small T), where the
+// routing kernel's one wave per token would add them with little parallelism;
+// the order, and so every bit, is the routing kernel's own.
+__global__ __launch_bounds__(256) void sum_partials_kernel(float* __restrict__ partial, int splits,
+                                                           int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float u = partial[i];
+  // loads in groups of eight so they are in flight together; adds in order
+  for (int q0 = 1; q0 < splits; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = q0 + j < splits ? partial[static_cast<int64_t>(q0 + j) * n + i] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q0 + j < splits) u = u + v[j];
+  }
+  partial[i] = u;
+}
+
 constexpr int kTokPerBlock = 4;  // one wave per token
 constexpr int kMaxE = 512;
 
@@ -112,7 +135,16 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ pa
     if (G > 1 && active) {
       // group score: fp32 sum of the group's topn best biased scores, largest first
       float gsc = -INFINITY;
-      if (lane < G) {
+      if (lane < G && p.topn <= 2) {
+        // the two best (or the best) of the group in two registers
+        float t0 = -INFINITY, t1 = -INFINITY;
+        for (int i = 0; i < GS; ++i) {
+          const float v = c_lds[wave][lane * GS + i];
+          if (v > t0) { t1 = t0; t0 = v; }
+          else if (v > t1) { t1 = v; }
+        }
+        gsc = p.topn == 2 ? t0 + t1 : t0;
+      } else if (lane < G) {
         float top[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) top[q] = -INFINITY;
@@ -233,6 +265,13 @@ hipError_t launch_router_f32(const float* x, const float* w, int64_t T, int d, i
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(router_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      s, x, w, T, d, E, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(float* partial, int splits, int64_t n, hipStream_t s) {
+  if (n == 0 || splits <= 1) return hipSuccess;
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, s, partial, splits, n);
   return hipGetLastError();
 }
 
