@@ -24,13 +24,11 @@ namespace {
 
 constexpr int BK = 64;  // k elements per stage: 128 bytes per row
 
-// Global loads run this many k-steps ahead (2 measured best on the layer's
-// shapes; 3 and 4 only add register pressure).
-constexpr int kPrefetch = 2;
-
-template <int BM_, int BN_, int WM_, int WN_>
+// BM x BN output tile in waves of WM x WN; NST LDS stages in the load ring
+// (loads run NST - 1 k-steps ahead).
+template <int BM_, int BN_, int WM_, int WN_, int NST_ = 3>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -41,13 +39,16 @@ struct Tile {
   static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
   // waves per SIMD the register budget is sized for
   static constexpr int MINW = (WM * WN >= 64 * 128) ? 1 : 2;
-  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static constexpr int LDS_ELEMS = NST * STAGE;
+  static_assert(NST >= 3, "loads run at least two steps ahead");
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA sub-tiles");
 };
 
-using TilePrefill = Tile<128, 256, 64, 64>;  // 8 waves, 96 KB LDS
-using TileDecode = Tile<32, 128, 32, 64>;    // 2 waves, 40 KB LDS
+using TilePrefill = Tile<128, 256, 64, 64>;  // 8 waves, 144 KB LDS
+// decode streams weights: one 2-wave workgroup per CU with a 7-stage ring
+// keeps six steps (120 KB) of loads in flight per CU
+using TileDecode = Tile<32, 128, 32, 64, 7>;
 
 // LDS element offset of 16-byte chunk `ch` (0..7) of row `r`. The chunk is
 // XOR-swizzled with (r >> 1) & 7: the 16 lanes that one 128-bit LDS access
@@ -67,35 +68,48 @@ __device__ __forceinline__ int b_local_row(int wn, int nj) {
   }
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor as four scalar words: base address, no stride,
+// `bytes` records (range-checked: offsets at or beyond it read as zeros).
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(b));
+  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load ... lds):
+// lane i writes lds_addr + 16 i, lds_addr wave-uniform (in M0). The load has
+// no register result, so nothing is in flight towards a VGPR; its completion
+// is waited for with vmcnt (the compiler does not track these loads, so the
+// GEMM loop places its own waits).
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
 // acc[mi][nj] += A * B^T over k in [k_begin, k_end) (multiples of 64).
-// Operands are read with buffer loads: one resource per operand and a 32-bit
-// byte offset per thread and row (the k = 0 element of the row). Offsets at
-// or beyond the resource size (kInvalidRow) read as zeros in hardware, so
-// padding rows cost no branches. With a_kmod != 0 the A column is k mod a_kmod
-// (router: the same activations meet the three weight terms). rows_valid is
-// informational: padded rows are multiplied as zeros, which keeps the tiles
-// that share a weight slab in step (skipping them lets those tiles drift apart
-// and lose the slab from L2).
+// Operands come from buffers (ra, rb) through a 32-bit byte offset per thread
+// and row (the k = 0 element of the row); offsets at or beyond the buffer
+// size (kInvalidRow) read as zeros, so padding rows cost no branches. With
+// a_kmod != 0 the A column is k mod a_kmod (router: the same activations meet
+// the three weight terms). Padding rows are multiplied as zeros.
 //
-// Global loads run PD k-steps ahead in PD register sets (loop unrolled by PD
-// so every set has fixed registers).
-// LDS is double buffered, one barrier per k-step; within a k-step the LDS
-// fragments of the next 16-wide sub-step are read while the current one
-// multiplies.
-
-template <class C>
-struct Stage {
-  uint4 a[C::A_LOADS];
-  uint4 b[C::B_LOADS];
-};
-
-template <class C, bool SWIGLU, int PD>
-__device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t ra,
-                                          const uint32_t (&aoff)[C::A_LOADS],
-                                          __amdgpu_buffer_rsrc_t rb,
+// Tiles go from global memory straight into a ring of NST LDS stages,
+// NST - 1 k-steps ahead, with one barrier per step: no registers hold tiles in
+// flight and no LDS store instructions are issued. Lane (row r, 16-byte
+// position ch) fetches logical chunk ch ^ swizzle(r), so the LDS image is the
+// swizzled layout lds_off describes. Within a step, the LDS fragments of the
+// next 16-wide sub-step are read while the current one multiplies.
+template <class C, bool SWIGLU>
+__device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
+                                          const uint32_t (&aoff)[C::A_LOADS], i32x4_t rb,
                                           const uint32_t (&boff)[C::B_LOADS], int k_begin,
-                                          int k_end, int a_kmod, int rows_valid,
-                                          f32x16_t (&acc)[C::MI][C::NJ]) {
+                                          int k_end, int a_kmod, f32x16_t (&acc)[C::MI][C::NJ]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -106,32 +120,30 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t 
     for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
-  (void)rows_valid;
-
-  auto gload = [&](Stage<C>& R, int k0) {
-    const uint32_t kb = static_cast<uint32_t>(k0 + ch * 8) * 2u;
-    const uint32_t ka = a_kmod ? static_cast<uint32_t>(k0 % a_kmod + ch * 8) * 2u : kb;
+  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
 #pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p)
-      R.a[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[p] + ka, 0, 0));
+  for (int p = 0; p < C::A_LOADS; ++p)
+    ao[p] = aoff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
 #pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p)
-      R.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[p] + kb, 0, 0));
-  };
-  auto sstore = [&](const Stage<C>& R, int st) {
-    uint16_t* As = lds + st * C::STAGE;
-    uint16_t* Bs = As + C::BM * BK;
+  for (int p = 0; p < C::B_LOADS; ++p)
+    bo[p] = boff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+  // LDS byte address of the block (the low 32 bits of a flat LDS address)
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  // this wave's 8 rows of each load pass start at row 8 * wave
+  auto issue = [&](int st, int k0) {
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    const uint32_t ka = a_kmod ? static_cast<uint32_t>(k0 % a_kmod) * 2u : kb;
+    const uint32_t a_base =
+        __builtin_amdgcn_readfirstlane(lds0 + (st * C::STAGE + wave * 8 * BK) * 2);
+    const uint32_t b_base = a_base + C::BM * BK * 2;
 #pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p)
-      *reinterpret_cast<uint4*>(As + lds_off(r0 + p * C::RPP, ch)) = R.a[p];
+    for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + ka, a_base + p * C::RPP * BK * 2);
 #pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p)
-      *reinterpret_cast<uint4*>(Bs + lds_off(r0 + p * C::RPP, ch)) = R.b[p];
+    for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + kb, b_base + p * C::RPP * BK * 2);
   };
   auto compute = [&](int st) {
     const uint16_t* As = lds + st * C::STAGE;
     const uint16_t* Bs = As + C::BM * BK;
-    // fragments of sub-step kk+1 are read from LDS while sub-step kk multiplies
     bf16x8_t af[2][C::MI], bfr[2][C::NJ];
     auto fetch = [&](int kk, int buf) {
       const int chk = kk * 2 + (lane >> 5);
@@ -161,45 +173,32 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, __amdgpu_buffer_rsrc_t 
     }
   };
 
+  constexpr int NST = C::NST;
+  // loads of the NST - 2 newest steps that may stay in flight at a wait
+  constexpr int INFLIGHT = (C::A_LOADS + C::B_LOADS) * (NST - 2);
+  static_assert(INFLIGHT <= 63, "vmcnt range");
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
-  // PD register stages rotate: stage j of each group of PD k-steps is reloaded
-  // with step k+PD right after step k-1's LDS copy made it free. The loads are
-  // unconditional, with the step clamped to the last one (in bounds, unused):
-  // a load under a branch makes the compiler's wait counts assume it may be
-  // missing, and it then waits for the loads just issued before every LDS
-  // store, which undoes the prefetch. Steps past the last full group of PD run
-  // in a tail that issues no loads.
+  // steps past the end reload the last one (in bounds, never read)
   auto kpos = [&](int k) { return k_begin + (k < nk ? k : nk - 1) * BK; };
-  Stage<C> S[PD];
 #pragma unroll
-  for (int j = 0; j < PD; ++j) gload(S[j], kpos(j));
-  sstore(S[0], 0);
+  for (int j = 0; j < NST - 1; ++j) issue(j, kpos(j));
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");  // stage 0 has landed
   __syncthreads();
-  const int nfull = nk - nk % PD;
-  for (int k0 = 0; k0 < nfull; k0 += PD) {
-#pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int k = k0 + j;
-      gload(S[j], kpos(k + PD));
-      // keep the loads at the top of the step (the scheduler would otherwise
-      // sink them towards their LDS store and shorten their latency slack)
-      __builtin_amdgcn_sched_barrier(0);
-      compute(k & 1);
-      // at k = nk - 1 this fills the idle buffer with data nobody reads
-      sstore(S[(j + 1) % PD], (k + 1) & 1);
-      __syncthreads();
-    }
+  int st = 0, st_issue = NST - 1;
+  for (int k = 0; k < nk; ++k) {
+    issue(st_issue, kpos(k + NST - 1));  // the stage read in step k - 1
+    compute(st);
+    // this wave's part of stage k+1 has landed (later steps' loads may be in
+    // flight); the barrier makes every wave's part visible and frees stage k
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");
+    __syncthreads();
+    st = st == NST - 1 ? 0 : st + 1;
+    st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
   }
-#pragma unroll
-  for (int j = 0; j < PD - 1; ++j) {
-    const int k = nfull + j;
-    if (k < nk) {
-      compute(k & 1);
-      if (k + 1 < nk) sstore(S[(j + 1) % PD], (k + 1) & 1);
-      __syncthreads();
-    }
-  }
+  // the loads of the clamped last steps land before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 
@@ -210,7 +209,7 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
 }
 
 // H = silu(A W1^T) * (A W3^T) per group.
-template <class C, int PD>
+template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int gtab[kMaxGroups + 1];
@@ -224,10 +223,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   const int total = gtab[a.E + 1];
   const int nb = gridDim.x;
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
-  const __amdgpu_buffer_rsrc_t rx =
-      a.perm ? buf_rsrc(a.x, static_cast<uint32_t>(a.T) * row_bytes)
-             : buf_rsrc(a.xperm, static_cast<uint32_t>(a.TK) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rxs = buf_rsrc(a.x, static_cast<uint32_t>(a.T) * row_bytes);
+  const i32x4_t rx = a.perm ? rsrc4(a.x, static_cast<uint32_t>(a.T) * row_bytes)
+                            : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * row_bytes);
+  const i32x4_t rxs = rsrc4(a.x, static_cast<uint32_t>(a.T) * row_bytes);
   uint16_t* H = static_cast<uint16_t*>(a.H);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
@@ -259,7 +257,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
     const uint16_t* W = shared ? static_cast<const uint16_t*>(a.ws13)
                                : static_cast<const uint16_t*>(a.w13) +
                                      static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(2 * Ig) * row_bytes);
+    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(2 * Ig) * row_bytes);
     uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
       boff[p] = col < Ig ? static_cast<uint32_t>(up ? Ig + col : col) * row_bytes : kInvalidRow;
     }
     f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, true, PD>(lds, shared ? rxs : rx, aoff, rw, boff, 0, a.d, 0, rows_left, acc);
+    gemm_tile<C, true>(lds, shared ? rxs : rx, aoff, rw, boff, 0, a.d, 0, acc);
 
     const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
 #pragma unroll
@@ -291,7 +289,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
 }
 
 // y = H W2^T per group: routed rows to y_perm, shared rows to y_shared.
-template <class C, int PD>
+template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int gtab[kMaxGroups + 1];
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   const int nb = gridDim.x;
   const uint32_t hrow_bytes = static_cast<uint32_t>(a.ldh) * 2u;
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(a.H, static_cast<uint32_t>(hrows) * hrow_bytes);
+  const i32x4_t rh = rsrc4(a.H, static_cast<uint32_t>(hrows) * hrow_bytes);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
     tc.g = __builtin_amdgcn_readfirstlane(tc.g);
@@ -327,7 +325,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
                                : static_cast<const uint16_t*>(a.w2) +
                                      static_cast<int64_t>(tc.g) * a.d * a.I;
     const uint32_t wrow_bytes = static_cast<uint32_t>(Ig) * 2u;
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(a.d) * wrow_bytes);
+    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(a.d) * wrow_bytes);
     uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
@@ -335,7 +333,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
       boff[p] = row < a.d ? static_cast<uint32_t>(row) * wrow_bytes : kInvalidRow;
     }
     f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, false, PD>(lds, rh, aoff, rw, boff, 0, Ig, 0, rows_left, acc);
+    gemm_tile<C, false>(lds, rh, aoff, rw, boff, 0, Ig, 0, acc);
 
     uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
                                  static_cast<int64_t>(tc.m) * C::BM * a.d
@@ -375,8 +373,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void router_bf16_kernel(const uint1
   const int k_begin = split * kchunk;
   const int k_end = min(3 * d, k_begin + kchunk);
   const uint32_t row_bytes = static_cast<uint32_t>(d) * 2u;
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, static_cast<uint32_t>(T) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wsplit, static_cast<uint32_t>(E) * 3u * row_bytes);
+  const i32x4_t rx = rsrc4(x, static_cast<uint32_t>(T) * row_bytes);
+  const i32x4_t rw = rsrc4(wsplit, static_cast<uint32_t>(E) * 3u * row_bytes);
   uint32_t aoff[C::A_LOADS];
 #pragma unroll
   for (int p = 0; p < C::A_LOADS; ++p) {
@@ -390,8 +388,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void router_bf16_kernel(const uint1
     boff[p] = e < E ? static_cast<uint32_t>(e) * 3u * row_bytes : kInvalidRow;
   }
   f32x16_t acc[C::MI][C::NJ];
-  gemm_tile<C, false, kPrefetch>(lds, rx, aoff, rw, boff, k_begin, k_end, d,
-                         static_cast<int>(min<int64_t>(T - m * C::BM, C::BM)), acc);
+  gemm_tile<C, false>(lds, rx, aoff, rw, boff, k_begin, k_end, d, acc);
   float* out = partial + static_cast<int64_t>(split) * T * E;
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi)
@@ -436,20 +433,20 @@ int occupancy_blocks(K kernel, int threads) {
   return nb;
 }
 
-template <class C1, class C2, int PD1, int PD2>
+template <class C1, class C2>
 hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
-  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C1, PD1>, C1::NT);
-  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C2, PD2>, C2::NT);
+  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C1>, C1::NT);
+  if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C2>, C2::NT);
   const int cus = device_cu_count();
   // persistent grids, multiples of 8 for the XCD remap
   const int g1 = ((cus * occ1 + 7) / 8) * 8;
   const int g2 = ((cus * occ2 + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn1_bf16_kernel<C1, PD1>), dim3(g1), dim3(C1::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn1_bf16_kernel<C1>), dim3(g1), dim3(C1::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((ffn2_bf16_kernel<C2, PD2>), dim3(g2), dim3(C2::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn2_bf16_kernel<C2>), dim3(g2), dim3(C2::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -477,8 +474,8 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
-  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode, kPrefetch, kPrefetch>(a, s, mid);
-  return launch_ffn_bf16_cfg<TilePrefill, TilePrefill, kPrefetch, kPrefetch>(a, s, mid);
+  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode>(a, s, mid);
+  return launch_ffn_bf16_cfg<TilePrefill, TilePrefill>(a, s, mid);
 }
 
 int router_splits(int64_t T, int d, int E, int act_dtype) {
