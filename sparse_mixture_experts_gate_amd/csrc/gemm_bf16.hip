@@ -68,30 +68,6 @@ __device__ __forceinline__ int b_local_row(int wn, int nj) {
   }
 }
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor as four scalar words: base address, no stride,
-// `bytes` records (range-checked: offsets at or beyond it read as zeros).
-__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = static_cast<int>(static_cast<uint32_t>(b));
-  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);
-  r[2] = static_cast<int>(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from a buffer straight into LDS (buffer_load ... lds):
-// lane i writes lds_addr + 16 i, lds_addr wave-uniform (in M0). The load has
-// no register result, so nothing is in flight towards a VGPR; its completion
-// is waited for with vmcnt (the compiler does not track these loads, so the
-// GEMM loop places its own waits).
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
 // acc[mi][nj] += A * B^T over k in [k_begin, k_end) (multiples of 64).
 // Operands come from buffers (ra, rb) through a 32-bit byte offset per thread
 // and row (the k = 0 element of the row); offsets at or beyond the buffer
@@ -127,8 +103,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
 #pragma unroll
   for (int p = 0; p < C::B_LOADS; ++p)
     bo[p] = boff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
-  // LDS byte address of the block (the low 32 bits of a flat LDS address)
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const uint32_t lds0 = lds_addr(lds);
   // this wave's 8 rows of each load pass start at row 8 * wave
   auto issue = [&](int st, int k0) {
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
@@ -455,14 +430,7 @@ hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) 
 GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
   GemmTiling t{};
   const double rows_per_expert = static_cast<double>(T) * K / E;
-  if (w_dtype == 2) {  // FP8: 128 intermediate columns per gate/up tile; see gemm_fp8.hip
-    if (rows_per_expert < 48.0) {
-      t.bm1 = 32; t.bnh1 = 128; t.bm2 = 32; t.bn2 = 128; t.variant = 1;
-    } else {
-      t.bm1 = 128; t.bnh1 = 128; t.bm2 = 128; t.bn2 = 128; t.variant = 0;
-    }
-    return t;
-  }
+  if (w_dtype == 2) return choose_tiling_fp8(rows_per_expert);
   if (rows_per_expert < 48.0) {
     t.bm1 = TileDecode::BM; t.bnh1 = TileDecode::BN / 2;
     t.bm2 = TileDecode::BM; t.bn2 = TileDecode::BN; t.variant = 1;

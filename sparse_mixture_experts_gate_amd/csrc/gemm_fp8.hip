@@ -24,14 +24,12 @@ namespace dsmoe {
 namespace {
 
 constexpr int BK8 = 128;  // E4M3 elements (bytes) per row per stage = one scale block
-// Global loads run this many k blocks ahead. One: the k block's MFMAs and
-// fp32 rescaling keep this kernel compute-bound, and a second register stage
-// does not fit beside the accumulators without spilling.
-constexpr int kPrefetch8 = 1;
 
-template <int BM_, int BN_, int WM_, int WN_>
+// BM x BN tile in waves of WM x WN; NST LDS stages in the load ring (loads run
+// NST - 1 k blocks ahead).
+template <int BM_, int BN_, int WM_, int WN_, int NST_ = 3>
 struct Tile8 {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -40,14 +38,18 @@ struct Tile8 {
   static constexpr int A_LOADS = BM / RPP;
   static constexpr int B_LOADS = BN / RPP;
   static constexpr int STAGE = (BM + BN) * BK8;  // bytes
+  static constexpr int LDS_BYTES = NST * STAGE;
+  // loads per thread and k block: A and B tiles, one row scale, two block scales
+  static constexpr int NL = A_LOADS + B_LOADS + 3;
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(BM <= NT, "one thread per row loads the activation scales");
+  static_assert(NST >= 3 && NL * (NST - 2) <= 63, "ring depth within the vmcnt range");
 };
 
-using T8Gate = Tile8<128, 256, 64, 64>;     // 8 waves, H tile 128 x 128, 96 KB LDS
-using T8Down = Tile8<128, 128, 64, 64>;     // 4 waves, 64 KB LDS
-using T8GateDec = Tile8<32, 256, 32, 64>;   // 4 waves
-using T8DownDec = Tile8<32, 128, 32, 64>;   // 2 waves
+using T8Gate = Tile8<128, 256, 64, 64>;        // 8 waves, H tile 128 x 128, 144 KB ring
+using T8Down = Tile8<128, 256, 64, 64>;        // 8 waves, 144 KB ring
+using T8GateDec = Tile8<32, 256, 32, 64, 4>;   // 4 waves, 144 KB ring
+using T8DownDec = Tile8<32, 128, 32, 64, 6>;   // 2 waves, 120 KB ring
 
 // Byte offset of 16-byte chunk `ch` of row `r`, swizzled with (r >> 1) & 7 so
 // that the 16 rows one 128-bit LDS access serves spread over all 64 banks.
@@ -77,33 +79,25 @@ __device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
 // acc[mi][nj] += sum over 128-wide k blocks kb of
 //   (A_kb B_kb^T) * s_a[row][kb] * s_b[kb]   (s_b: sb_lo for the first half of
 // the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
-// Scales come through buffer resources too: rsa + sa_off is the byte offset of
-// this thread's row of activation scales when threadIdx.x < BM (kInvalidRow
-// otherwise or for padding rows, which reads zeros); rsb + sb_lo / sb_hi are
-// byte offsets of the weight block scales of the tile's columns.
-// Operands come through buffer resources (padding rows read as zeros); global
-// loads, scales included, run kPrefetch8 k blocks ahead in rotating register
-// sets; LDS is double buffered.
-template <class C>
-struct Stage8 {
-  uint4 a[C::A_LOADS];
-  uint4 b[C::B_LOADS];
-  float sa, sbl, sbh;
-};
-
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
+// Scales come from buffers too: rsa + sa_off is the byte offset of this
+// thread's row of activation scales (kInvalidRow for threads past BM and for
+// padding rows, which reads zeros); rsb + sb_lo / sb_hi are byte offsets of
+// the weight block scales of the tile's gate (lo) and up (hi) columns.
+//
+// All loads go from global memory straight into a ring of NST LDS stages,
+// NST - 1 k blocks ahead, with one barrier per k block: the code tiles with
+// 16-byte loads (lane (row r, position ch) fetches logical chunk
+// ch ^ swizzle(r), giving the layout lds_off8 describes), the row scales with
+// one 4-byte load per lane into lds_sa[stage][thread], the two block scales
+// with lane-0-only 4-byte loads into the wave's own slot of lds_sb. Every
+// wave issues the same number of loads per k block, so one vmcnt bound holds
+// for all of them.
 template <class C, bool SWIGLU>
-__device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
-                                           __amdgpu_buffer_rsrc_t ra,
-                                           const uint32_t (&aoff)[C::A_LOADS],
-                                           __amdgpu_buffer_rsrc_t rsa, uint32_t sa_off,
-                                           __amdgpu_buffer_rsrc_t rb,
-                                           const uint32_t (&boff)[C::B_LOADS],
-                                           __amdgpu_buffer_rsrc_t rsb, uint32_t sb_lo,
-                                           uint32_t sb_hi, int K, int rows_valid,
+__device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa, float* lds_sb, i32x4_t ra,
+                                           const uint32_t (&aoff)[C::A_LOADS], i32x4_t rsa,
+                                           uint32_t sa_off, i32x4_t rb,
+                                           const uint32_t (&boff)[C::B_LOADS], i32x4_t rsb,
+                                           uint32_t sb_lo, uint32_t sb_hi, int K,
                                            f32x4_t (&acc)[C::MI][C::NJ]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,53 +107,52 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
   for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // padding rows hold zero codes and are multiplied like the others: a
-  // per-group skip becomes selects on every product and accumulator
-  (void)rows_valid;
-
-  auto gload = [&](Stage8<C>& R, int kb) {
-    const uint32_t off = static_cast<uint32_t>(kb * BK8 + ch * 16);
+  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
 #pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p)
-      R.a[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[p] + off, 0, 0));
+  for (int p = 0; p < C::A_LOADS; ++p)
+    ao[p] = aoff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
 #pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p)
-      R.b[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[p] + off, 0, 0));
-    R.sa = load_f32(rsa, sa_off + static_cast<uint32_t>(kb) * 4u);
-    R.sbl = load_f32(rsb, sb_lo + static_cast<uint32_t>(kb) * 4u);
-    R.sbh = SWIGLU ? load_f32(rsb, sb_hi + static_cast<uint32_t>(kb) * 4u) : R.sbl;
-  };
-  // LDS scales per stage: row scale x weight block scale, for the gate half
-  // (then the up half with SWIGLU) of the tile's columns, one per row
-  constexpr int SA_STRIDE = SWIGLU ? 2 * C::BM : C::BM;
-  auto sstore = [&](const Stage8<C>& R, int st) {
-    uint8_t* As = lds + st * C::STAGE;
-    uint8_t* Bs = As + C::BM * BK8;
+  for (int p = 0; p < C::B_LOADS; ++p)
+    bo[p] = boff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+  const uint32_t lds0 = lds_addr(lds), sa0 = lds_addr(lds_sa), sb0 = lds_addr(lds_sb);
+  auto issue = [&](int st, int kb) {
+    const uint32_t off = static_cast<uint32_t>(kb) * BK8;
+    const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + st * C::STAGE + wave * 8 * BK8);
+    const uint32_t b_base = a_base + C::BM * BK8;
 #pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p)
-      *reinterpret_cast<uint4*>(As + lds_off8(r0 + p * C::RPP, ch)) = R.a[p];
+    for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + off, a_base + p * C::RPP * BK8);
 #pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p)
-      *reinterpret_cast<uint4*>(Bs + lds_off8(r0 + p * C::RPP, ch)) = R.b[p];
-    if (tid < C::BM) {
-      lds_sa[st * SA_STRIDE + tid] = R.sa * R.sbl;
-      if constexpr (SWIGLU) lds_sa[st * SA_STRIDE + C::BM + tid] = R.sa * R.sbh;
+    for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + off, b_base + p * C::RPP * BK8);
+    const uint32_t kb4 = static_cast<uint32_t>(kb) * 4u;
+    dma4(rsa, sa_off + kb4,
+         __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
+    const uint32_t sb_base =
+        __builtin_amdgcn_readfirstlane(sb0 + ((st * C::NWAVES + wave) * 2) * 4);
+    if (lane == 0) {
+      dma4(rsb, sb_lo + kb4, sb_base);
+      dma4(rsb, sb_hi + kb4, sb_base + 4);
     }
   };
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int st) {
     const uint8_t* As = lds + st * C::STAGE;
     const uint8_t* Bs = As + C::BM * BK8;
+    const float s_lo = lds_sb[(st * C::NWAVES + wave) * 2];
+    const float s_hi = SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
     const int kg = lane >> 4;
     i32x8_t bfr[C::NJ];
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
     auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
-    // combined scales of the lane's 4 rows in 16-row group m, gate (lo) and up (hi)
+    // row scale x block scale for the lane's 4 rows of 16-row group m
     auto row_scales = [&](int m, f32x4_t& s_l, f32x4_t& s_h) {
-      const float* base = lds_sa + st * SA_STRIDE + wm * C::WM + m * 16 + 4 * kg;
-      s_l = *reinterpret_cast<const f32x4_t*>(base);
-      s_h = SWIGLU ? *reinterpret_cast<const f32x4_t*>(base + C::BM) : s_l;
+      const f32x4_t sa =
+          *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::NT + wm * C::WM + m * 16 + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s_l[r] = sa[r] * s_lo;
+        s_h[r] = sa[r] * s_hi;
+      }
     };
     // Software pipeline over the MI x NJ products of the k block: MFMA t runs
     // in the matrix core while the VALU folds product t-1 into its
@@ -200,46 +193,38 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa,
     }
   };
 
+  constexpr int NST = C::NST;
+  constexpr int INFLIGHT = C::NL * (NST - 2);  // loads of the NST - 2 newest k blocks
   const int nk = K / BK8;
   if (nk <= 0) return;
-  // Unconditional loads with the block index clamped to the last one, a
-  // branch-free main loop over full groups of kPrefetch8 blocks and a tail
-  // without loads: a load under a branch makes the compiler wait for the
-  // loads just issued before every LDS store (same scheme as the bf16 GEMMs).
+  // k blocks past the end reload the last one (in bounds, never read)
   auto kpos = [&](int k) { return k < nk ? k : nk - 1; };
-  Stage8<C> S[kPrefetch8];
 #pragma unroll
-  for (int j = 0; j < kPrefetch8; ++j) gload(S[j], kpos(j));
-  sstore(S[0], 0);
+  for (int j = 0; j < NST - 1; ++j) issue(j, kpos(j));
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");  // stage 0 has landed
   __syncthreads();
-  const int nfull = nk - nk % kPrefetch8;
-  for (int k0 = 0; k0 < nfull; k0 += kPrefetch8) {
-#pragma unroll
-    for (int j = 0; j < kPrefetch8; ++j) {
-      const int k = k0 + j;
-      gload(S[j], kpos(k + kPrefetch8));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(k & 1);
-      sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
-      __syncthreads();
-    }
+  int st = 0, st_issue = NST - 1;
+  for (int k = 0; k < nk; ++k) {
+    issue(st_issue, kpos(k + NST - 1));  // the stage read in block k - 1
+    compute(st);
+    // this wave's part of stage k+1 has landed; the barrier makes every
+    // wave's part visible and frees stage k
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");
+    __syncthreads();
+    st = st == NST - 1 ? 0 : st + 1;
+    st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
   }
-#pragma unroll
-  for (int j = 0; j < kPrefetch8 - 1; ++j) {
-    const int k = nfull + j;
-    if (k < nk) {
-      compute(k & 1);
-      if (k + 1 < nk) sstore(S[(j + 1) % kPrefetch8], (k + 1) & 1);
-      __syncthreads();
-    }
-  }
+  // the loads of the clamped last blocks land before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // H (E4M3 + 1x128 scales) = quant(silu(A W1^T) * (A W3^T)); tile = 128 H columns.
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float lds_sa[2 * 2 * C::BM];  // 2 stages x gate, up
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_sa[C::NST * C::NT];
+  __shared__ __attribute__((aligned(16))) float lds_sb[C::NST * C::NWAVES * 2];
   __shared__ float red[C::WAVES_N][C::BM];
   __shared__ int gtab[kMaxGroups + 1];
   constexpr int HALF = C::BN / 2;  // 128 H columns
@@ -254,16 +239,16 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
   const int dkb = a.d / 128;
   const int hkb = a.ldh / 128;
   const float* XS = a.perm ? a.x_scale : a.xperm_scale;
-  const __amdgpu_buffer_rsrc_t rx =
-      a.perm ? buf_rsrc(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d))
-             : buf_rsrc(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
-  const __amdgpu_buffer_rsrc_t rxs =
-      buf_rsrc(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
+  const i32x4_t rx =
+      a.perm ? rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d))
+             : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
+  const i32x4_t rxs =
+      rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
   // activation scales: gathered rows (or x_perm rows) and the shared rows
-  const __amdgpu_buffer_rsrc_t rsxp =
-      buf_rsrc(XS, static_cast<uint32_t>(a.perm ? a.T : a.TK) * static_cast<uint32_t>(dkb) * 4u);
-  const __amdgpu_buffer_rsrc_t rsx =
-      buf_rsrc(a.x_scale, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(dkb) * 4u);
+  const i32x4_t rsxp =
+      rsrc4(XS, static_cast<uint32_t>(a.perm ? a.T : a.TK) * static_cast<uint32_t>(dkb) * 4u);
+  const i32x4_t rsx =
+      rsrc4(a.x_scale, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(dkb) * 4u);
   uint8_t* H = static_cast<uint8_t*>(a.H);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
@@ -301,7 +286,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
                                     static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
     const float* WS = shared ? a.ws13_scale
                              : a.w13_scale + static_cast<int64_t>(tc.g) * (2 * a.I / 128) * dkb;
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(2 * Ig) * a.d);
+    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(2 * Ig) * a.d);
     uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
@@ -310,13 +295,13 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       const int col = tc.n * HALF + (up ? lr - HALF : lr);
       boff[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
     }
-    const __amdgpu_buffer_rsrc_t rws =
-        buf_rsrc(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
+    const i32x4_t rws =
+        rsrc4(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
     const uint32_t sb_gate = static_cast<uint32_t>(tc.n * dkb) * 4u;
     const uint32_t sb_up = static_cast<uint32_t>((Ig / 128 + tc.n) * dkb) * 4u;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, true>(lds, lds_sa, shared ? rxs : rx, aoff, shared ? rsx : rsxp, sa_off, rw,
-                        boff, rws, sb_gate, sb_up, a.d, tc.rows - tc.m * C::BM, acc);
+    gemm8_tile<C, true>(lds, lds_sa, lds_sb, shared ? rxs : rx, aoff, shared ? rsx : rsxp, sa_off,
+                        rw, boff, rws, sb_gate, sb_up, a.d, acc);
 
     // SwiGLU, then the row max-abs over the 128 columns (across the wave's
     // 16-lane groups and the tile's WAVES_N waves)
@@ -382,8 +367,9 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
 // y = dequant(H) dequant(W2)^T per group, bf16 out.
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float lds_sa[2 * C::BM];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_sa[C::NST * C::NT];
+  __shared__ __attribute__((aligned(16))) float lds_sb[C::NST * C::NWAVES * 2];
   __shared__ int gtab[kMaxGroups + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -394,10 +380,10 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   const int nb = gridDim.x;
   const int hkb = a.ldh / 128;
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const __amdgpu_buffer_rsrc_t rh =
-      buf_rsrc(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
-  const __amdgpu_buffer_rsrc_t rsh =
-      buf_rsrc(a.H_scale, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(hkb) * 4u);
+  const i32x4_t rh =
+      rsrc4(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
+  const i32x4_t rsh =
+      rsrc4(a.H_scale, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(hkb) * 4u);
   for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
     TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
     tc.g = __builtin_amdgcn_readfirstlane(tc.g);
@@ -425,19 +411,22 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
     const int ikb = Ig / 128;
     const float* WS = shared ? a.ws2_scale
                              : a.w2_scale + static_cast<int64_t>(tc.g) * (a.d / 128) * (a.I / 128);
-    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W, static_cast<uint32_t>(a.d) * static_cast<uint32_t>(Ig));
+    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(a.d) * static_cast<uint32_t>(Ig));
     uint32_t boff[C::B_LOADS];
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int row = tc.n * C::BN + r0 + p * C::RPP;
       boff[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
     }
-    const __amdgpu_buffer_rsrc_t rws =
-        buf_rsrc(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
-    const uint32_t sb = static_cast<uint32_t>(((tc.n * C::BN) / 128) * ikb) * 4u;
+    const i32x4_t rws =
+        rsrc4(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
+    // weight block scales of this wave's WN output columns (inside one
+    // 128-row block of W2)
+    static_assert(128 % C::WN == 0, "a wave's columns lie in one scale block");
+    const uint32_t sb = static_cast<uint32_t>(((tc.n * C::BN + wn * C::WN) / 128) * ikb) * 4u;
     f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, false>(lds, lds_sa, rh, aoff, rsh, sa_off, rw, boff, rws, sb, sb, Ig,
-                         rows_left, acc);
+    gemm8_tile<C, false>(lds, lds_sa, lds_sb, rh, aoff, rsh, sa_off, rw, boff, rws, sb, sb, Ig,
+                         acc);
 
     uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
                                  static_cast<int64_t>(tc.m) * C::BM * a.d
@@ -484,6 +473,18 @@ hipError_t launch_fp8_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
 }
 
 }  // namespace
+
+GemmTiling choose_tiling_fp8(double rows_per_expert) {
+  GemmTiling t{};
+  if (rows_per_expert < 48.0) {
+    t.bm1 = T8GateDec::BM; t.bnh1 = T8GateDec::BN / 2;
+    t.bm2 = T8DownDec::BM; t.bn2 = T8DownDec::BN; t.variant = 1;
+  } else {
+    t.bm1 = T8Gate::BM; t.bnh1 = T8Gate::BN / 2;
+    t.bm2 = T8Down::BM; t.bn2 = T8Down::BN; t.variant = 0;
+  }
+  return t;
+}
 
 hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
   if (t.variant == 1) return launch_fp8_pair<T8GateDec, T8DownDec>(a, s, mid);

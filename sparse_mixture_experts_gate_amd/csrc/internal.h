@@ -87,6 +87,8 @@ struct GemmTiling {
 };
 
 GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype);
+// FP8 tiles (gemm_fp8.hip), by the mean number of rows per expert.
+GemmTiling choose_tiling_fp8(double rows_per_expert);
 // `mid` (may be NULL) is recorded between the gate/up and the down GEMM.
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s, hipEvent_t mid);

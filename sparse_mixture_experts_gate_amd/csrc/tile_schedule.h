@@ -56,6 +56,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
                                            static_cast<int>(bytes), 0x00020000);
 }
 
+// Raw buffer descriptor as four scalar words: base address, no stride,
+// `bytes` records (range-checked: offsets at or beyond it read as zeros).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(b));
+  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// LDS byte address of a pointer into __shared__ memory (the low 32 bits of
+// its flat address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Buffer loads straight into LDS (buffer_load ... lds): lane i writes
+// lds_addr + 16 i (dma16) or + 4 i (dma4), lds_addr wave-uniform (in M0).
+// The loads have no register result, so nothing is in flight towards a VGPR;
+// the compiler does not track them, so callers wait with explicit vmcnt
+// (and keep no compiler-visible vector loads between those waits, whose
+// counts would not include these).
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
 // Output tile staging: values are written to LDS as bf16 at (row, col), rows
 // padded by 16 bytes so the two row groups one store instruction touches fall
 // in different banks; then whole rows leave with 16-byte stores.
