@@ -147,7 +147,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times, so that HBM byte "
                          "counters can be scaled against a kernel of known traffic")
