@@ -283,3 +283,39 @@ def test_fp8_quantizers_bit_exact():
     rq, rs = O.quantize_rows_1x128(host(x))
     assert np.array_equal(host(xq), rq)
     assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", ["bf16", "fp8"])
+def test_all_tokens_on_the_same_experts(w):
+    """A bias that outweighs every affinity (sigmoid < 1 < bias) sends all
+    tokens to the same K experts: K segments of T rows next to empty experts,
+    the extreme of load skew. Routing is checked on the kernel's logits and
+    every token's output against the oracle."""
+    wl = Workload("skew", T=1500, d=256, E=16, K=4, I=256, Is=128, G=4, M=2, topn=2, act="bf16",
+                  w=w, x_kind="normal", bias_kind="uniform", bias_amp=0.05, w_std=0.05, seed=9)
+    _log(f"all tokens on experts 0..3, {w}")
+    P = make_inputs(wl, DEV)
+    P["bias"].zero_()
+    P["bias"][: wl.K] = 2.0
+    layer = M.MoELayer(wl, P)
+    g = {k: host(v) for k, v in forward(layer, P["x"]).items()}
+    rr = O.route(g["logits"], host(P["bias"]), **route_args(wl))
+    assert np.array_equal(g["topk_idx"], rr.idx)
+    assert np.array_equal(g["topk_gate"].view(np.uint32), rr.gate.view(np.uint32))
+    assert set(np.unique(rr.idx)) == set(range(wl.K))
+    assert np.array_equal(g["counts"][: wl.K], np.full(wl.K, wl.T))
+    assert not g["counts"][wl.K:].any()
+    x = host(P["x"])
+    if w == "bf16":
+        ref = oracle_rows(wl, P, np.arange(wl.T), rr.idx, rr.gate)
+    else:
+        q13 = {e: O.quantize_blocks_128(host(P["w13"][e])) for e in range(wl.K)}
+        q2 = {e: O.quantize_blocks_128(host(P["w2"][e])) for e in range(wl.K)}
+        s13 = O.quantize_blocks_128(host(P["ws13"]))
+        s2 = O.quantize_blocks_128(host(P["ws2"]))
+        ref = O.layer_output_fp8(x, rr.idx, rr.gate, {e: v[0] for e, v in q13.items()},
+                                 {e: v[1] for e, v in q13.items()}, {e: v[0] for e, v in q2.items()},
+                                 {e: v[1] for e, v in q2.items()}, s13[0], s13[1], s2[0], s2[1])
+    err = row_rel_err(g["y"], O.round_bf16(ref))
+    _log(f"  err {err:.3e}")
+    assert err <= TOL[w]
