@@ -12,6 +12,14 @@
       `bench.py --calibrate-copy` runs first: the copy reads and writes
       exactly 1 GiB. Writes <out-dir>/traffic_<name>_<workload>.json (read by
       bench.py while the kernel source is unchanged) and a markdown summary.
+
+  python profile_summary.py kernels <kernel_stats.csv> <fetch csv> <write csv>
+      <mfma csv> <workload> <commands-file>
+      Per library kernel: mean duration (kernel trace), HBM bytes read and
+      written per dispatch (FETCH_SIZE / WRITE_SIZE, scaled as above), the
+      achieved HBM rate against 8 TB/s, and the MFMA pipe busy fraction
+      (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x 1024 SIMDs).
+      Markdown on stdout.
 """
 import collections
 import csv
@@ -113,12 +121,54 @@ def traffic(fetch_csv, write_csv, sub, name, workload, source, out_dir, cmd_f, c
     print(json.dumps(rec))
 
 
+HBM_PEAK = 8e12
+N_XCD, N_SIMD = 8, 1024
+
+
+def _means(path: str, counter: str):
+    return {k: sum(v) / len(v) for k, v in _per_dispatch(path, counter).items()}
+
+
+def kernels(stats_csv, fetch_csv, write_csv, mfma_csv, workload, cmd_file) -> str:
+    dur = {r["Name"]: float(r["AverageNs"]) * 1e-9
+           for r in csv.DictReader(open(_find(stats_csv, "kernel_stats.csv")))}
+    pf, pw = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = GIB_KIB / (sum(sorted(pf[COPY])[-3:]) / 3)
+    w_scale = GIB_KIB / (sum(sorted(pw[COPY])[-3:]) / 3)
+    busy, grbm = _means(mfma_csv, "SQ_VALU_MFMA_BUSY_CYCLES"), _means(mfma_csv, "GRBM_GUI_ACTIVE")
+    out = [f"# Per-kernel counters: {workload}", "",
+           "Commands (from the repository root), one counter group per run, then this summary:",
+           "", "```", open(cmd_file).read().strip(), "```", "",
+           f"HBM bytes are FETCH_SIZE x {f_scale:.4f} and WRITE_SIZE x {w_scale:.4f} "
+           "(calibrated on plain 1 GiB copies), per dispatch; GB/s uses the kernel-trace mean "
+           "duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 "
+           "SIMDs).", "",
+           "| kernel | mean µs | read GB | written GB | HBM GB/s | % of 8 TB/s | MFMA busy |",
+           "|---|---|---|---|---|---|---|"]
+    for name in sorted(dur, key=lambda n: -dur[n]):
+        if "dsmoe" not in name or name not in pf:
+            continue
+        rd = sum(pf[name]) / len(pf[name]) * f_scale * 1024
+        wr = sum(pw[name]) / len(pw[name]) * w_scale * 1024 if name in pw else 0.0
+        gbs = (rd + wr) / dur[name] / 1e9
+        mf = ""
+        if name in busy and grbm.get(name):
+            mf = f"{busy[name] / (grbm[name] / N_XCD * N_SIMD):.1%}"
+        short = name.replace("dsmoe::(anonymous namespace)::", "")[:70]
+        out.append(f"| `{short}` | {dur[name] * 1e6:.1f} | {rd / 1e9:.4f} | {wr / 1e9:.4f} | "
+                   f"{gbs:.0f} | {gbs * 1e9 / HBM_PEAK:.1%} | {mf} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[0] == "stats":
         sys.stdout.write(stats(argv[1], argv[2], argv[3]))
         return 0
     if len(argv) == 10 and argv[0] == "traffic":
         traffic(*argv[1:])
+        return 0
+    if len(argv) == 7 and argv[0] == "kernels":
+        sys.stdout.write(kernels(*argv[1:]))
         return 0
     print(__doc__, file=sys.stderr)
     return 2
