@@ -84,8 +84,9 @@ typedef enum moe_dtype {
  * Divisibility: d, I, Is multiples of 64 for BF16/F32 weights and of 128 for
  * FP8 weights. The router weights and bias are always fp32. Size limits (the
  * kernels use 32-bit byte offsets): T*d*sizeof(x), T*(K+1)*max(I,Is)*sizeof(H)
- * (H is bf16 / fp32 / one byte with FP8), one expert's weights and 6*E*d must
- * each stay below 2^31 bytes; larger calls return MOE_ERR_UNSUPPORTED. */
+ * (H is bf16 / fp32 / one byte with FP8), one expert's weights, 6*E*d and
+ * T*K*4 (the int32 selections) must each stay below 2^31 bytes; larger calls
+ * return MOE_ERR_UNSUPPORTED. */
 typedef struct moe_layer_desc {
   int64_t T;
   int32_t d;

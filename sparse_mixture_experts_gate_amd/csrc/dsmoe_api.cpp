@@ -85,6 +85,9 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_ERR_UNSUPPORTED, "d, inter, shared_inter must be multiples of %d", mult);
   if (d->T * static_cast<int64_t>(d->top_k) + d->T >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*(K+1) must be < 2^31");
+  // the permutation reads topk_idx through a 32-bit byte range
+  if (d->T * static_cast<int64_t>(d->top_k) * 4 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*K*4 must be < 2^31 bytes");
   // the GEMMs address x, H and each expert's weights with 32-bit byte offsets
   const int64_t lim = (int64_t(1) << 31) - 1;
   const int64_t s_act = d->act_dtype == MOE_DT_F32 ? 4 : 2;

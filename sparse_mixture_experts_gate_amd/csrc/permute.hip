@@ -74,13 +74,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
 }
 
-// One workgroup per expert: scans every (t, k) pair in token order and gives
-// the matches consecutive positions, so the order inside an expert is the
-// ascending token order without depending on atomics. Each thread owns
-// kPermTok consecutive tokens per pass; a workgroup-wide exclusive scan of the
-// per-thread match counts places them.
+// One workgroup per expert: scans the flat selections idx[t * K + k] in
+// order and gives the matches consecutive positions, so the order inside an
+// expert is the ascending token order (a token selects an expert at most
+// once, so flat order is token order) without depending on atomics. Each
+// thread owns kPermEnt consecutive flat entries per pass, read with 16-byte
+// buffer loads (coalesced across the wave); the next pass's loads are issued
+// before the current pass is placed; a workgroup-wide exclusive scan of the
+// per-thread match counts places the matches.
 constexpr int kPermThreads = 1024;
-constexpr int kPermTok = 4;
+constexpr int kPermEnt = 16;  // four 16-byte loads
+constexpr int64_t kPermPass = static_cast<int64_t>(kPermThreads) * kPermEnt;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ offsets,
@@ -93,23 +97,38 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   const int base = offsets[e];
   if (offsets[e + 1] == base) return;
   const int64_t TK = T * K;
-  int running = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += static_cast<int64_t>(kPermThreads) * kPermTok) {
-    const int64_t tb = t0 + static_cast<int64_t>(tid) * kPermTok;
-    int slot[kPermTok];
-    int mine = 0;
+  // flat entries past TK read as zeros (range-checked) and are masked below
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(idx), static_cast<short>(0),
+                                        static_cast<int>(TK * 4), 0x00020000);
+  auto load = [&](int64_t pass, uint4 (&v)[kPermEnt / 4]) {
+    const int64_t f0 = pass * kPermPass + static_cast<int64_t>(tid) * kPermEnt;
 #pragma unroll
-    for (int q = 0; q < kPermTok; ++q) {
-      slot[q] = -1;
-      const int64_t t = tb + q;
-      if (t < T) {
-        const int32_t* row = idx + t * K;
-        for (int k = 0; k < K; ++k)
-          if (row[k] == e) slot[q] = k;
-      }
-      mine += slot[q] >= 0;
+    for (int q = 0; q < kPermEnt / 4; ++q) {
+      const int64_t f = f0 + 4 * q;
+      v[q] = f < TK ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    r, static_cast<uint32_t>(f * 4), 0, 0))
+                    : make_uint4(0, 0, 0, 0);
     }
-    // inclusive scan of `mine` inside the wave
+  };
+  const int64_t npass = (TK + kPermPass - 1) / kPermPass;
+  uint4 cur[kPermEnt / 4], nxt[kPermEnt / 4];
+  load(0, cur);
+  int running = 0;
+  for (int64_t pass = 0; pass < npass; ++pass) {
+    if (pass + 1 < npass) load(pass + 1, nxt);
+    const int64_t f0 = pass * kPermPass + static_cast<int64_t>(tid) * kPermEnt;
+    uint32_t match = 0;  // bit j: entry f0 + j selects expert e
+#pragma unroll
+    for (int q = 0; q < kPermEnt / 4; ++q) {
+      const int32_t v4[4] = {static_cast<int32_t>(cur[q].x), static_cast<int32_t>(cur[q].y),
+                             static_cast<int32_t>(cur[q].z), static_cast<int32_t>(cur[q].w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v4[j] == e && f0 + 4 * q + j < TK) match |= 1u << (4 * q + j);
+    }
+    const int mine = __builtin_popcount(match);
+    // inclusive scan of `mine` inside the wave, then across the waves
     int incl = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -125,18 +144,20 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
       tot += wsum[q];
     }
     int pos = base + running + pre + incl - mine;
-#pragma unroll
-    for (int q = 0; q < kPermTok; ++q) {
-      if (slot[q] >= 0) {
-        if (pos < TK) {  // guards counts that disagree with topk_idx
-          perm[pos] = static_cast<int32_t>(tb + q);
-          inv[(tb + q) * K + slot[q]] = pos;
-        }
-        ++pos;
+    while (match) {
+      const int j = __builtin_ctz(match);
+      match &= match - 1;
+      const int64_t f = f0 + j;
+      if (pos < TK) {  // guards counts that disagree with topk_idx
+        perm[pos] = static_cast<int32_t>(f / K);
+        inv[f] = pos;
       }
+      ++pos;
     }
     running += tot;
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPermEnt / 4; ++q) cur[q] = nxt[q];
   }
 }
 
