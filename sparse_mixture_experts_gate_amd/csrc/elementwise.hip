@@ -12,37 +12,56 @@ namespace {
 // is ungated and sees every token (mhpq.cn "DeepSeek-V3 高效训练关键技术全景
 // 解析" §1.1); routed outputs weighted by the normalized gates (kaiyunto.com
 // DeepSeek-V3 walkthrough). One workgroup per token, 16-byte accesses,
-// fp32 accumulation in slot order.
+// fp32 accumulation in slot order. KT > 0 fixes K at compile time so the K
+// gathered rows of a chunk are all loaded before the (in-order) FMAs.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(w[q] << 16);
+    f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+}
+
+template <int KT>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ yperm,
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ gate,
                                                            const uint16_t* __restrict__ yshared,
-                                                           uint16_t* __restrict__ y, int K, int d) {
+                                                           uint16_t* __restrict__ y, int K_rt, int d) {
+  const int K = KT > 0 ? KT : K_rt;
   const int64_t t = blockIdx.x;
   const int nch = d / 8;
   for (int c = threadIdx.x; c < nch; c += blockDim.x) {
     float acc[8];
     if (yshared) {
-      const uint4 v = *reinterpret_cast<const uint4*>(yshared + t * d + c * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = __uint_as_float(w[q] << 16);
-        acc[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-      }
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(yshared + t * d + c * 8), acc);
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     }
-    for (int k = 0; k < K; ++k) {
-      const float g = gate[t * K + k];
-      const int64_t row = inv[t * K + k];
-      const uint4 v = *reinterpret_cast<const uint4*>(yperm + row * d + c * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (KT > 0) {
+      uint4 v[KT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = __builtin_fmaf(g, __uint_as_float(w[q] << 16), acc[2 * q]);
-        acc[2 * q + 1] = __builtin_fmaf(g, __uint_as_float(w[q] & 0xFFFF0000u), acc[2 * q + 1]);
+      for (int k = 0; k < KT; ++k)
+        v[k] = *reinterpret_cast<const uint4*>(yperm + static_cast<int64_t>(inv[t * KT + k]) * d +
+                                               c * 8);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float g = gate[t * KT + k];
+        float f[8];
+        bf16x8_to_f32(v[k], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g, f[q], acc[q]);
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const float g = gate[t * K + k];
+        float f[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(
+                          yperm + static_cast<int64_t>(inv[t * K + k]) * d + c * 8), f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g, f[q], acc[q]);
       }
     }
     uint4 o;
@@ -202,11 +221,18 @@ hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* ga
                           const void* yshared, void* y, int64_t T, int K, int d, int io_dtype,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (io_dtype == 1)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(yperm), inv, gate,
-                       static_cast<const uint16_t*>(yshared), static_cast<uint16_t*>(y), K, d);
-  else
+  if (io_dtype == 1) {
+    const auto* yp = static_cast<const uint16_t*>(yperm);
+    const auto* ys = static_cast<const uint16_t*>(yshared);
+    auto* yo = static_cast<uint16_t*>(y);
+    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    if (K == 8)
+      hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
+    else if (K == 6)
+      hipLaunchKernelGGL(combine_bf16_kernel<6>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
+    else
+      hipLaunchKernelGGL(combine_bf16_kernel<0>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
+  } else
     hipLaunchKernelGGL(combine_f32_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
                        static_cast<const float*>(yperm), inv, gate,
                        static_cast<const float*>(yshared), static_cast<float*>(y), K, d);
