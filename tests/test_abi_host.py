@@ -55,6 +55,9 @@ def _desc(L, **kw):
     (dict(n_groups=4, topk_groups=2, group_topn=5), 1), (dict(inter=0), 1),
     (dict(shared_inter=-1), 1), (dict(act_dtype=0), 2), (dict(w_dtype=2, d=192), 2),
     (dict(d=200), 2), (dict(inter=96), 2), (dict(near_tie_eps=float("nan")), 1),
+    # 32-bit byte-offset limits: x, H, one expert's weights, the split router weights
+    (dict(T=1 << 22), 2), (dict(T=1 << 20, inter=1024), 2), (dict(inter=1 << 21), 2),
+    (dict(n_experts=512, d=699072), 2),
 ])
 def test_descriptor_validation(L, kw, status):
     n = ctypes.c_size_t(0)
