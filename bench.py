@@ -232,6 +232,20 @@ def main() -> int:
                             "hbm_frac": a8["layer_bytes"] / (ms8 / 1e3) / HBM_PEAK,
                             "stage_ms": r8["stage_ms"]}
             log(f"fp8: {ms8:.3f} ms, {wl8.T / ms8 * 1e3 / 1e6:.3f} M tok/s")
+            dec8 = {}
+            for T in (16, 64, 256):
+                x = make_tokens(CONFIGS["v3_decode_bf16"], T, 3, dev)
+                rd = time_layer(layer8, x, 20, 3, bias_update=False)
+                nt = int((rd["out"]["counts"] > 0).sum())
+                a = algorithmic(wl8, T, nt)
+                dms = rd["wall_ms_per_step"]
+                dec8[str(T)] = {"ms": dms, "tokens_per_s": T / (dms / 1e3),
+                                "hbm_GBps": a["layer_bytes"] / (dms / 1e3) / 1e9,
+                                "hbm_frac": a["layer_bytes"] / (dms / 1e3) / HBM_PEAK,
+                                "n_touched": nt, "stage_ms": rd["stage_ms"]}
+                log(f"fp8 decode T={T}: {dms:.3f} ms, {dec8[str(T)]['hbm_GBps']:.0f} GB/s, "
+                    f"{nt} experts")
+            extra["decode_fp8"] = dec8
             del layer8
         except M.MoeError as e:
             extra["fp8"] = {"error": str(e)}

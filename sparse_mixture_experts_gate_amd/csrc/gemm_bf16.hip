@@ -68,19 +68,100 @@ __device__ __forceinline__ int b_local_row(int wn, int nj) {
   }
 }
 
-// acc[mi][nj] += A * B^T over k in [k_begin, k_end) (multiples of 64).
+// Global byte offsets of one thread's rows with the chunk swizzle folded in:
+// lane (row r, 16-byte position ch) fetches logical chunk ch ^ swizzle(r), so
+// the LDS image of a stage is the swizzled layout lds_off describes.
+template <class C, int N>
+__device__ __forceinline__ void swizzle_rows(uint32_t (&o)[N]) {
+  const int ch = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+  for (int p = 0; p < N; ++p)
+    o[p] += static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+}
+
+// Issues one k-step of A and B rows (byte offsets ao, bo plus ka, kb) from
+// global memory straight into ring stage st: no registers hold tiles in flight
+// and no LDS store instructions are issued. This wave's 8 rows of each load
+// pass start at row 8 * wave.
+template <class C>
+__device__ __forceinline__ void stage_issue(uint32_t lds0, int st, int wave, i32x4_t ra,
+                                            const uint32_t (&ao)[C::A_LOADS], uint32_t ka,
+                                            i32x4_t rb, const uint32_t (&bo)[C::B_LOADS],
+                                            uint32_t kb) {
+  const uint32_t a_base =
+      __builtin_amdgcn_readfirstlane(lds0 + (st * C::STAGE + wave * 8 * BK) * 2);
+  const uint32_t b_base = a_base + C::BM * BK * 2;
+#pragma unroll
+  for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + ka, a_base + p * C::RPP * BK * 2);
+#pragma unroll
+  for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + kb, b_base + p * C::RPP * BK * 2);
+}
+
+// acc += one 64-wide k-step of the tile in ring stage st. Within the step the
+// LDS fragments of the next 16-wide sub-step are read while the current one
+// multiplies. SWAP puts the B (weight) fragment first, so that acc holds the
+// transposed tile: lane l then owns output row l % 32 and, per group of four
+// registers, four adjacent output columns (one 8-byte bf16 store).
+template <class C, bool SWIGLU, bool SWAP>
+__device__ __forceinline__ void stage_mma(const uint16_t* lds, int st, int wm, int wn, int lane,
+                                          f32x16_t (&acc)[C::MI][C::NJ]) {
+  const uint16_t* As = lds + st * C::STAGE;
+  const uint16_t* Bs = As + C::BM * BK;
+  bf16x8_t af[2][C::MI], bfr[2][C::NJ];
+  auto fetch = [&](int kk, int buf) {
+    const int chk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj)
+      bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
+          Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
+          As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+    // the reads above go out before this sub-step's MFMAs (the scheduler
+    // would otherwise reuse their registers and serialize read and multiply)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        if constexpr (SWAP)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][nj], af[kk & 1][mi],
+                                                                acc[mi][nj], 0, 0, 0);
+        else
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bfr[kk & 1][nj],
+                                                                acc[mi][nj], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::MI][C::NJ]) {
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+}
+
+// loads of the NST - 2 newest steps that may stay in flight at a wait
+template <class C>
+constexpr int kInflight = (C::A_LOADS + C::B_LOADS) * (C::NST - 2);
+
+// acc = A * B^T over k in [k_begin, k_end) (multiples of 64) for one tile.
 // Operands come from buffers (ra, rb) through a 32-bit byte offset per thread
 // and row (the k = 0 element of the row); offsets at or beyond the buffer
 // size (kInvalidRow) read as zeros, so padding rows cost no branches. With
 // a_kmod != 0 the A column is k mod a_kmod (router: the same activations meet
-// the three weight terms). Padding rows are multiplied as zeros.
-//
-// Tiles go from global memory straight into a ring of NST LDS stages,
-// NST - 1 k-steps ahead, with one barrier per step: no registers hold tiles in
-// flight and no LDS store instructions are issued. Lane (row r, 16-byte
-// position ch) fetches logical chunk ch ^ swizzle(r), so the LDS image is the
-// swizzled layout lds_off describes. Within a step, the LDS fragments of the
-// next 16-wide sub-step are read while the current one multiplies.
+// the three weight terms). Loads run NST - 1 k-steps ahead through the ring,
+// one barrier per step.
 template <class C, bool SWIGLU>
 __device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
                                           const uint32_t (&aoff)[C::A_LOADS], i32x4_t rb,
@@ -89,68 +170,22 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int ch = tid & 7, r0 = tid >> 3;
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+  zero_acc<C>(acc);
   uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
 #pragma unroll
-  for (int p = 0; p < C::A_LOADS; ++p)
-    ao[p] = aoff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+  for (int p = 0; p < C::A_LOADS; ++p) ao[p] = aoff[p];
 #pragma unroll
-  for (int p = 0; p < C::B_LOADS; ++p)
-    bo[p] = boff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+  for (int p = 0; p < C::B_LOADS; ++p) bo[p] = boff[p];
+  swizzle_rows<C>(ao);
+  swizzle_rows<C>(bo);
   const uint32_t lds0 = lds_addr(lds);
-  // this wave's 8 rows of each load pass start at row 8 * wave
   auto issue = [&](int st, int k0) {
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
     const uint32_t ka = a_kmod ? static_cast<uint32_t>(k0 % a_kmod) * 2u : kb;
-    const uint32_t a_base =
-        __builtin_amdgcn_readfirstlane(lds0 + (st * C::STAGE + wave * 8 * BK) * 2);
-    const uint32_t b_base = a_base + C::BM * BK * 2;
-#pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + ka, a_base + p * C::RPP * BK * 2);
-#pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + kb, b_base + p * C::RPP * BK * 2);
+    stage_issue<C>(lds0, st, wave, ra, ao, ka, rb, bo, kb);
   };
-  auto compute = [&](int st) {
-    const uint16_t* As = lds + st * C::STAGE;
-    const uint16_t* Bs = As + C::BM * BK;
-    bf16x8_t af[2][C::MI], bfr[2][C::NJ];
-    auto fetch = [&](int kk, int buf) {
-      const int chk = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
-        bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
-            Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
-        af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
-            As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
-    };
-    fetch(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
-      // the reads above go out before this sub-step's MFMAs (the scheduler
-      // would otherwise reuse their registers and serialize read and multiply)
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) {
-#pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bfr[kk & 1][nj],
-                                                                acc[mi][nj], 0, 0, 0);
-      }
-    }
-  };
-
   constexpr int NST = C::NST;
-  // loads of the NST - 2 newest steps that may stay in flight at a wait
-  constexpr int INFLIGHT = (C::A_LOADS + C::B_LOADS) * (NST - 2);
+  constexpr int INFLIGHT = kInflight<C>;
   static_assert(INFLIGHT <= 63, "vmcnt range");
   const int nk = (k_end - k_begin + BK - 1) / BK;
   if (nk <= 0) return;
@@ -158,24 +193,158 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
   auto kpos = [&](int k) { return k_begin + (k < nk ? k : nk - 1) * BK; };
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j) issue(j, kpos(j));
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");  // stage 0 has landed
+  vm_wait<INFLIGHT>();  // stage 0 has landed
   __syncthreads();
   int st = 0, st_issue = NST - 1;
   for (int k = 0; k < nk; ++k) {
     issue(st_issue, kpos(k + NST - 1));  // the stage read in step k - 1
-    compute(st);
+    stage_mma<C, SWIGLU, false>(lds, st, wm, wn, lane, acc);
     // this wave's part of stage k+1 has landed (later steps' loads may be in
     // flight); the barrier makes every wave's part visible and frees stage k
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");
+    vm_wait<INFLIGHT>();
     __syncthreads();
     st = st == NST - 1 ? 0 : st + 1;
     st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
   }
   // the loads of the clamped last steps land before the LDS is reused
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait<0>();
   __syncthreads();
 }
 
+// Operands of one tile's k-stream: buffer resources, per-thread row byte
+// offsets (swizzle folded in) and the number of 64-wide k-steps.
+template <class C>
+struct StreamOps {
+  i32x4_t ra, rb;
+  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
+  int nk;
+};
+
+// The persistent grouped GEMMs run every tile of a workgroup (tiles first,
+// first + nb, ... below total) as one k-stream through the NST-stage ring:
+// the first steps of a tile are loaded during the previous tile's last
+// steps, so the ring never drains at a tile boundary, and a tile's epilogue
+// (stores straight from registers, no LDS) runs while the next tile's first
+// stages land.
+//   next_ops(tile, index, ops): operands of the index-th tile of the issue
+//     side (called once per tile, in order, after the previous tile's last
+//     step was issued);
+//   nk_of(tile): k-steps of a tile;
+//   epilogue(tile, acc): stores a finished tile (acc in the SWAP layout).
+// Vector-memory waits count only this stream's loads: every step issues the
+// same loads (once the tiles run out, the last step is loaded again into
+// stages nobody reads), so with loads NST - 1 steps ahead at most the newest
+// kInflight<C> may be in flight when a stage is read; extra loads or stores
+// issued in between only make such a wait stronger.
+// Within a step, the fragments of sub-step kk + 1 are read while sub-step kk
+// multiplies; the step's barrier sits before its last sub-step, whose
+// fragments are already in registers, so that the next stage's first
+// fragments are read while those MFMAs run.
+template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue>
+__device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
+                                            NextOps&& next_ops, NkOf&& nk_of,
+                                            Epilogue&& epilogue) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  constexpr int NST = C::NST;
+  constexpr int INFLIGHT = kInflight<C>;
+  static_assert(INFLIGHT <= 63, "vmcnt range");
+  static_assert(BK / 16 == 4, "four MFMA sub-steps per k-step");
+  const uint32_t lds0 = lds_addr(lds);
+
+  // issue side
+  StreamOps<C> op;
+  int ti = first, ki = 0, index = 0;
+  bool more = true;
+  next_ops(ti, index, op);
+  auto issue = [&](int st) {
+    const uint32_t kb = static_cast<uint32_t>(ki) * (BK * 2);
+    stage_issue<C>(lds0, st, wave, op.ra, op.ao, kb, op.rb, op.bo, kb);
+    if (more) ++ki;
+  };
+  auto advance = [&]() {
+    if (!more || ki < op.nk) return;
+    ki = 0;
+    ti += nb;
+    if (ti < total) {
+      next_ops(ti, ++index, op);
+    } else {
+      more = false;
+      ki = op.nk - 1;
+    }
+  };
+
+  // fragments of sub-step kk of stage st
+  bf16x8_t af[2][C::MI], bfr[2][C::NJ];
+  auto fetch = [&](int st, int kk, int buf) {
+    const uint16_t* As = lds + st * C::STAGE;
+    const uint16_t* Bs = As + C::BM * BK;
+    const int chk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj)
+      bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
+          Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
+          As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
+  };
+  f32x16_t acc[C::MI][C::NJ];
+  // the weight fragment goes first: acc holds the transposed tile
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][nj], af[buf][mi],
+                                                              acc[mi][nj], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) {
+    issue(j);
+    advance();
+  }
+  vm_wait<INFLIGHT>();  // stage 0 has landed
+  lds_barrier();
+
+  // compute side
+  int st = 0, st_issue = NST - 1;
+  fetch(st, 0, 0);
+  for (int tc = first; tc < total; tc += nb) {
+    zero_acc<C>(acc);
+    const int nkc = nk_of(tc);
+    for (int kc = 0; kc < nkc; ++kc) {
+      issue(st_issue);  // into the stage read in the previous step
+      fetch(st, 1, 1);
+      // fragment reads go out before the MFMAs that do not need them (the
+      // scheduler would otherwise reuse their registers and serialize)
+      __builtin_amdgcn_sched_barrier(0);
+      mma(0);
+      advance();
+      fetch(st, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(1);
+      fetch(st, 3, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(0);
+      // this wave's part of the next stage has landed; the barrier makes
+      // every wave's part visible and frees the stage whose last fragments
+      // are now in registers
+      vm_wait<INFLIGHT>();
+      lds_barrier();
+      st = st == NST - 1 ? 0 : st + 1;
+      st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
+      fetch(st, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(1);
+    }
+    epilogue(tc, acc);
+  }
+  // the reloads past the last step land before the workgroup ends
+  vm_wait<0>();
+}
 
 // Row (within the tile) of accumulator element r of a 32x32 sub-tile, for
 // this lane; the lane's column is lane % 32.
@@ -183,150 +352,200 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// H = silu(A W1^T) * (A W3^T) per group.
+// Four bf16 values as one 8-byte word.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+// H = silu(A W1^T) * (A W3^T) per group. Routed rows of A are gathered
+// through perm: the token indices of a tile are brought into an LDS slot by
+// the same asynchronous loads as the operands, one tile ahead, so that the
+// tile loop issues no compiler-visible global loads.
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  __shared__ int gtab[kMaxGroups + 1];
+  __shared__ GroupTables gt;
+  constexpr int PS = C::BM > 64 ? C::BM : 64;  // one dma4 per 64 rows
+  __shared__ __attribute__((aligned(16))) int pslot[2][PS];
   constexpr int HALF = C::BN / 2;
-  static_assert(C::BM * (HALF + 8) <= C::LDS_ELEMS, "the H tile fits in the LDS stages");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  load_group_table(gtab, a.tiles1, a.E);
-  const int total = gtab[a.E + 1];
+  load_group_tables(gt, a.tiles1, a.offsets, a.E);
+  const int total = gt.total;
   const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
-  const i32x4_t rx = a.perm ? rsrc4(a.x, static_cast<uint32_t>(a.T) * row_bytes)
-                            : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * row_bytes);
   const i32x4_t rxs = rsrc4(a.x, static_cast<uint32_t>(a.T) * row_bytes);
+  const i32x4_t rx = a.perm ? rxs : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * row_bytes);
+  const i32x4_t rperm = rsrc4(a.perm, static_cast<uint32_t>(a.TK) * 4u);
+  const int nk = a.d / BK;
   uint16_t* H = static_cast<uint16_t*>(a.H);
-  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
-    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
-    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
-    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
-    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
-    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
-    const bool shared = tc.g == a.E;
-    const int Ig = shared ? a.Is : a.I;
-    const int rows_left = tc.rows - tc.m * C::BM;
-    uint32_t aoff[C::A_LOADS];
+
+  // token indices of a routed tile's rows into slot s (rows past the group
+  // are masked where they are used)
+  auto fetch_perm = [&](int tile, int s) {
+    if (!a.perm || wave * 64 >= C::BM) return;
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    if (c.shared) return;
+    const int j = wave * 64 + lane;
+    const uint32_t off =
+        j < C::BM ? static_cast<uint32_t>(c.rbase + c.m * C::BM + j) * 4u : kInvalidRow;
+    dma4(rperm, off, __builtin_amdgcn_readfirstlane(lds_addr(&pslot[s][wave * 64])));
+  };
+  // the first tile's indices, and the second's one tile ahead
+  fetch_perm(first, 0);
+  if (first + nb < total) fetch_perm(first + nb, 1);
+  vm_wait<0>();
+  lds_barrier();
+
+  auto next_ops = [&](int tile, int index, StreamOps<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int* slot = pslot[index & 1];
+    if (index > 0) {
+      // slot index & 1 was filled while tile index - 1 was issued, nk steps
+      // ago: landed once NST - 2 further steps of loads were issued after it
+      if (nk < C::NST - 1) {
+        vm_wait<0>();
+        lds_barrier();
+      }
+      if (tile + nb < total) fetch_perm(tile + nb, (index + 1) & 1);
+    }
+    const int Ig = c.shared ? a.Is : a.I;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
-      const int r = tc.m * C::BM + r0 + p * C::RPP;
+      const int r = c.m * C::BM + r0 + p * C::RPP;
       uint32_t off = kInvalidRow;
-      if (r < tc.rows) {
-        if (shared) {
+      if (r < c.rows) {
+        if (c.shared) {
           off = static_cast<uint32_t>(r) * row_bytes;
         } else if (a.perm) {
-          const int tok = a.perm[tc.rbase + r];
+          const int tok = slot[r0 + p * C::RPP];
           if (tok >= 0 && tok < a.T) off = static_cast<uint32_t>(tok) * row_bytes;
         } else {
-          off = static_cast<uint32_t>(tc.rbase + r) * row_bytes;
+          off = static_cast<uint32_t>(c.rbase + r) * row_bytes;
         }
       }
-      aoff[p] = off;
+      op.ao[p] = off;
     }
-    const uint16_t* W = shared ? static_cast<const uint16_t*>(a.ws13)
-                               : static_cast<const uint16_t*>(a.w13) +
-                                     static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
-    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(2 * Ig) * row_bytes);
-    uint32_t boff[C::B_LOADS];
+    op.ra = c.shared ? rxs : rx;
+    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws13)
+                                 : static_cast<const uint16_t*>(a.w13) +
+                                       static_cast<int64_t>(c.g) * 2 * a.I * a.d;
+    op.rb = rsrc4(W, static_cast<uint32_t>(2 * Ig) * row_bytes);
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
       const bool up = lr >= HALF;
-      const int col = tc.n * HALF + (up ? lr - HALF : lr);
-      boff[p] = col < Ig ? static_cast<uint32_t>(up ? Ig + col : col) * row_bytes : kInvalidRow;
+      const int col = c.n * HALF + (up ? lr - HALF : lr);
+      op.bo[p] = col < Ig ? static_cast<uint32_t>(up ? Ig + col : col) * row_bytes : kInvalidRow;
     }
-    f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, true>(lds, shared ? rxs : rx, aoff, rw, boff, 0, a.d, 0, acc);
-
-    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
+    swizzle_rows<C>(op.ao);
+    swizzle_rows<C>(op.bo);
+    op.nk = nk;
+  };
+  auto nk_of = [&](int) { return nk; };
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int rows_left = c.rows - c.m * C::BM;
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int row = wm * C::WM + mi * 32 + (lane & 31);
+      if (row >= rows_left) continue;
+      uint16_t* hp = H + (hrow0 + row) * a.ldh;
 #pragma unroll
-      for (int nj = 0; nj < C::NJ / 2; ++nj) {
-        const int col = wn * (C::WN / 2) + nj * 32 + (lane & 31);
+      for (int nj = 0; nj < C::NJ / 2; ++nj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float h = silu_f32(acc[mi][nj][r]) * acc[mi][nj + C::NJ / 2][r];
-          out_put<C, HALF>(lds, wm * C::WM + mi * 32 + acc_row(lane, r), col, h);
+        for (int g = 0; g < 4; ++g) {
+          const int col = c.n * HALF + wn * (C::WN / 2) + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (col >= Ig) continue;
+          const f32x16_t& gv = acc[mi][nj];
+          const f32x16_t& uv = acc[mi][nj + C::NJ / 2];
+          *reinterpret_cast<uint2*>(hp + col) =
+              pack_bf16x4(silu_f32(gv[4 * g]) * uv[4 * g], silu_f32(gv[4 * g + 1]) * uv[4 * g + 1],
+                          silu_f32(gv[4 * g + 2]) * uv[4 * g + 2],
+                          silu_f32(gv[4 * g + 3]) * uv[4 * g + 3]);
         }
-      }
-    __syncthreads();
-    out_flush<C, HALF>(lds, H + hrow0 * a.ldh + tc.n * HALF, a.ldh, rows_left,
-                       Ig - tc.n * HALF);
-    __syncthreads();
-  }
+    }
+  };
+  gemm_stream<C, true>(lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 // y = H W2^T per group: routed rows to y_perm, shared rows to y_shared.
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  __shared__ int gtab[kMaxGroups + 1];
-  static_assert(C::BM * (C::BN + 8) <= C::LDS_ELEMS, "the output tile fits in the LDS stages");
+  __shared__ GroupTables gt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  load_group_table(gtab, a.tiles2, a.E);
-  const int total = gtab[a.E + 1];
+  load_group_tables(gt, a.tiles2, a.offsets, a.E);
+  const int total = gt.total;
   const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
   const uint32_t hrow_bytes = static_cast<uint32_t>(a.ldh) * 2u;
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
   const i32x4_t rh = rsrc4(a.H, static_cast<uint32_t>(hrows) * hrow_bytes);
-  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
-    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
-    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
-    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
-    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
-    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
-    const bool shared = tc.g == a.E;
-    const int Ig = shared ? a.Is : a.I;
-    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
-    const int rows_left = tc.rows - tc.m * C::BM;
-    uint32_t aoff[C::A_LOADS];
+  // the shared group's tiles are the last ones
+  const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
+
+  auto next_ops = [&](int tile, int, StreamOps<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    const int rows_left = c.rows - c.m * C::BM;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      aoff[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * hrow_bytes : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * hrow_bytes : kInvalidRow;
     }
-    const uint16_t* W = shared ? static_cast<const uint16_t*>(a.ws2)
-                               : static_cast<const uint16_t*>(a.w2) +
-                                     static_cast<int64_t>(tc.g) * a.d * a.I;
+    op.ra = rh;
+    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2)
+                                 : static_cast<const uint16_t*>(a.w2) +
+                                       static_cast<int64_t>(c.g) * a.d * a.I;
     const uint32_t wrow_bytes = static_cast<uint32_t>(Ig) * 2u;
-    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(a.d) * wrow_bytes);
-    uint32_t boff[C::B_LOADS];
+    op.rb = rsrc4(W, static_cast<uint32_t>(a.d) * wrow_bytes);
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
-      const int row = tc.n * C::BN + r0 + p * C::RPP;
-      boff[p] = row < a.d ? static_cast<uint32_t>(row) * wrow_bytes : kInvalidRow;
+      const int row = c.n * C::BN + r0 + p * C::RPP;
+      op.bo[p] = row < a.d ? static_cast<uint32_t>(row) * wrow_bytes : kInvalidRow;
     }
-    f32x16_t acc[C::MI][C::NJ];
-    gemm_tile<C, false>(lds, rh, aoff, rw, boff, 0, Ig, 0, acc);
-
-    uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
-                                 static_cast<int64_t>(tc.m) * C::BM * a.d
-                           : static_cast<uint16_t*>(a.yperm) +
-                                 (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
+    swizzle_rows<C>(op.ao);
+    swizzle_rows<C>(op.bo);
+    op.nk = Ig / BK;
+  };
+  auto nk_of = [&](int tile) { return (tile >= shared_first ? a.Is : a.I) / BK; };
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int rows_left = c.rows - c.m * C::BM;
+    uint16_t* out = c.shared ? static_cast<uint16_t*>(a.yshared) +
+                                   static_cast<int64_t>(c.m) * C::BM * a.d
+                             : static_cast<uint16_t*>(a.yperm) +
+                                   (static_cast<int64_t>(c.rbase) + c.m * C::BM) * a.d;
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int row = wm * C::WM + mi * 32 + (lane & 31);
+      if (row >= rows_left) continue;
+      uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) {
-        const int col = wn * C::WN + nj * 32 + (lane & 31);
+      for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          out_put<C, C::BN>(lds, wm * C::WM + mi * 32 + acc_row(lane, r), col, acc[mi][nj][r]);
-      }
-    __syncthreads();
-    out_flush<C, C::BN>(lds, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
-    __syncthreads();
-  }
+        for (int g = 0; g < 4; ++g) {
+          const int col = c.n * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (col >= a.d) continue;
+          const f32x16_t& v = acc[mi][nj];
+          *reinterpret_cast<uint2*>(yp + col) =
+              pack_bf16x4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        }
+    }
+  };
+  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 // Router: partial[s][t][e] = sum over k-split s of x[t, k mod d] * wsplit[e, k],

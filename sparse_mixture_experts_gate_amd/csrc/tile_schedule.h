@@ -45,6 +45,65 @@ __device__ __forceinline__ TileCoord tile_coord(const FfnArgs& a, const int* gta
   return c;
 }
 
+// LDS copy of the tile schedule for kernels whose tile loop must issue no
+// global loads of its own (their vector-memory waits are counted by hand).
+// gnext[i] is the first tile of group i + 1 (i < E) and INT_MAX beyond, so
+// the group of a tile is the number of entries <= tile; off holds the row
+// offsets of the routed groups.
+struct __attribute__((aligned(16))) GroupTables {
+  int gnext[kMaxGroups - 1];
+  int off[kMaxGroups];
+  int total;
+};
+static_assert(kMaxGroups - 1 == 8 * 64, "one wave scans gnext with 8 entries per lane");
+
+__device__ __forceinline__ void load_group_tables(GroupTables& t, const int32_t* tiles,
+                                                  const int32_t* offsets, int E) {
+  for (int i = threadIdx.x; i < kMaxGroups - 1; i += blockDim.x)
+    t.gnext[i] = i < E ? tiles[i + 1] : 0x7fffffff;
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) t.off[i] = offsets[i];
+  if (threadIdx.x == 0) t.total = tiles[E + 1];
+  __syncthreads();
+}
+
+// tile_coord over the LDS tables, wave-uniform: every lane compares eight
+// entries of gnext with the tile and the ballots count them, two LDS reads
+// deep instead of a binary search's nine.
+__device__ __forceinline__ TileCoord tile_coord_lds(const GroupTables& t, int E, int64_t T,
+                                                    int tile, int bm) {
+  const int lane = threadIdx.x & 63;
+  const int4 v0 = *reinterpret_cast<const int4*>(t.gnext + 8 * lane);
+  const int4 v1 = *reinterpret_cast<const int4*>(t.gnext + 8 * lane + 4);
+  const int g = __popcll(__ballot(v0.x <= tile)) + __popcll(__ballot(v0.y <= tile)) +
+                __popcll(__ballot(v0.z <= tile)) + __popcll(__ballot(v0.w <= tile)) +
+                __popcll(__ballot(v1.x <= tile)) + __popcll(__ballot(v1.y <= tile)) +
+                __popcll(__ballot(v1.z <= tile)) + __popcll(__ballot(v1.w <= tile));
+  TileCoord c;
+  c.g = g;
+  c.shared = g == E;
+  const int start = __builtin_amdgcn_readfirstlane(g == 0 ? 0 : t.gnext[g - 1]);
+  c.rbase = c.shared ? 0 : __builtin_amdgcn_readfirstlane(t.off[g]);
+  c.rows = c.shared ? static_cast<int>(T)
+                    : __builtin_amdgcn_readfirstlane(t.off[g + 1]) - c.rbase;
+  const int mt = (c.rows + bm - 1) / bm;
+  const int local = tile - start;
+  c.n = local / mt;
+  c.m = local - c.n * mt;
+  return c;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads: LDS accesses
+// have completed, vector memory operations (loads into LDS, stores) may still
+// be in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // Buffer resources: operands are read with raw buffer loads through a 32-bit
 // byte offset; offsets at or beyond the resource size read as zeros in
 // hardware, which is how padding rows are handled without branches.
