@@ -24,6 +24,10 @@ COMMON = [
 ]
 # routing and quantization decide integers from fp32 values: no contraction
 NO_CONTRACT = {"router.hip", "elementwise.hip"}
+# MFMA results in VGPRs: the FP8 kernels scale every product on the VALU, and
+# with the product in AGPRs the compiler reused one AGPR quad per product,
+# which serialized the MFMAs of the decode tiles behind the copies out
+MFMA_VGPR = {"gemm_fp8.hip"}
 SOURCES = ["dsmoe_api.cpp", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip",
            "gemm_fp8.hip", "elementwise.hip"]
 
@@ -33,6 +37,8 @@ def _compile(src: str) -> str:
     cmd = [HIPCC, *COMMON]
     if src in NO_CONTRACT:
         cmd.append("-ffp-contract=off")
+    if src in MFMA_VGPR:
+        cmd += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

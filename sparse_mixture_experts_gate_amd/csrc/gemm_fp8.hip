@@ -140,56 +140,49 @@ __device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa, float* l
     const float s_lo = lds_sb[(st * C::NWAVES + wave) * 2];
     const float s_hi = SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
     const int kg = lane >> 4;
+    // the weight fragment goes first: lane l then owns row l % 16 of each
+    // 16-row group and four adjacent columns, so one row scale x block scale
+    // product serves all four values of a product
+    float sl[C::MI], sh[C::MI];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 16 + (lane & 15)];
+      sl[mi] = sa * s_lo;
+      sh[mi] = sa * s_hi;
+    }
     i32x8_t bfr[C::NJ];
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
     auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
-    // row scale x block scale for the lane's 4 rows of 16-row group m
-    auto row_scales = [&](int m, f32x4_t& s_l, f32x4_t& s_h) {
-      const f32x4_t sa =
-          *reinterpret_cast<const f32x4_t*>(lds_sa + st * C::NT + wm * C::WM + m * 16 + 4 * kg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s_l[r] = sa[r] * s_lo;
-        s_h[r] = sa[r] * s_hi;
-      }
-    };
     // Software pipeline over the MI x NJ products of the k block: MFMA t runs
     // in the matrix core while the VALU folds product t-1 into its
-    // accumulator with the scales (4 FMAs, shorter than one MFMA).
+    // accumulator with its scale (4 FMAs, shorter than one MFMA).
     constexpr int NP = C::MI * C::NJ;
     f32x4_t p[2];
     i32x8_t af[2];
-    f32x4_t sl[2], sh[2];
     af[0] = a_frag(0);
-    row_scales(0, sl[0], sh[0]);
 #pragma unroll
     for (int t = 0; t < NP; ++t) {
       const int mi = t / C::NJ, nj = t % C::NJ;
-      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi & 1], bfr[nj], zero, 0, 0,
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nj], af[mi & 1], zero, 0, 0,
                                                                   0, 127, 0, 127);
       if (nj == 0 && mi + 1 < C::MI) af[(mi + 1) & 1] = a_frag(mi + 1);
       __builtin_amdgcn_sched_barrier(0);
       if (t > 0) {
         const int pm = (t - 1) / C::NJ, pn = (t - 1) % C::NJ;
-        const bool lo = !SWIGLU || pn < C::NJ / 2;
+        const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], lo ? sl[pm & 1][r] : sh[pm & 1][r],
-                                          acc[pm][pn][r]);
+          acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], s, acc[pm][pn][r]);
       }
-      // group mi+1's scales go to the slot of group mi-1, whose last product
-      // was folded in just above
-      if (nj == 0 && mi + 1 < C::MI) row_scales(mi + 1, sl[(mi + 1) & 1], sh[(mi + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     {
       constexpr int pm = C::MI - 1, pn = C::NJ - 1;
-      constexpr bool lo = !SWIGLU || pn < C::NJ / 2;
+      const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], lo ? sl[pm & 1][r] : sh[pm & 1][r],
-                                        acc[pm][pn][r]);
+        acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], s, acc[pm][pn][r]);
     }
   };
 
@@ -303,62 +296,47 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
     gemm8_tile<C, true>(lds, lds_sa, lds_sb, shared ? rxs : rx, aoff, shared ? rsx : rsxp, sa_off,
                         rw, boff, rws, sb_gate, sb_up, a.d, acc);
 
-    // SwiGLU, then the row max-abs over the 128 columns (across the wave's
-    // 16-lane groups and the tile's WAVES_N waves)
+    // SwiGLU, then the row max-abs over the 128 columns: lane l holds row
+    // l % 16 of each 16-row group and four adjacent columns per product, so
+    // the max runs over the lane's values, the four lanes of the row, and the
+    // tile's WAVES_N waves
     constexpr int NJH = C::NJ / 2;
     float h[C::MI][NJH][4];
-    float pm[C::MI][4];
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      float m = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = 0.0f;
+      for (int nj = 0; nj < NJH; ++nj)
 #pragma unroll
-        for (int nj = 0; nj < NJH; ++nj) {
+        for (int r = 0; r < 4; ++r) {
           h[mi][nj][r] = silu_f32(acc[mi][nj][r]) * acc[mi][nj + NJH][r];
           m = fmaxf(m, fabsf(h[mi][nj][r]));
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        pm[mi][r] = m;
-      }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wn][wm * C::WM + mi * 16 + 4 * (lane >> 4) + r] = pm[mi][r];
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (lane < 16) red[wn][wm * C::WM + mi * 16 + lane] = m;
     }
     __syncthreads();
     const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
     const int rows_left = tc.rows - tc.m * C::BM;
-    // E4M3 codes of the 128 x 128 H tile are staged in LDS (rows padded by 16
-    // bytes), then leave as 16-byte stores
-    constexpr int HSTR = HALF + 16;
-    static_assert(C::BM * HSTR <= 2 * C::STAGE, "the H tile fits in the LDS stages");
+    // E4M3 codes leave straight from registers, four columns per 4-byte store
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int lr = wm * C::WM + mi * 16 + (lane & 15);
+      float amax = red[0][lr];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lr = wm * C::WM + mi * 16 + 4 * (lane >> 4) + r;
-        float amax = red[0][lr];
+      for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
+      if (lr >= rows_left) continue;
+      const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
+      uint8_t* hp = H + (hrow0 + lr) * a.ldh + tc.n * HALF + wn * (C::WN / 2) + 4 * (lane >> 4);
 #pragma unroll
-        for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
-        const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
-#pragma unroll
-        for (int nj = 0; nj < NJH; ++nj) {
-          const int col = wn * (C::WN / 2) + nj * 16 + (lane & 15);
-          const uint32_t q = amax == 0.0f ? 0u : e4m3_pack4(h[mi][nj][r] * inv, 0.f, 0.f, 0.f);
-          lds[lr * HSTR + col] = static_cast<uint8_t>(q & 0xFFu);
-        }
-        if (wn == 0 && (lane & 15) == 0 && lr < rows_left)
-          a.H_scale[(hrow0 + lr) * hkb + tc.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
-      }
-    __syncthreads();
-    for (int i = tid; i < C::BM * (HALF / 16); i += C::NT) {
-      const int row = i / (HALF / 16), c = (i % (HALF / 16)) * 16;
-      if (row < rows_left)
-        *reinterpret_cast<uint4*>(H + (hrow0 + row) * a.ldh + tc.n * HALF + c) =
-            *reinterpret_cast<const uint4*>(lds + row * HSTR + c);
+      for (int nj = 0; nj < NJH; ++nj)
+        *reinterpret_cast<uint32_t*>(hp + nj * 16) =
+            amax == 0.0f ? 0u
+                         : e4m3_pack4(h[mi][nj][0] * inv, h[mi][nj][1] * inv, h[mi][nj][2] * inv,
+                                      h[mi][nj][3] * inv);
+      if (wn == 0 && lane < 16)
+        a.H_scale[(hrow0 + lr) * hkb + tc.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
     }
     __syncthreads();  // red[] is rewritten by the next tile
   }
@@ -432,19 +410,41 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
                                  static_cast<int64_t>(tc.m) * C::BM * a.d
                            : static_cast<uint16_t*>(a.yperm) +
                                  (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
-    uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
-    static_assert(C::BM * (C::BN + 8) * 2 <= 2 * C::STAGE, "the output tile fits in the LDS stages");
+    if constexpr (C::BM >= 128) {
+      // large tiles: the bf16 tile is staged in LDS and leaves as whole
+      // 16-byte row pieces (3% faster than 8-byte stores from registers)
+      uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
+      static_assert(C::BM * (C::BN + 8) * 2 <= 2 * C::STAGE,
+                    "the output tile fits in the LDS stages");
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+      for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
+        for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out_put<C, C::BN>(ot, wm * C::WM + mi * 16 + 4 * (lane >> 4) + r,
-                            wn * C::WN + nj * 16 + (lane & 15), acc[mi][nj][r]);
-    __syncthreads();
-    out_flush<C, C::BN>(ot, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
-    __syncthreads();
+          for (int r = 0; r < 4; ++r)
+            out_put<C, C::BN>(ot, wm * C::WM + mi * 16 + (lane & 15),
+                              wn * C::WN + nj * 16 + 4 * (lane >> 4) + r, acc[mi][nj][r]);
+      __syncthreads();
+      out_flush<C, C::BN>(ot, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
+      __syncthreads();
+    } else {
+      // decode tiles hold a few valid rows: 8-byte stores straight from
+      // registers, no LDS round trip
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) {
+        const int row = wm * C::WM + mi * 16 + (lane & 15);
+        if (row >= rows_left) continue;
+        uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
+#pragma unroll
+        for (int nj = 0; nj < C::NJ; ++nj) {
+          const int col = tc.n * C::BN + wn * C::WN + nj * 16 + 4 * (lane >> 4);
+          if (col >= a.d) continue;
+          const f32x4_t& v = acc[mi][nj];
+          *reinterpret_cast<uint2*>(yp + col) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+    }
   }
 }
 
