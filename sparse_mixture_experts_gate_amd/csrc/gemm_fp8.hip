@@ -76,226 +76,315 @@ __device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
   return v;
 }
 
-// acc[mi][nj] += sum over 128-wide k blocks kb of
-//   (A_kb B_kb^T) * s_a[row][kb] * s_b[kb]   (s_b: sb_lo for the first half of
-// the wave's column sub-tiles, sb_hi for the second half; equal without SWIGLU).
-// Scales come from buffers too: rsa + sa_off is the byte offset of this
-// thread's row of activation scales (kInvalidRow for threads past BM and for
-// padding rows, which reads zeros); rsb + sb_lo / sb_hi are byte offsets of
-// the weight block scales of the tile's gate (lo) and up (hi) columns.
-//
-// All loads go from global memory straight into a ring of NST LDS stages,
-// NST - 1 k blocks ahead, with one barrier per k block: the code tiles with
-// 16-byte loads (lane (row r, position ch) fetches logical chunk
-// ch ^ swizzle(r), giving the layout lds_off8 describes), the row scales with
-// one 4-byte load per lane into lds_sa[stage][thread], the two block scales
-// with lane-0-only 4-byte loads into the wave's own slot of lds_sb. Every
-// wave issues the same number of loads per k block, so one vmcnt bound holds
-// for all of them.
-template <class C, bool SWIGLU>
-__device__ __forceinline__ void gemm8_tile(uint8_t* lds, float* lds_sa, float* lds_sb, i32x4_t ra,
-                                           const uint32_t (&aoff)[C::A_LOADS], i32x4_t rsa,
-                                           uint32_t sa_off, i32x4_t rb,
-                                           const uint32_t (&boff)[C::B_LOADS], i32x4_t rsb,
-                                           uint32_t sb_lo, uint32_t sb_hi, int K,
-                                           f32x4_t (&acc)[C::MI][C::NJ]) {
+// Operands of one tile's k-stream: buffer resources, per-thread row byte
+// offsets (swizzle folded in), this thread's activation-scale row offset, the
+// weight block-scale offsets of the wave's gate (lo) and up (hi) columns, and
+// the number of 128-wide k blocks.
+template <class C>
+struct StreamOps8 {
+  i32x4_t ra, rsa, rb, rsb;
+  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
+  uint32_t sa_off, sb_lo, sb_hi;
+  int nk;
+};
+
+// Folds the chunk swizzle into the row offsets: lane (row r, 16-byte position
+// ch) fetches logical chunk ch ^ swizzle(r), giving the layout lds_off8 reads.
+template <class C, int N>
+__device__ __forceinline__ void swizzle_rows8(uint32_t (&o)[N]) {
+  const int ch = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+#pragma unroll
+  for (int p = 0; p < N; ++p)
+    o[p] += static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
+}
+
+// Issues k block kb of a tile into ring stage st. All loads go from global
+// memory straight into LDS: the code tiles with 16-byte loads, the row scales
+// with one 4-byte load per lane into lds_sa[stage][thread] (zeros past the
+// tile's rows), the two block scales with lane-0-only 4-byte loads into the
+// wave's own slot of lds_sb. Every wave issues the same number of loads per
+// k block, so one vmcnt bound holds for all of them.
+template <class C>
+__device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32_t sb0, int st,
+                                             int wave, int lane, const StreamOps8<C>& op,
+                                             int kb) {
+  const uint32_t off = static_cast<uint32_t>(kb) * BK8;
+  const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + st * C::STAGE + wave * 8 * BK8);
+  const uint32_t b_base = a_base + C::BM * BK8;
+#pragma unroll
+  for (int p = 0; p < C::A_LOADS; ++p) dma16(op.ra, op.ao[p] + off, a_base + p * C::RPP * BK8);
+#pragma unroll
+  for (int p = 0; p < C::B_LOADS; ++p) dma16(op.rb, op.bo[p] + off, b_base + p * C::RPP * BK8);
+  const uint32_t kb4 = static_cast<uint32_t>(kb) * 4u;
+  dma4(op.rsa, op.sa_off + kb4, __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
+  const uint32_t sb_base =
+      __builtin_amdgcn_readfirstlane(sb0 + ((st * C::NWAVES + wave) * 2) * 4);
+  if (lane == 0) {
+    dma4(op.rsb, op.sb_lo + kb4, sb_base);
+    dma4(op.rsb, op.sb_hi + kb4, sb_base + 4);
+  }
+}
+
+// acc[mi][nj] += (A_kb B_kb^T) * s_a[row][kb] * s_b[kb] for the k block in
+// ring stage st (s_b: the gate block for the first half of the wave's column
+// sub-tiles, the up block for the second; one block without SWIGLU). The
+// weight fragment goes first: lane l then owns row l % 16 of each 16-row
+// group and four adjacent columns, so one row-scale x block-scale product
+// serves all four values of a product. The MI x NJ products are pipelined one
+// MFMA deep: MFMA t runs in the matrix core while the VALU folds product t-1
+// into its accumulator (4 FMAs). mid() runs once every LDS read of the stage
+// has been issued, before the last row group's MFMAs, whose operands are
+// then in registers.
+template <class C, bool SWIGLU, class Mid>
+__device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_sa,
+                                           const float* lds_sb, int st, int wave, int wm, int wn,
+                                           int lane, f32x4_t (&acc)[C::MI][C::NJ], Mid&& mid) {
+  const uint8_t* As = lds + st * C::STAGE;
+  const uint8_t* Bs = As + C::BM * BK8;
+  const float s_lo = lds_sb[(st * C::NWAVES + wave) * 2];
+  const float s_hi = SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
+  const int kg = lane >> 4;
+  float sl[C::MI], sh[C::MI];
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+    const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 16 + (lane & 15)];
+    sl[mi] = sa * s_lo;
+    sh[mi] = sa * s_hi;
+  }
+  i32x8_t bfr[C::NJ];
+#pragma unroll
+  for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
+  auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NP = C::MI * C::NJ;
+  constexpr int TMID = (C::MI - 1) * C::NJ;  // first product of the last row group
+  f32x4_t p[2];
+  i32x8_t af[2];
+  af[0] = a_frag(0);
+#pragma unroll
+  for (int t = 0; t < NP; ++t) {
+    const int mi = t / C::NJ, nj = t % C::NJ;
+    if (t == TMID) {
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nj], af[mi & 1], zero, 0, 0, 0,
+                                                                127, 0, 127);
+    if (nj == 0 && mi + 1 < C::MI) af[(mi + 1) & 1] = a_frag(mi + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t > 0) {
+      const int pm = (t - 1) / C::NJ, pn = (t - 1) % C::NJ;
+      const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], s, acc[pm][pn][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    constexpr int pm = C::MI - 1, pn = C::NJ - 1;
+    const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], s, acc[pm][pn][r]);
+  }
+}
+
+// The persistent FP8 GEMMs run every tile of a workgroup (tiles first,
+// first + nb, ... below total) as one k-stream through the NST-stage ring:
+// the first k blocks of a tile are loaded during the previous tile's last
+// ones, so the ring never drains at a tile boundary.
+//   next_ops(tile, index, ops): operands of the index-th tile of the issue
+//     side (called once per tile, in order, after the previous tile's last
+//     k block was issued);
+//   nk_of(tile): k blocks of a tile;
+//   epilogue(tile, acc): stores a finished tile.
+// Vector-memory waits count only this stream's loads: every k block issues
+// the same loads (once the tiles run out, the last block is loaded again into
+// stages nobody reads), so with loads NST - 1 blocks ahead at most the newest
+// NL * (NST - 2) may be in flight when a stage is read; extra loads or stores
+// in between only make such a wait stronger.
+template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue>
+__device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float* lds_sb, int first,
+                                             int nb, int total, NextOps&& next_ops, NkOf&& nk_of,
+                                             Epilogue&& epilogue) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int ch = tid & 7, r0 = tid >> 3;
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
-#pragma unroll
-  for (int p = 0; p < C::A_LOADS; ++p)
-    ao[p] = aoff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
-#pragma unroll
-  for (int p = 0; p < C::B_LOADS; ++p)
-    bo[p] = boff[p] + static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
-  const uint32_t lds0 = lds_addr(lds), sa0 = lds_addr(lds_sa), sb0 = lds_addr(lds_sb);
-  auto issue = [&](int st, int kb) {
-    const uint32_t off = static_cast<uint32_t>(kb) * BK8;
-    const uint32_t a_base = __builtin_amdgcn_readfirstlane(lds0 + st * C::STAGE + wave * 8 * BK8);
-    const uint32_t b_base = a_base + C::BM * BK8;
-#pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + off, a_base + p * C::RPP * BK8);
-#pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + off, b_base + p * C::RPP * BK8);
-    const uint32_t kb4 = static_cast<uint32_t>(kb) * 4u;
-    dma4(rsa, sa_off + kb4,
-         __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
-    const uint32_t sb_base =
-        __builtin_amdgcn_readfirstlane(sb0 + ((st * C::NWAVES + wave) * 2) * 4);
-    if (lane == 0) {
-      dma4(rsb, sb_lo + kb4, sb_base);
-      dma4(rsb, sb_hi + kb4, sb_base + 4);
-    }
-  };
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int st) {
-    const uint8_t* As = lds + st * C::STAGE;
-    const uint8_t* Bs = As + C::BM * BK8;
-    const float s_lo = lds_sb[(st * C::NWAVES + wave) * 2];
-    const float s_hi = SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
-    const int kg = lane >> 4;
-    // the weight fragment goes first: lane l then owns row l % 16 of each
-    // 16-row group and four adjacent columns, so one row scale x block scale
-    // product serves all four values of a product
-    float sl[C::MI], sh[C::MI];
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 16 + (lane & 15)];
-      sl[mi] = sa * s_lo;
-      sh[mi] = sa * s_hi;
-    }
-    i32x8_t bfr[C::NJ];
-#pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
-    auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
-    // Software pipeline over the MI x NJ products of the k block: MFMA t runs
-    // in the matrix core while the VALU folds product t-1 into its
-    // accumulator with its scale (4 FMAs, shorter than one MFMA).
-    constexpr int NP = C::MI * C::NJ;
-    f32x4_t p[2];
-    i32x8_t af[2];
-    af[0] = a_frag(0);
-#pragma unroll
-    for (int t = 0; t < NP; ++t) {
-      const int mi = t / C::NJ, nj = t % C::NJ;
-      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nj], af[mi & 1], zero, 0, 0,
-                                                                  0, 127, 0, 127);
-      if (nj == 0 && mi + 1 < C::MI) af[(mi + 1) & 1] = a_frag(mi + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t > 0) {
-        const int pm = (t - 1) / C::NJ, pn = (t - 1) % C::NJ;
-        const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], s, acc[pm][pn][r]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    {
-      constexpr int pm = C::MI - 1, pn = C::NJ - 1;
-      const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], s, acc[pm][pn][r]);
-    }
-  };
-
   constexpr int NST = C::NST;
-  constexpr int INFLIGHT = C::NL * (NST - 2);  // loads of the NST - 2 newest k blocks
-  const int nk = K / BK8;
-  if (nk <= 0) return;
-  // k blocks past the end reload the last one (in bounds, never read)
-  auto kpos = [&](int k) { return k < nk ? k : nk - 1; };
+  constexpr int INFLIGHT = C::NL * (NST - 2);
+  const uint32_t lds0 = lds_addr(lds), sa0 = lds_addr(lds_sa), sb0 = lds_addr(lds_sb);
+
+  // issue side
+  StreamOps8<C> op;
+  int ti = first, ki = 0, index = 0;
+  bool more = true;
+  next_ops(ti, index, op);
+  auto issue = [&](int st) {
+    stage8_issue<C>(lds0, sa0, sb0, st, wave, lane, op, ki);
+    if (more) ++ki;
+  };
+  auto advance = [&]() {
+    if (!more || ki < op.nk) return;
+    ki = 0;
+    ti += nb;
+    if (ti < total) {
+      next_ops(ti, ++index, op);
+    } else {
+      more = false;
+      ki = op.nk - 1;
+    }
+  };
 #pragma unroll
-  for (int j = 0; j < NST - 1; ++j) issue(j, kpos(j));
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");  // stage 0 has landed
-  __syncthreads();
-  int st = 0, st_issue = NST - 1;
-  for (int k = 0; k < nk; ++k) {
-    issue(st_issue, kpos(k + NST - 1));  // the stage read in block k - 1
-    compute(st);
-    // this wave's part of stage k+1 has landed; the barrier makes every
-    // wave's part visible and frees stage k
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(INFLIGHT) : "memory");
-    __syncthreads();
-    st = st == NST - 1 ? 0 : st + 1;
-    st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
+  for (int j = 0; j < NST - 1; ++j) {
+    issue(j);
+    advance();
   }
-  // the loads of the clamped last blocks land before the LDS is reused
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  vm_wait<INFLIGHT>();  // stage 0 has landed
+  lds_barrier();
+
+  // compute side
+  int st = 0, st_issue = NST - 1;
+  // this wave's part of the next stage has landed; the barrier makes every
+  // wave's part visible and frees the stage being read
+  auto mid = [&]() {
+    vm_wait<INFLIGHT>();
+    lds_barrier();
+  };
+  for (int tc = first; tc < total; tc += nb) {
+    f32x4_t acc[C::MI][C::NJ];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nkc = nk_of(tc);
+    for (int kc = 0; kc < nkc; ++kc) {
+      issue(st_issue);  // into the stage read in the previous k block
+      advance();
+      stage8_mma<C, SWIGLU>(lds, lds_sa, lds_sb, st, wave, wm, wn, lane, acc, mid);
+      st = st == NST - 1 ? 0 : st + 1;
+      st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
+    }
+    epilogue(tc, acc);
+  }
+  // the reloads past the last block land before the workgroup ends
+  vm_wait<0>();
 }
 
-// H (E4M3 + 1x128 scales) = quant(silu(A W1^T) * (A W3^T)); tile = 128 H columns.
+// H (E4M3 + 1x128 scales) = quant(silu(A W1^T) * (A W3^T)); tile = 128 H
+// columns. Routed rows of A are gathered through perm: the token indices of a
+// tile's rows come into an LDS slot by the same asynchronous loads as the
+// operands, one tile ahead, so that the tile loop issues no compiler-visible
+// global loads.
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float lds_sa[C::NST * C::NT];
   __shared__ __attribute__((aligned(16))) float lds_sb[C::NST * C::NWAVES * 2];
   __shared__ float red[C::WAVES_N][C::BM];
-  __shared__ int gtab[kMaxGroups + 1];
+  __shared__ GroupTables gt;
+  constexpr int PS = C::BM > 64 ? C::BM : 64;  // one dma4 per 64 rows
+  __shared__ __attribute__((aligned(16))) int pslot[2][PS];
   constexpr int HALF = C::BN / 2;  // 128 H columns
   static_assert(HALF == 128, "one 1x128 quantization tile of H per tile");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  load_group_table(gtab, a.tiles1, a.E);
-  const int total = gtab[a.E + 1];
+  load_group_tables(gt, a.tiles1, a.offsets, a.E);
+  const int total = gt.total;
   const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
   const int dkb = a.d / 128;
   const int hkb = a.ldh / 128;
   const float* XS = a.perm ? a.x_scale : a.xperm_scale;
+  const i32x4_t rxs = rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
   const i32x4_t rx =
-      a.perm ? rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d))
-             : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
-  const i32x4_t rxs =
-      rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
+      a.perm ? rxs : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
   // activation scales: gathered rows (or x_perm rows) and the shared rows
   const i32x4_t rsxp =
       rsrc4(XS, static_cast<uint32_t>(a.perm ? a.T : a.TK) * static_cast<uint32_t>(dkb) * 4u);
   const i32x4_t rsx =
       rsrc4(a.x_scale, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(dkb) * 4u);
+  const i32x4_t rperm = rsrc4(a.perm, static_cast<uint32_t>(a.TK) * 4u);
+  const int nk = a.d / BK8;
   uint8_t* H = static_cast<uint8_t*>(a.H);
-  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.I, a.Is, HALF);
-    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
-    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
-    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
-    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
-    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
-    const bool shared = tc.g == a.E;
-    const int Ig = shared ? a.Is : a.I;
-    // A rows: gathered token rows of the quantized x (or rows of x_perm); the
-    // shared expert reads x's rows in order
-    auto src_row = [&](int r) -> int64_t {
-      if (r >= tc.rows) return -1;
-      if (shared) return r;
+
+  // token indices of a routed tile's rows into slot s (rows past the group
+  // are masked where they are used)
+  auto fetch_perm = [&](int tile, int s) {
+    if (!a.perm || wave * 64 >= C::BM) return;
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    if (c.shared) return;
+    const int j = wave * 64 + lane;
+    const uint32_t off =
+        j < C::BM ? static_cast<uint32_t>(c.rbase + c.m * C::BM + j) * 4u : kInvalidRow;
+    dma4(rperm, off, __builtin_amdgcn_readfirstlane(lds_addr(&pslot[s][wave * 64])));
+  };
+  fetch_perm(first, 0);
+  if (first + nb < total) fetch_perm(first + nb, 1);
+  vm_wait<0>();
+  lds_barrier();
+
+  auto next_ops = [&](int tile, int index, StreamOps8<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int* slot = pslot[index & 1];
+    if (index > 0) {
+      // slot index & 1 was filled while tile index - 1 was issued, nk blocks
+      // ago: landed once NST - 2 further blocks of loads were issued after it
+      if (nk < C::NST - 1) {
+        vm_wait<0>();
+        lds_barrier();
+      }
+      if (tile + nb < total) fetch_perm(tile + nb, (index + 1) & 1);
+    }
+    const int Ig = c.shared ? a.Is : a.I;
+    // source row (token) of tile row r, or -1
+    auto src_row = [&](int r) -> int {
+      const int gr = c.m * C::BM + r;
+      if (gr >= c.rows) return -1;
+      if (c.shared) return gr;
       if (a.perm) {
-        const int tok = a.perm[tc.rbase + r];
+        const int tok = slot[r];
         return (tok >= 0 && tok < a.T) ? tok : -1;
       }
-      return tc.rbase + r;
+      return c.rbase + gr;
     };
-    uint32_t aoff[C::A_LOADS];
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
-      const int64_t row = src_row(tc.m * C::BM + r0 + p * C::RPP);
-      aoff[p] = row >= 0 ? static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) : kInvalidRow;
+      const int row = src_row(r0 + p * C::RPP);
+      op.ao[p] = row >= 0 ? static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) : kInvalidRow;
     }
-    uint32_t sa_off = kInvalidRow;
+    op.sa_off = kInvalidRow;
     if (tid < C::BM) {
-      const int64_t row = src_row(tc.m * C::BM + tid);
-      if (row >= 0) sa_off = static_cast<uint32_t>(row * dkb) * 4u;
+      const int row = src_row(tid);
+      if (row >= 0) op.sa_off = static_cast<uint32_t>(row * dkb) * 4u;
     }
-    const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws13)
-                              : static_cast<const uint8_t*>(a.w13) +
-                                    static_cast<int64_t>(tc.g) * 2 * a.I * a.d;
-    const float* WS = shared ? a.ws13_scale
-                             : a.w13_scale + static_cast<int64_t>(tc.g) * (2 * a.I / 128) * dkb;
-    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(2 * Ig) * a.d);
-    uint32_t boff[C::B_LOADS];
+    op.ra = c.shared ? rxs : rx;
+    op.rsa = c.shared ? rsx : rsxp;
+    const uint8_t* W = c.shared ? static_cast<const uint8_t*>(a.ws13)
+                                : static_cast<const uint8_t*>(a.w13) +
+                                      static_cast<int64_t>(c.g) * 2 * a.I * a.d;
+    const float* WS = c.shared ? a.ws13_scale
+                               : a.w13_scale + static_cast<int64_t>(c.g) * (2 * a.I / 128) * dkb;
+    op.rb = rsrc4(W, static_cast<uint32_t>(2 * Ig) * a.d);
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
       const bool up = lr >= HALF;
-      const int col = tc.n * HALF + (up ? lr - HALF : lr);
-      boff[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
+      const int col = c.n * HALF + (up ? lr - HALF : lr);
+      op.bo[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
     }
-    const i32x4_t rws =
-        rsrc4(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
-    const uint32_t sb_gate = static_cast<uint32_t>(tc.n * dkb) * 4u;
-    const uint32_t sb_up = static_cast<uint32_t>((Ig / 128 + tc.n) * dkb) * 4u;
-    f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, true>(lds, lds_sa, lds_sb, shared ? rxs : rx, aoff, shared ? rsx : rsxp, sa_off,
-                        rw, boff, rws, sb_gate, sb_up, a.d, acc);
-
+    op.rsb = rsrc4(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
+    op.sb_lo = static_cast<uint32_t>(c.n * dkb) * 4u;
+    op.sb_hi = static_cast<uint32_t>((Ig / 128 + c.n) * dkb) * 4u;
+    swizzle_rows8<C>(op.ao);
+    swizzle_rows8<C>(op.bo);
+    op.nk = nk;
+  };
+  auto nk_of = [&](int) { return nk; };
+  auto epilogue = [&](int tile, f32x4_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
     // SwiGLU, then the row max-abs over the 128 columns: lane l holds row
     // l % 16 of each 16-row group and four adjacent columns per product, so
     // the max runs over the lane's values, the four lanes of the row, and the
@@ -316,9 +405,9 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       if (lane < 16) red[wn][wm * C::WM + mi * 16 + lane] = m;
     }
-    __syncthreads();
-    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
-    const int rows_left = tc.rows - tc.m * C::BM;
+    lds_barrier();
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    const int rows_left = c.rows - c.m * C::BM;
     // E4M3 codes leave straight from registers, four columns per 4-byte store
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
@@ -328,7 +417,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
       if (lr >= rows_left) continue;
       const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
-      uint8_t* hp = H + (hrow0 + lr) * a.ldh + tc.n * HALF + wn * (C::WN / 2) + 4 * (lane >> 4);
+      uint8_t* hp = H + (hrow0 + lr) * a.ldh + c.n * HALF + wn * (C::WN / 2) + 4 * (lane >> 4);
 #pragma unroll
       for (int nj = 0; nj < NJH; ++nj)
         *reinterpret_cast<uint32_t*>(hp + nj * 16) =
@@ -336,116 +425,100 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
                          : e4m3_pack4(h[mi][nj][0] * inv, h[mi][nj][1] * inv, h[mi][nj][2] * inv,
                                       h[mi][nj][3] * inv);
       if (wn == 0 && lane < 16)
-        a.H_scale[(hrow0 + lr) * hkb + tc.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
+        a.H_scale[(hrow0 + lr) * hkb + c.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
     }
-    __syncthreads();  // red[] is rewritten by the next tile
-  }
+    // red[] is rewritten by the next tile's epilogue only after at least one
+    // more k block, whose barrier orders these reads first
+  };
+  gemm8_stream<C, true>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
 }
 
-// y = dequant(H) dequant(W2)^T per group, bf16 out.
+// y = dequant(H) dequant(W2)^T per group, bf16 out, stored from registers.
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float lds_sa[C::NST * C::NT];
   __shared__ __attribute__((aligned(16))) float lds_sb[C::NST * C::NWAVES * 2];
-  __shared__ int gtab[kMaxGroups + 1];
+  __shared__ GroupTables gt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r0 = tid >> 3;
-  load_group_table(gtab, a.tiles2, a.E);
-  const int total = gtab[a.E + 1];
+  load_group_tables(gt, a.tiles2, a.offsets, a.E);
+  const int total = gt.total;
   const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
   const int hkb = a.ldh / 128;
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const i32x4_t rh =
-      rsrc4(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
+  const i32x4_t rh = rsrc4(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
   const i32x4_t rsh =
       rsrc4(a.H_scale, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(hkb) * 4u);
-  for (int tile = xcd_logical_block(blockIdx.x, nb); tile < total; tile += nb) {
-    TileCoord tc = tile_coord(a, gtab, tile, C::BM, a.d, a.d, C::BN);
-    tc.g = __builtin_amdgcn_readfirstlane(tc.g);
-    tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
-    tc.rbase = __builtin_amdgcn_readfirstlane(tc.rbase);
-    tc.m = __builtin_amdgcn_readfirstlane(tc.m);
-    tc.n = __builtin_amdgcn_readfirstlane(tc.n);
-    const bool shared = tc.g == a.E;
-    const int Ig = shared ? a.Is : a.I;
-    const int64_t hrow0 = (shared ? a.TK : tc.rbase) + static_cast<int64_t>(tc.m) * C::BM;
-    const int rows_left = tc.rows - tc.m * C::BM;
-    uint32_t aoff[C::A_LOADS];
+  // the shared group's tiles are the last ones
+  const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
+  // weight block scales of a wave's WN output columns (inside one 128-row
+  // block of W2)
+  static_assert(128 % C::WN == 0, "a wave's columns lie in one scale block");
+
+  auto next_ops = [&](int tile, int, StreamOps8<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    const int rows_left = c.rows - c.m * C::BM;
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      aoff[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * static_cast<uint32_t>(a.ldh)
-                               : kInvalidRow;
+      op.ao[p] = lr < rows_left
+                     ? static_cast<uint32_t>(hrow0 + lr) * static_cast<uint32_t>(a.ldh)
+                     : kInvalidRow;
     }
-    const uint32_t sa_off = (tid < C::BM && tid < rows_left)
-                                ? static_cast<uint32_t>((hrow0 + tid) * hkb) * 4u
-                                : kInvalidRow;
-    const uint8_t* W = shared ? static_cast<const uint8_t*>(a.ws2)
-                              : static_cast<const uint8_t*>(a.w2) +
-                                    static_cast<int64_t>(tc.g) * a.d * a.I;
+    op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>((hrow0 + tid) * hkb) * 4u
+                                                 : kInvalidRow;
+    op.ra = rh;
+    op.rsa = rsh;
+    const uint8_t* W = c.shared ? static_cast<const uint8_t*>(a.ws2)
+                                : static_cast<const uint8_t*>(a.w2) +
+                                      static_cast<int64_t>(c.g) * a.d * a.I;
     const int ikb = Ig / 128;
-    const float* WS = shared ? a.ws2_scale
-                             : a.w2_scale + static_cast<int64_t>(tc.g) * (a.d / 128) * (a.I / 128);
-    const i32x4_t rw = rsrc4(W, static_cast<uint32_t>(a.d) * static_cast<uint32_t>(Ig));
-    uint32_t boff[C::B_LOADS];
+    const float* WS = c.shared ? a.ws2_scale
+                               : a.w2_scale + static_cast<int64_t>(c.g) * (a.d / 128) * (a.I / 128);
+    op.rb = rsrc4(W, static_cast<uint32_t>(a.d) * static_cast<uint32_t>(Ig));
 #pragma unroll
     for (int p = 0; p < C::B_LOADS; ++p) {
-      const int row = tc.n * C::BN + r0 + p * C::RPP;
-      boff[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
+      const int row = c.n * C::BN + r0 + p * C::RPP;
+      op.bo[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
     }
-    const i32x4_t rws =
-        rsrc4(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
-    // weight block scales of this wave's WN output columns (inside one
-    // 128-row block of W2)
-    static_assert(128 % C::WN == 0, "a wave's columns lie in one scale block");
-    const uint32_t sb = static_cast<uint32_t>(((tc.n * C::BN + wn * C::WN) / 128) * ikb) * 4u;
-    f32x4_t acc[C::MI][C::NJ];
-    gemm8_tile<C, false>(lds, lds_sa, lds_sb, rh, aoff, rsh, sa_off, rw, boff, rws, sb, sb, Ig,
-                         acc);
-
-    uint16_t* out = shared ? static_cast<uint16_t*>(a.yshared) +
-                                 static_cast<int64_t>(tc.m) * C::BM * a.d
-                           : static_cast<uint16_t*>(a.yperm) +
-                                 (static_cast<int64_t>(tc.rbase) + tc.m * C::BM) * a.d;
-    if constexpr (C::BM >= 128) {
-      // large tiles: the bf16 tile is staged in LDS and leaves as whole
-      // 16-byte row pieces (3% faster than 8-byte stores from registers)
-      uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
-      static_assert(C::BM * (C::BN + 8) * 2 <= 2 * C::STAGE,
-                    "the output tile fits in the LDS stages");
+    op.rsb = rsrc4(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
+    op.sb_lo = op.sb_hi =
+        static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * ikb) * 4u;
+    swizzle_rows8<C>(op.ao);
+    swizzle_rows8<C>(op.bo);
+    op.nk = Ig / BK8;
+  };
+  auto nk_of = [&](int tile) { return (tile >= shared_first ? a.Is : a.I) / BK8; };
+  auto epilogue = [&](int tile, f32x4_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int rows_left = c.rows - c.m * C::BM;
+    uint16_t* out = c.shared ? static_cast<uint16_t*>(a.yshared) +
+                                   static_cast<int64_t>(c.m) * C::BM * a.d
+                             : static_cast<uint16_t*>(a.yperm) +
+                                   (static_cast<int64_t>(c.rbase) + c.m * C::BM) * a.d;
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int row = wm * C::WM + mi * 16 + (lane & 15);
+      if (row >= rows_left) continue;
+      uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
 #pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            out_put<C, C::BN>(ot, wm * C::WM + mi * 16 + (lane & 15),
-                              wn * C::WN + nj * 16 + 4 * (lane >> 4) + r, acc[mi][nj][r]);
-      __syncthreads();
-      out_flush<C, C::BN>(ot, out + tc.n * C::BN, a.d, rows_left, a.d - tc.n * C::BN);
-      __syncthreads();
-    } else {
-      // decode tiles hold a few valid rows: 8-byte stores straight from
-      // registers, no LDS round trip
-#pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) {
-        const int row = wm * C::WM + mi * 16 + (lane & 15);
-        if (row >= rows_left) continue;
-        uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
-#pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj) {
-          const int col = tc.n * C::BN + wn * C::WN + nj * 16 + 4 * (lane >> 4);
-          if (col >= a.d) continue;
-          const f32x4_t& v = acc[mi][nj];
-          *reinterpret_cast<uint2*>(yp + col) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        const int col = c.n * C::BN + wn * C::WN + nj * 16 + 4 * (lane >> 4);
+        if (col >= a.d) continue;
+        const f32x4_t& v = acc[mi][nj];
+        *reinterpret_cast<uint2*>(yp + col) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
-  }
+  };
+  gemm8_stream<C, false>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 template <class K>
