@@ -14,42 +14,14 @@ struct TileCoord {
 
 constexpr int kMaxGroups = 513;  // 512 routed experts + the shared expert
 
-// Copies the tile prefix table (group g owns tiles [tiles[g], tiles[g+1])) to LDS.
-__device__ __forceinline__ void load_group_table(int* gtab, const int32_t* tiles, int E) {
-  for (int i = threadIdx.x; i <= E + 1; i += blockDim.x) gtab[i] = tiles[i];
-  __syncthreads();
-}
-
-// Group owning `tile` (the last g with gtab[g] <= tile), then (m, n) with m
-// fastest: the tiles that one XCD runs together share one weight slab, whose
-// whole k-extent stays in that XCD's L2 however far the tiles drift apart.
-__device__ __forceinline__ TileCoord tile_coord(const FfnArgs& a, const int* gtab, int tile, int bm,
-                                                int n_cols, int n_cols_shared, int bn) {
-  (void)n_cols;
-  (void)n_cols_shared;
-  (void)bn;
-  int lo = 0, hi = a.E + 1;  // gtab[lo] <= tile < gtab[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (gtab[mid] <= tile) lo = mid; else hi = mid;
-  }
-  TileCoord c;
-  c.g = lo;
-  c.shared = c.g == a.E;
-  c.rbase = c.shared ? 0 : a.offsets[c.g];
-  c.rows = c.shared ? static_cast<int>(a.T) : a.offsets[c.g + 1] - c.rbase;
-  const int mt = (c.rows + bm - 1) / bm;
-  const int local = tile - gtab[c.g];
-  c.n = local / mt;
-  c.m = local % mt;
-  return c;
-}
-
-// LDS copy of the tile schedule for kernels whose tile loop must issue no
-// global loads of its own (their vector-memory waits are counted by hand).
-// gnext[i] is the first tile of group i + 1 (i < E) and INT_MAX beyond, so
-// the group of a tile is the number of entries <= tile; off holds the row
-// offsets of the routed groups.
+// LDS copy of the device-built tile schedule (group g owns tiles
+// [tiles[g], tiles[g+1]); the shared expert is group E), for tile loops that
+// must issue no global loads of their own (their vector-memory waits are
+// counted by hand). gnext[i] is the first tile of group i + 1 (i < E) and
+// INT_MAX beyond, so the group of a tile is the number of entries <= tile;
+// off holds the row offsets of the routed groups. Tiles are numbered
+// (group, n, m) with m fastest: the tiles that one XCD runs together share
+// one weight slab.
 struct __attribute__((aligned(16))) GroupTables {
   int gnext[kMaxGroups - 1];
   int off[kMaxGroups];
@@ -109,12 +81,6 @@ __device__ __forceinline__ void vm_wait() {
 // hardware, which is how padding rows are handled without branches.
 constexpr uint32_t kInvalidRow = 0x80000000u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer (stride 0), range-checked against `bytes`
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
 // Raw buffer descriptor as four scalar words: base address, no stride,
 // `bytes` records (range-checked: offsets at or beyond it read as zeros).
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -148,34 +114,5 @@ __device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t voff, uint32_t lds) 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
-
-// Output tile staging: values are written to LDS as bf16 at (row, col), rows
-// padded by 16 bytes so the two row groups one store instruction touches fall
-// in different banks; then whole rows leave with 16-byte stores.
-template <int NCOLS>
-struct OutTile {
-  static constexpr int STRIDE = NCOLS + 8;  // bf16 elements per LDS row
-  static_assert(NCOLS % 8 == 0, "16-byte chunks");
-};
-
-template <class C, int NCOLS>
-__device__ __forceinline__ void out_put(uint16_t* lds, int row, int col, float v) {
-  lds[row * OutTile<NCOLS>::STRIDE + col] = f32_to_bf16(v);
-}
-
-// Copies rows [0, rows) and columns [0, cols) of the staged tile to
-// dst + row * ld (bf16 elements); cols a multiple of 8.
-template <class C, int NCOLS>
-__device__ __forceinline__ void out_flush(const uint16_t* lds, uint16_t* dst, int64_t ld, int rows,
-                                          int cols) {
-  constexpr int CPR = NCOLS / 8;  // 16-byte chunks per row
-  for (int i = threadIdx.x; i < C::BM * CPR; i += C::NT) {
-    const int row = i / CPR, c = (i % CPR) * 8;
-    if (row < rows && c < cols)
-      *reinterpret_cast<uint4*>(dst + row * ld + c) =
-          *reinterpret_cast<const uint4*>(lds + row * OutTile<NCOLS>::STRIDE + c);
-  }
-}
-
 
 }  // namespace dsmoe
