@@ -269,10 +269,18 @@ moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_route
                     const float* bias, float* logits, int32_t* idx, float* gate, int32_t* counts,
                     int32_t* near_tie, void* ws, const GateLayout& L, hipStream_t s) {
   int32_t* ntie = near_tie ? near_tie : at<int32_t>(ws, L.ntie);
+  float* partial = at<float>(ws, L.partial);
+  if (d->T > 0 && d->T <= kSmallRouterT && d->act_dtype == MOE_DT_BF16) {
+    // one launch: logits from the fp32 weights, counts and near_tie cleared
+    HIP_TRY(launch_router_small(x, w_router, d->T, d->d, d->n_experts, partial, counts, ntie, s),
+            "router (small batch)");
+    HIP_TRY(launch_route(partial, 1, logits, bias, route_params(d), idx, gate, counts, ntie, s),
+            "route");
+    return MOE_OK;
+  }
   HIP_TRY(launch_fill_i32(counts, d->n_experts, 0, s), "zero counts");
   HIP_TRY(launch_fill_i32(ntie, 1, 0, s), "zero near_tie");
   if (d->T == 0) return MOE_OK;
-  float* partial = at<float>(ws, L.partial);
   if (d->act_dtype == MOE_DT_F32)
     HIP_TRY(launch_router_f32(static_cast<const float*>(x), w_router, d->T, d->d, d->n_experts,
                               partial, s),

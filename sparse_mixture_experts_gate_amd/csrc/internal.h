@@ -27,6 +27,11 @@ hipError_t launch_router_logits_bf16(const void* x, const float* w_router, int64
                                      int splits, uint16_t* wsplit, float* partial, hipStream_t s);
 // Adds the split-K partials [splits, n] in split order into partial[0 .. n).
 hipError_t launch_sum_partials(float* partial, int splits, int64_t n, hipStream_t s);
+// Small batches (T <= kSmallRouterT, bf16 activations): fp32 logits straight
+// from the fp32 router weights; also zeroes counts[E] and *near_tie.
+constexpr int64_t kSmallRouterT = 32;
+hipError_t launch_router_small(const void* x, const float* w, int64_t T, int d, int E, float* out,
+                               int32_t* counts, int32_t* near_tie, hipStream_t s);
 hipError_t launch_route(const float* partial, int splits, float* logits_out, const float* bias,
                         const RouteParams& p, int32_t* idx, float* gate, int32_t* counts,
                         int32_t* near_tie, hipStream_t s);

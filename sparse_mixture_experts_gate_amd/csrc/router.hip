@@ -82,6 +82,116 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(float* __restrict__ p
   partial[i] = u;
 }
 
+// Router for small batches (T <= kSmallRouterT, bf16 activations): the fp32
+// weights are read once and multiplied on the VALU, fp32 FMA per term (one
+// rounding per term, as with the exact bf16-split products added in fp32).
+// Block b handles experts [b*EPB, (b+1)*EPB) for all tokens. Each thread
+// owns the 4-element k groups tid + 512 q of d; its weight groups stay in
+// registers and the activation groups of eight tokens are loaded together,
+// so a pass waits for memory once. The per-thread partial dot products are
+// reduced in a fixed order (shuffle tree, then the eight waves in order), so
+// every run gives the same bits. Block 0 also clears the per-expert counts
+// and the near-tie count that the routing kernel adds to.
+constexpr int kSmallEPB = 2;       // experts per block
+constexpr int kSmallThreads = 512;
+constexpr int kSmallKPT = 4;       // 4-element k groups per thread per chunk
+constexpr int kSmallMaxT = 32;
+
+__global__ __launch_bounds__(kSmallThreads) void router_small_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w, int T, int d, int E,
+    float* __restrict__ out, int32_t* __restrict__ counts, int32_t* __restrict__ near_tie) {
+  constexpr int NW = kSmallThreads / 64;
+  __shared__ float red[NW][kSmallEPB * kSmallMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += kSmallThreads) counts[e] = 0;
+    if (tid == 0 && near_tie) *near_tie = 0;
+  }
+  const int e0 = blockIdx.x * kSmallEPB;
+  const int d4 = d >> 2;
+  float acc[kSmallEPB][kSmallMaxT];
+#pragma unroll
+  for (int i = 0; i < kSmallEPB; ++i)
+#pragma unroll
+    for (int t = 0; t < kSmallMaxT; ++t) acc[i][t] = 0.0f;
+  for (int kc = 0; kc < d4; kc += kSmallThreads * kSmallKPT) {
+    float4 wv[kSmallEPB][kSmallKPT];
+#pragma unroll
+    for (int i = 0; i < kSmallEPB; ++i)
+#pragma unroll
+      for (int q = 0; q < kSmallKPT; ++q) {
+        const int k4 = kc + tid + kSmallThreads * q;
+        wv[i][q] = (e0 + i < E && k4 < d4)
+                       ? reinterpret_cast<const float4*>(w + static_cast<int64_t>(e0 + i) * d)[k4]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int t0 = 0; t0 < kSmallMaxT; t0 += 8) {
+      if (t0 >= T) continue;
+      uint2 xv[8][kSmallKPT];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int q = 0; q < kSmallKPT; ++q) {
+          const int k4 = kc + tid + kSmallThreads * q;
+          xv[j][q] = (t0 + j < T && k4 < d4)
+                         ? reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t0 + j) * d)[k4]
+                         : make_uint2(0u, 0u);
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int q = 0; q < kSmallKPT; ++q) {
+          const float x0 = bf16_to_f32(static_cast<uint16_t>(xv[j][q].x & 0xFFFFu));
+          const float x1 = bf16_to_f32(static_cast<uint16_t>(xv[j][q].x >> 16));
+          const float x2 = bf16_to_f32(static_cast<uint16_t>(xv[j][q].y & 0xFFFFu));
+          const float x3 = bf16_to_f32(static_cast<uint16_t>(xv[j][q].y >> 16));
+#pragma unroll
+          for (int i = 0; i < kSmallEPB; ++i) {
+            float v = acc[i][t0 + j];
+            v = __builtin_fmaf(x0, wv[i][q].x, v);
+            v = __builtin_fmaf(x1, wv[i][q].y, v);
+            v = __builtin_fmaf(x2, wv[i][q].z, v);
+            v = __builtin_fmaf(x3, wv[i][q].w, v);
+            acc[i][t0 + j] = v;
+          }
+        }
+    }
+  }
+  // fixed-order reduction. Reduce-scatter butterfly over the wave: at the
+  // step with lane bit o, a lane keeps the half of its values whose index has
+  // that bit equal to its own, adds the partner's copy of that half, and
+  // sends the other half; after six steps lane l holds the wave's sum for
+  // value index l = (expert in block) * 32 + token. Then the waves in order.
+  static_assert(kSmallEPB * kSmallMaxT == 64, "one value per lane after the butterfly");
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < kSmallEPB; ++i)
+#pragma unroll
+    for (int t = 0; t < kSmallMaxT; ++t) v[i * kSmallMaxT + t] = acc[i][t];
+#pragma unroll
+  for (int n = 64, o = 32; o >= 1; n >>= 1, o >>= 1) {
+    const bool upper = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = upper ? v[i + n / 2] : v[i];
+      const float send = upper ? v[i] : v[i + n / 2];
+      v[i] = keep + __shfl_xor(send, o, 64);
+    }
+  }
+  red[wave][lane] = v[0];
+  __syncthreads();
+  if (tid < 64) {
+    const int i = tid / kSmallMaxT, t = tid % kSmallMaxT;
+    if (t < T && e0 + i < E) {
+      float r = red[0][tid];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) r = r + red[q][tid];
+      out[static_cast<int64_t>(t) * E + e0 + i] = r;
+    }
+  }
+}
+
 constexpr int kTokPerBlock = 4;  // one wave per token
 constexpr int kMaxE = 512;
 
@@ -265,6 +375,16 @@ hipError_t launch_router_f32(const float* x, const float* w, int64_t T, int d, i
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(router_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      s, x, w, T, d, E, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_small(const void* x, const float* w, int64_t T, int d, int E, float* out,
+                               int32_t* counts, int32_t* near_tie, hipStream_t s) {
+  const int blocks = (E + kSmallEPB - 1) / kSmallEPB;
+  static_assert(kSmallRouterT <= kSmallMaxT, "the small router holds all tokens in registers");
+  hipLaunchKernelGGL(router_small_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kSmallThreads), 0, s,
+                     static_cast<const uint16_t*>(x), w, static_cast<int>(T), d, E, out, counts,
+                     near_tie);
   return hipGetLastError();
 }
 
