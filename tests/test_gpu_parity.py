@@ -49,11 +49,18 @@ def check_routing_same_logits(wl, P, g):
     return rr
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16"])
-def test_gate_bit_exact_and_independent(name):
-    wl = CONFIGS[name]
-    _log(f"gate parity {name}")
-    P = make_inputs(wl, DEV)
+# the V3 router (d = 7168, 256 experts in 8 groups of 32, top-4 groups) with
+# small experts, so that only the gate's shapes are real
+V3_GATE = CONFIGS["v3_decode_bf16"].with_(name="v3_gate", I=64, Is=64)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("small_bf16", None), ("small_bf16", 16),
+                                    ("small_bf16", 1), ("v3_gate", 32), ("v3_gate", 7)])
+def test_gate_bit_exact_and_independent(name, T):
+    # T <= 32 with bf16 activations takes the small-batch router kernel
+    wl = V3_GATE if name == "v3_gate" else CONFIGS[name]
+    _log(f"gate parity {name} T={T}")
+    P = make_inputs(wl, DEV, T=T) if T is not None else make_inputs(wl, DEV)
     g = run_gate(wl, P)
     rr = check_routing_same_logits(wl, P, g)
     # independent mode: the oracle's own fp64 router product
@@ -63,6 +70,27 @@ def test_gate_bit_exact_and_independent(name):
     differ = np.any(np.sort(ro.idx, 1) != np.sort(rr.idx, 1), axis=1)
     assert np.all(ro.near_tie[differ] | rr.near_tie[differ])
     assert ro.near_tie.mean() < 1e-3
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 64])
+def test_router_integer_inputs_exact(T):
+    """Integer-valued x and router weights make every dot product exact in
+    fp32 whatever the summation order, so the logits of both router paths
+    (small batches: fp32 FMA on the VALU; larger: split-bf16 MFMA) must equal
+    the integer products bit for bit; counts start from garbage and must be
+    cleared. E = 99 leaves the last expert block of the small path half full."""
+    wl = Workload("int_router", T=T, d=512, E=99, K=3, I=64, Is=0)
+    _log(f"router integer exact T={T}")
+    rng = np.random.default_rng(1000 + T)
+    xi = rng.integers(-3, 4, (T, wl.d))
+    wi = rng.integers(-3, 4, (wl.E, wl.d))
+    P = {"x": torch.tensor(xi, dtype=torch.bfloat16, device=DEV),
+         "w_router": torch.tensor(wi, dtype=torch.float32, device=DEV),
+         "bias": torch.zeros(wl.E, dtype=torch.float32, device=DEV)}
+    g = run_gate(wl, P)
+    exact = (xi.astype(np.int64) @ wi.astype(np.int64).T).astype(np.float32)
+    assert np.array_equal(g["logits"].view(np.uint32), exact.view(np.uint32))
+    check_routing_same_logits(wl, P, g)
 
 
 def test_route_golden_hand_example():
