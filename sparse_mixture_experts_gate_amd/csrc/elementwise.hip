@@ -11,9 +11,11 @@ namespace {
 // y[t] = y_shared[t] + sum_k gate[t,k] * y_perm[inv[t,k]]: the shared expert
 // is ungated and sees every token (mhpq.cn "DeepSeek-V3 高效训练关键技术全景
 // 解析" §1.1); routed outputs weighted by the normalized gates (kaiyunto.com
-// DeepSeek-V3 walkthrough). One workgroup per token, 16-byte accesses,
-// fp32 accumulation in slot order. KT > 0 fixes K at compile time so the K
-// gathered rows of a chunk are all loaded before the (in-order) FMAs.
+// DeepSeek-V3 walkthrough). One workgroup per token with one 16-byte chunk of
+// the row per thread (d / 8 threads up to 1024: all K + 1 loads of a thread
+// are in flight together), fp32 accumulation in slot order. KT > 0 fixes K
+// at compile time so the K gathered rows of a chunk are all loaded before
+// the (in-order) FMAs.
 __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -24,7 +26,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
 }
 
 template <int KT>
-__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ yperm,
+__global__ __launch_bounds__(1024) void combine_bf16_kernel(const uint16_t* __restrict__ yperm,
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ gate,
                                                            const uint16_t* __restrict__ yshared,
@@ -225,7 +227,9 @@ hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* ga
     const auto* yp = static_cast<const uint16_t*>(yperm);
     const auto* ys = static_cast<const uint16_t*>(yshared);
     auto* yo = static_cast<uint16_t*>(y);
-    const dim3 grid(static_cast<unsigned>(T)), block(256);
+    int nthr = ((d / 8 + 63) / 64) * 64;
+    if (nthr > 1024) nthr = 1024;
+    const dim3 grid(static_cast<unsigned>(T)), block(static_cast<unsigned>(nthr));
     if (K == 8)
       hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
     else if (K == 6)
