@@ -50,13 +50,42 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Lane moves within 16-lane rows (DPP; every lane has a source lane).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane l <-> 7 - l within 8
+constexpr int kDppMirror = 0x140;     // lane l <-> 15 - l within 16
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+// Best (value, index) of the wave in every lane. Each step pairs every lane
+// with a lane of a disjoint set that holds the same partial result, and
+// keeps the better of the two: quads, 8-lane halves and 16-lane rows by DPP,
+// then rows and half-waves by shuffles. better() is a strict order, so the
+// result is the unique best whatever the pairing.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(v, m, kWave);
-    const int oi = __shfl_xor(i, m, kWave);
+  auto step = [&](float ov, int oi) {
     if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  }
+  };
+  step(dpp_f<kDppXor1>(v), dpp_i<kDppXor1>(i));
+  step(dpp_f<kDppXor2>(v), dpp_i<kDppXor2>(i));
+  step(dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
+  step(dpp_f<kDppMirror>(v), dpp_i<kDppMirror>(i));
+  step(__shfl_xor(v, 16, kWave), __shfl_xor(i, 16, kWave));
+  step(__shfl_xor(v, 32, kWave), __shfl_xor(i, 32, kWave));
+}
+
+// Top two (with multiplicity) of the union of two disjoint sets' top twos.
+__device__ __forceinline__ void merge_top2(float& a0, float& a1, float b0, float b1) {
+  const float hi = fmaxf(a0, b0), lo = fminf(a0, b0);
+  a1 = fmaxf(lo, fmaxf(a1, b1));
+  a0 = hi;
 }
 
 // partial[i] = ((partial[i] + partial[n + i]) + ...) + partial[(S-1) n + i]:
@@ -245,7 +274,27 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ pa
     if (G > 1 && active) {
       // group score: fp32 sum of the group's topn best biased scores, largest first
       float gsc = -INFINITY;
-      if (lane < G && p.topn <= 2) {
+      if (GS == 32 && p.topn <= 2) {
+        // groups of 32 are half-waves: expert lane + 64 j is in group
+        // 2 j + lane / 32, so each half-wave reduces its top two in registers
+        float gs[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          float t0 = c[j], t1 = -INFINITY;
+          merge_top2(t0, t1, dpp_f<kDppXor1>(t0), dpp_f<kDppXor1>(t1));
+          merge_top2(t0, t1, dpp_f<kDppXor2>(t0), dpp_f<kDppXor2>(t1));
+          merge_top2(t0, t1, dpp_f<kDppHalfMirror>(t0), dpp_f<kDppHalfMirror>(t1));
+          merge_top2(t0, t1, dpp_f<kDppMirror>(t0), dpp_f<kDppMirror>(t1));
+          merge_top2(t0, t1, __shfl_xor(t0, 16, kWave), __shfl_xor(t1, 16, kWave));
+          gs[j] = p.topn == 2 ? t0 + t1 : t0;
+        }
+        // lane g < G collects group g = 2 (g / 2) + g % 2 from its half-wave
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const float v = __shfl(gs[j], (lane & 1) * 32, kWave);
+          if ((lane >> 1) == j && lane < G) gsc = v;
+        }
+      } else if (lane < G && p.topn <= 2) {
         // the two best (or the best) of the group in two registers
         float t0 = -INFINITY, t1 = -INFINITY;
         for (int i = 0; i < GS; ++i) {
