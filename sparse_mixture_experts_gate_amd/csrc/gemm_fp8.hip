@@ -5,9 +5,12 @@
 // partial products are promoted to fp32 at every 128-wide slice of the
 // contraction (mhpq.cn "DeepSeek-V3 高效训练关键技术全景解析" §4.1; gkm0120.cn
 // DeepSeek-V3 notes, Q8). Here one LDS stage holds exactly one 128-wide slice,
-// so a single v_mfma_scale_f32_16x16x128_f8f6f4 (unit hardware scales) yields
-// the slice's exact-product partial sum for a 16x16 sub-tile; the fp32 scale
-// product s_a(row) * s_b(block) is applied on the VALU as it is accumulated.
+// so two chained v_mfma_scale_f32_32x32x64_f8f6f4 (unit hardware scales, k 0-63
+// then 64-127) yield the slice's exact-product partial sum for a 32x32
+// sub-tile; the fp32 scale product s_a(row) * s_b(block) is applied on the
+// VALU as it is accumulated. The 32x32x64 operand pattern (32 rows x two
+// 32-byte k groups per wave) reads LDS without bank conflicts; the 16x16x128
+// one (16 rows x four k groups) is two-way conflicted under any chunk swizzle.
 //
 // The gate/up GEMM covers 128 intermediate columns per tile, i.e. exactly one
 // 1x128 quantization tile of H: its epilogue computes silu(gate) * up, the
@@ -33,7 +36,7 @@ struct Tile8 {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
-  static constexpr int MI = WM / 16, NJ = WN / 16;
+  static constexpr int MI = WM / 32, NJ = WN / 32;
   static constexpr int RPP = NT / 8;
   static constexpr int A_LOADS = BM / RPP;
   static constexpr int B_LOADS = BN / RPP;
@@ -41,6 +44,7 @@ struct Tile8 {
   static constexpr int LDS_BYTES = NST * STAGE;
   // loads per thread and k block: A and B tiles, one row scale, two block scales
   static constexpr int NL = A_LOADS + B_LOADS + 3;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "waves cover whole 32x32 products");
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(BM <= NT, "one thread per row loads the activation scales");
   static_assert(NST >= 3 && NL * (NST - 2) <= 63, "ring depth within the vmcnt range");
@@ -52,7 +56,8 @@ using T8GateDec = Tile8<32, 256, 32, 64, 4>;   // 4 waves, 144 KB ring
 using T8DownDec = Tile8<32, 128, 32, 64, 6>;   // 2 waves, 120 KB ring
 
 // Byte offset of 16-byte chunk `ch` of row `r`, swizzled with (r >> 1) & 7 so
-// that the 16 rows one 128-bit LDS access serves spread over all 64 banks.
+// that the 32 rows x 2 chunks one 128-bit fragment read serves spread over all
+// 64 banks.
 __device__ __forceinline__ int lds_off8(int r, int ch) {
   return r * BK8 + ((ch ^ ((r >> 1) & 7)) << 4);
 }
@@ -61,15 +66,16 @@ template <class C, bool SWIGLU>
 __device__ __forceinline__ int b_row8(int wn, int nj) {
   if constexpr (SWIGLU) {
     constexpr int half = C::BN / 2, hw = C::WN / 2, njh = C::NJ / 2;
-    return nj < njh ? wn * hw + nj * 16 : half + wn * hw + (nj - njh) * 16;
+    return nj < njh ? wn * hw + nj * 32 : half + wn * hw + (nj - njh) * 32;
   } else {
-    return wn * C::WN + nj * 16;
+    return wn * C::WN + nj * 32;
   }
 }
 
-__device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int kg) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_off8(r, 2 * kg));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_off8(r, 2 * kg + 1));
+// 32 bytes of row r: chunks ch and ch + 1
+__device__ __forceinline__ i32x8_t frag8(const uint8_t* tile, int r, int ch) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + lds_off8(r, ch));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + lds_off8(r, ch + 1));
   i32x8_t v;
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
@@ -128,39 +134,50 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
 // acc[mi][nj] += (A_kb B_kb^T) * s_a[row][kb] * s_b[kb] for the k block in
 // ring stage st (s_b: the gate block for the first half of the wave's column
 // sub-tiles, the up block for the second; one block without SWIGLU). The
-// weight fragment goes first: lane l then owns row l % 16 of each 16-row
-// group and four adjacent columns, so one row-scale x block-scale product
-// serves all four values of a product. The MI x NJ products are pipelined one
-// MFMA deep: MFMA t runs in the matrix core while the VALU folds product t-1
-// into its accumulator (4 FMAs). mid() runs once every LDS read of the stage
-// has been issued, before the last row group's MFMAs, whose operands are
-// then in registers.
+// weight fragment goes first: lane l then owns token row l % 32 of each
+// 32-row group and 16 columns of each 32x32 product (columns 8g + 4(l / 32)
+// + q, g and q below 4), so one row-scale x block-scale product serves all 16
+// values of a product. A product is two MFMAs (k 0-63, then 64-127 onto the
+// first's result, in the matrix core). Products are pipelined one deep:
+// product t's MFMAs run while the VALU folds product t-1 into its
+// accumulator. mid() runs once every LDS read of the stage has been issued,
+// before the last row group's MFMAs, whose operands are then in registers.
 template <class C, bool SWIGLU, class Mid>
 __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_sa,
                                            const float* lds_sb, int st, int wave, int wm, int wn,
-                                           int lane, f32x4_t (&acc)[C::MI][C::NJ], Mid&& mid) {
+                                           int lane, f32x16_t (&acc)[C::MI][C::NJ], Mid&& mid) {
   const uint8_t* As = lds + st * C::STAGE;
   const uint8_t* Bs = As + C::BM * BK8;
   const float s_lo = lds_sb[(st * C::NWAVES + wave) * 2];
   const float s_hi = SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
-  const int kg = lane >> 4;
+  const int rl = lane & 31;
+  const int ch = 2 * (lane >> 5);  // first chunk of the lane's 32-byte k group
   float sl[C::MI], sh[C::MI];
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
-    const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 16 + (lane & 15)];
+    const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 32 + rl];
     sl[mi] = sa * s_lo;
     sh[mi] = sa * s_hi;
   }
-  i32x8_t bfr[C::NJ];
+  i32x8_t bfr[C::NJ][2];
 #pragma unroll
-  for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + (lane & 15), kg);
-  auto a_frag = [&](int m) { return frag8(As, wm * C::WM + m * 16 + (lane & 15), kg); };
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      bfr[nj][h] = frag8(Bs, b_row8<C, SWIGLU>(wn, nj) + rl, 4 * h + ch);
+  auto a_frag = [&](int m, int h) { return frag8(As, wm * C::WM + m * 32 + rl, 4 * h + ch); };
   constexpr int NP = C::MI * C::NJ;
   constexpr int TMID = (C::MI - 1) * C::NJ;  // first product of the last row group
-  f32x4_t p[2];
-  i32x8_t af[2];
-  af[0] = a_frag(0);
+  f32x16_t p[2];
+  i32x8_t af[2][2];
+  af[0][0] = a_frag(0, 0);
+  af[0][1] = a_frag(0, 1);
+  auto fold = [&](int u) {
+    const int pm = u / C::NJ, pn = u % C::NJ;
+    const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[pm][pn][r] = __builtin_fmaf(p[u & 1][r], s, acc[pm][pn][r]);
+  };
 #pragma unroll
   for (int t = 0; t < NP; ++t) {
     const int mi = t / C::NJ, nj = t % C::NJ;
@@ -169,24 +186,20 @@ __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_
       mid();
       __builtin_amdgcn_sched_barrier(0);
     }
-    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[nj], af[mi & 1], zero, 0, 0, 0,
-                                                                127, 0, 127);
-    if (nj == 0 && mi + 1 < C::MI) af[(mi + 1) & 1] = a_frag(mi + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t > 0) {
-      const int pm = (t - 1) / C::NJ, pn = (t - 1) % C::NJ;
-      const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[pm][pn][r] = __builtin_fmaf(p[(t - 1) & 1][r], s, acc[pm][pn][r]);
+    const f32x16_t zero = {};
+    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][0], af[mi & 1][0], zero, 0,
+                                                               0, 0, 127, 0, 127);
+    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][1], af[mi & 1][1],
+                                                               p[t & 1], 0, 0, 0, 127, 0, 127);
+    if (nj == 0 && mi + 1 < C::MI) {
+      af[(mi + 1) & 1][0] = a_frag(mi + 1, 0);
+      af[(mi + 1) & 1][1] = a_frag(mi + 1, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (t > 0) fold(t - 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  {
-    constexpr int pm = C::MI - 1, pn = C::NJ - 1;
-    const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[pm][pn][r] = __builtin_fmaf(p[(NP - 1) & 1][r], s, acc[pm][pn][r]);
-  }
+  fold(NP - 1);
 }
 
 // The persistent FP8 GEMMs run every tile of a workgroup (tiles first,
@@ -251,11 +264,11 @@ __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float*
     lds_barrier();
   };
   for (int tc = first; tc < total; tc += nb) {
-    f32x4_t acc[C::MI][C::NJ];
+    f32x16_t acc[C::MI][C::NJ];
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x16_t{};
     const int nkc = nk_of(tc);
     for (int kc = 0; kc < nkc; ++kc) {
       issue(st_issue);  // into the stage read in the previous k block
@@ -383,27 +396,25 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
     op.nk = nk;
   };
   auto nk_of = [&](int) { return nk; };
-  auto epilogue = [&](int tile, f32x4_t (&acc)[C::MI][C::NJ]) {
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
-    // SwiGLU, then the row max-abs over the 128 columns: lane l holds row
-    // l % 16 of each 16-row group and four adjacent columns per product, so
-    // the max runs over the lane's values, the four lanes of the row, and the
-    // tile's WAVES_N waves
+    // SwiGLU, then the row max-abs over the 128 columns: lane l holds 16 of
+    // the 32 columns of row l % 32 in each product, lane l ^ 32 the other 16,
+    // and the tile's WAVES_N waves the rest of the row
     constexpr int NJH = C::NJ / 2;
-    float h[C::MI][NJH][4];
+    float h[C::MI][NJH][16];
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
       float m = 0.0f;
 #pragma unroll
       for (int nj = 0; nj < NJH; ++nj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 16; ++r) {
           h[mi][nj][r] = silu_f32(acc[mi][nj][r]) * acc[mi][nj + NJH][r];
           m = fmaxf(m, fabsf(h[mi][nj][r]));
         }
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
       m = fmaxf(m, __shfl_xor(m, 32, 64));
-      if (lane < 16) red[wn][wm * C::WM + mi * 16 + lane] = m;
+      if (lane < 32) red[wn][wm * C::WM + mi * 32 + lane] = m;
     }
     lds_barrier();
     const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
@@ -411,20 +422,22 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
     // E4M3 codes leave straight from registers, four columns per 4-byte store
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
-      const int lr = wm * C::WM + mi * 16 + (lane & 15);
+      const int lr = wm * C::WM + mi * 32 + (lane & 31);
       float amax = red[0][lr];
 #pragma unroll
       for (int w = 1; w < C::WAVES_N; ++w) amax = fmaxf(amax, red[w][lr]);
       if (lr >= rows_left) continue;
       const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
-      uint8_t* hp = H + (hrow0 + lr) * a.ldh + c.n * HALF + wn * (C::WN / 2) + 4 * (lane >> 4);
+      uint8_t* hp = H + (hrow0 + lr) * a.ldh + c.n * HALF + wn * (C::WN / 2) + 4 * (lane >> 5);
 #pragma unroll
       for (int nj = 0; nj < NJH; ++nj)
-        *reinterpret_cast<uint32_t*>(hp + nj * 16) =
-            amax == 0.0f ? 0u
-                         : e4m3_pack4(h[mi][nj][0] * inv, h[mi][nj][1] * inv, h[mi][nj][2] * inv,
-                                      h[mi][nj][3] * inv);
-      if (wn == 0 && lane < 16)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float* v = &h[mi][nj][4 * g];
+          *reinterpret_cast<uint32_t*>(hp + nj * 32 + 8 * g) =
+              amax == 0.0f ? 0u : e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        }
+      if (wn == 0 && lane < 32)
         a.H_scale[(hrow0 + lr) * hkb + c.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
     }
     // red[] is rewritten by the next tile's epilogue only after at least one
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
     op.nk = Ig / BK8;
   };
   auto nk_of = [&](int tile) { return (tile >= shared_first ? a.Is : a.I) / BK8; };
-  auto epilogue = [&](int tile, f32x4_t (&acc)[C::MI][C::NJ]) {
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
     const int rows_left = c.rows - c.m * C::BM;
     uint16_t* out = c.shared ? static_cast<uint16_t*>(a.yshared) +
@@ -505,17 +518,19 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
                                    (static_cast<int64_t>(c.rbase) + c.m * C::BM) * a.d;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
-      const int row = wm * C::WM + mi * 16 + (lane & 15);
+      const int row = wm * C::WM + mi * 32 + (lane & 31);
       if (row >= rows_left) continue;
       uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) {
-        const int col = c.n * C::BN + wn * C::WN + nj * 16 + 4 * (lane >> 4);
-        if (col >= a.d) continue;
-        const f32x4_t& v = acc[mi][nj];
-        *reinterpret_cast<uint2*>(yp + col) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
+      for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = c.n * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (col >= a.d) continue;
+          const f32x16_t& v = acc[mi][nj];
+          *reinterpret_cast<uint2*>(yp + col) = make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]),
+                                                           pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+        }
     }
   };
   gemm8_stream<C, false>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
