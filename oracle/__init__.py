@@ -7,3 +7,4 @@ HIP library (no kernels, headers, helpers or tables); the only thing both
 sides see is the seeded input data.
 """
 from .moe_oracle import *  # noqa: F401,F403
+from .moe_backward import *  # noqa: F401,F403
