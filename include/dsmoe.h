@@ -216,6 +216,90 @@ moe_status moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t n
 moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, int32_t cols,
                                  uint8_t* q, float* scale, hipStream_t stream);
 
+/* ---- Training: forward that keeps tensors for the backward, and the backward
+ *
+ * bf16 activations and bf16 weights only (other dtypes: MOE_ERR_UNSUPPORTED).
+ * The backward differentiates the layer for the selection its forward made
+ * (top-K is piecewise constant in every parameter): with the gates
+ * g = s / S over the selected sigmoid scores (kaiyunto.com walkthrough,
+ * DeepSeekMoE paragraph), gradient flows to the selected router logits
+ * through the normalisation and the sigmoid, and from there to x and the
+ * router weights; the selection bias receives none, since it is adjusted by
+ * the load rule instead (mhpq.cn §1.2). Weight gradients are fp32: the pages
+ * keep weight gradients in high precision (mhpq.cn §4.1). Intermediates are
+ * bf16 with fp32 accumulation, like the forward's. */
+
+/* Tensors the training forward writes for the backward (device pointers,
+ * caller-owned; TK = T*K, ldh = max(I, Is); rows 0..TK-1 are the routed
+ * rows in permuted order, rows TK..TK+T-1 the shared expert's):
+ *   logits [T, E] fp32, topk_idx [T, K] int32, topk_gate [T, K] fp32,
+ *   counts [E] int32, offsets [E+1] int32, perm [TK] int32, inv [T, K] int32
+ *     as in moe_gate / moe_permute;
+ *   h      [TK + T, ldh] bf16, silu(a) * b, the down projection's input;
+ *   gu     [TK + T, 2 ldh] bf16, the pre-activations a = x W1^T in columns
+ *          [0, Ig) and b = x W3^T in [Ig, 2 Ig), Ig = I for routed rows and
+ *          Is for shared rows;
+ *   y_perm [TK, d] bf16, the routed experts' outputs before gating. */
+typedef struct moe_saved {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  void* h;
+  void* gu;
+  void* y_perm;
+} moe_saved;
+
+/* deepseek_moe_forward that also fills `saved` (every field required; h and
+ * gu only when Is > 0 covers the shared rows too). Same workspace as
+ * deepseek_moe_forward. */
+moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const float* w_router,
+                             const float* bias, const moe_weights* w, void* y,
+                             const moe_saved* saved, int32_t* near_tie, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Transposed bf16 copies of the expert weights, read by the backward's
+ * input-gradient GEMMs (whose contraction runs over the weights' output
+ * rows): w13_t [E, d, 2I], w2_t [E, I, d], ws13_t [d, 2Is], ws2_t [Is, d].
+ * To be refreshed whenever the weights change. */
+typedef struct moe_weights_t {
+  void* w13_t;
+  void* w2_t;
+  void* ws13_t;
+  void* ws2_t;
+} moe_weights_t;
+
+moe_status moe_transpose_weights(const moe_layer_desc* desc, const moe_weights* w,
+                                 const moe_weights_t* wt, hipStream_t stream);
+
+/* Gradients of the layer (fp32, device pointers, fully overwritten):
+ *   dw13 [E, 2I, d], dw2 [E, d, I], dws13 [2Is, d], dws2 [d, Is]
+ *   (the shared ones NULL when Is == 0), dw_router [E, d]. An expert that
+ *   received no token gets zero gradients. */
+typedef struct moe_grads {
+  float* dw13;
+  float* dw2;
+  float* dws13;
+  float* dws2;
+  float* dw_router;
+} moe_grads;
+
+/* Bytes of workspace moe_backward needs for `desc`. Host only. */
+moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes);
+
+/* Backward of the layer from the output gradient dy [T, d] bf16:
+ *   dx [T, d] bf16 OUT, the input gradient (experts, shared expert and router);
+ *   g  OUT, the weight gradients;
+ * x, w_router: the forward's inputs; wt: moe_transpose_weights of the
+ * forward's weights; saved: what moe_forward_train wrote. */
+moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* w_router,
+                        const moe_weights_t* wt, const moe_saved* saved, const void* dy,
+                        void* dx, const moe_grads* g, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 /* Timing hook for benchmarks (thread-local setting). With n_events >= 6,
  * deepseek_moe_forward records events[0..5] on its stream: before the router,
  * after routing, right before the gate/up GEMM, after it, after the down GEMM

@@ -42,6 +42,20 @@ class MoeWeights(ctypes.Structure):
                 ("w13", "w2", "ws13", "ws2", "w13_scale", "w2_scale", "ws13_scale", "ws2_scale")]
 
 
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logits", "topk_idx", "topk_gate", "counts", "offsets", "perm", "inv", "h", "gu",
+                 "y_perm")]
+
+
+class MoeWeightsT(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w13_t", "w2_t", "ws13_t", "ws2_t")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dw13", "dw2", "dws13", "dws2", "dw_router")]
+
+
 def header_symbols() -> list[str]:
     """Names of the functions that include/dsmoe.h declares."""
     txt = open(HEADER).read()
@@ -72,6 +86,12 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_fp8_blocks": [P, I32, I64, I32, I32, P, P, P],
             "moe_quantize_fp8_rows": [P, I32, I64, I32, P, P, P],
             "moe_profile_events": [ctypes.POINTER(ctypes.c_void_p), I32],
+            "moe_forward_train": [D, P, P, P, W, P, ctypes.POINTER(MoeSaved), P, P,
+                                  ctypes.c_size_t, P],
+            "moe_transpose_weights": [D, W, ctypes.POINTER(MoeWeightsT), P],
+            "moe_backward_workspace_size": [D, ctypes.POINTER(ctypes.c_size_t)],
+            "moe_backward": [D, P, P, ctypes.POINTER(MoeWeightsT), ctypes.POINTER(MoeSaved), P, P,
+                             ctypes.POINTER(MoeGrads), P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -197,3 +217,48 @@ def moe_profile_events(events) -> None:
 def moe_quantize_fp8_rows(src, q, scale, stream=None):
     _check(lib().moe_quantize_fp8_rows(_p(src), _dt(src), src.shape[0], src.shape[1], _p(q),
                                        _p(scale), _stream(stream)), "moe_quantize_fp8_rows")
+
+
+def _struct(cls, **tensors):
+    return cls(**{k: (None if v is None else _p(v).value) for k, v in tensors.items()})
+
+
+def make_saved(**tensors) -> MoeSaved:
+    """MoeSaved from tensors named like its fields."""
+    return _struct(MoeSaved, **tensors)
+
+
+def make_weights_t(w13_t, w2_t, ws13_t=None, ws2_t=None) -> MoeWeightsT:
+    return _struct(MoeWeightsT, w13_t=w13_t, w2_t=w2_t, ws13_t=ws13_t, ws2_t=ws2_t)
+
+
+def make_grads(dw13, dw2, dws13, dws2, dw_router) -> MoeGrads:
+    return _struct(MoeGrads, dw13=dw13, dw2=dw2, dws13=dws13, dws2=dws2, dw_router=dw_router)
+
+
+def moe_forward_train(desc, x, w_router, bias, weights: MoeWeights, y, saved: MoeSaved, near_tie,
+                      ws, stream=None):
+    _check(lib().moe_forward_train(ctypes.byref(desc), _p(x), _p(w_router), _p(bias),
+                                   ctypes.byref(weights), _p(y), ctypes.byref(saved), _p(near_tie),
+                                   _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward_train")
+
+
+def moe_transpose_weights(desc, weights: MoeWeights, wt: MoeWeightsT, stream=None):
+    _check(lib().moe_transpose_weights(ctypes.byref(desc), ctypes.byref(weights),
+                                       ctypes.byref(wt), _stream(stream)),
+           "moe_transpose_weights")
+
+
+def moe_backward_workspace_size(desc: MoeLayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return n.value
+
+
+def moe_backward(desc, x, w_router, wt: MoeWeightsT, saved: MoeSaved, dy, dx, grads: MoeGrads, ws,
+                 stream=None):
+    _check(lib().moe_backward(ctypes.byref(desc), _p(x), _p(w_router), ctypes.byref(wt),
+                              ctypes.byref(saved), _p(dy), _p(dx), ctypes.byref(grads), _p(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_backward")

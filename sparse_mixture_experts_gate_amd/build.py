@@ -29,7 +29,7 @@ NO_CONTRACT = {"router.hip", "elementwise.hip"}
 # which serialized the MFMAs of the decode tiles behind the copies out
 MFMA_VGPR = {"gemm_fp8.hip"}
 SOURCES = ["dsmoe_api.cpp", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "gemm_fp8.hip", "elementwise.hip"]
+           "gemm_fp8.hip", "elementwise.hip", "backward.hip"]
 
 
 def _compile(src: str) -> str:

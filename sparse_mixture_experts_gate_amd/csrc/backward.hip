@@ -1,0 +1,594 @@
+// Backward of the DeepSeekMoE feed-forward layer on gfx950 for bf16
+// activations and weights: fp32 accumulation everywhere, fp32 weight
+// gradients (the pages keep weight gradients in high precision: mhpq.cn
+// "DeepSeek-V3 高效训练关键技术全景解析" §4.1), bf16 intermediates like the
+// forward's.
+//
+// For a fixed selection the layer is y_t = FFN_s(x_t) + sum_k g_tk FFN_e(x_t)
+// with g = s / S over the selected sigmoid scores (kaiyunto.com DeepSeek-V3
+// walkthrough, DeepSeekMoE paragraph; mhpq.cn §1.1); the selection bias gets
+// no gradient (it follows the load rule, mhpq.cn §1.2). The steps:
+//   gate:    dg_tk = <dy_t, y_perm[r]>, dYp[r] = g_tk dy_t (r = inv[t,k]),
+//            du_tk = (dg_tk - sum_j g_tj dg_tj) / S_t * s_tk (1 - s_tk);
+//   dgrad2:  dH = dYp W2_e (shared: dy Ws2), then the SwiGLU backward
+//            da = dH b silu'(a), db = dH silu(a) from the saved a, b;
+//   dgrad1:  dA = [da | db] [W1_e; W3_e] (the forward's down-GEMM kernel on
+//            transposed weight copies);
+//   combine: dx_t = dA_s[t] + sum_k dA[inv[t,k]] + sum_k du_tk Wr[e_tk];
+//   router:  dWr[e] = sum over e's rows of du x;
+//   wgrad:   dW13_e = [da | db]_e^T A_e, dW2_e = dYp_e^T H_e, as GEMMs whose
+//            contraction runs over the expert's tokens, on token-major copies
+//            of the operands with every segment padded to 64 tokens.
+#include "device_common.h"
+#include "internal.h"
+#include "tile_schedule.h"
+#include "gemm_bf16_core.h"
+#include "sigmoid_ieee.h"
+
+namespace dsmoe {
+
+namespace {
+
+// ---- transposes ------------------------------------------------------------
+
+constexpr int kTr = 64;       // tile edge
+constexpr int kTrPitch = 66;  // LDS row pitch (elements): 132-byte rows keep the
+                              // four 16-row groups of a column read on distinct banks
+
+// dst[b][c][r] = src[b][r][c] for r < R, c < C (R, C multiples of 8).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             int R, int C,
+                                                             uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTr * kTrPitch];
+  const int tid = threadIdx.x;
+  const int64_t mat = static_cast<int64_t>(blockIdx.z) * R * C;
+  const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr;
+  {
+    const int r = tid >> 2, cc = (tid & 3) * 16;
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + r * kTrPitch + cc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      const int c = c0 + cc + 8 * h;
+      if (r0 + r < R && c < C)
+        v = *reinterpret_cast<const uint4*>(src + mat + static_cast<int64_t>(r0 + r) * C + c);
+      t32[4 * h + 0] = v.x;
+      t32[4 * h + 1] = v.y;
+      t32[4 * h + 2] = v.z;
+      t32[4 * h + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, rr = (tid & 3) * 16;
+  if (c0 + c >= C) return;
+  uint16_t* out = dst + mat + static_cast<int64_t>(c0 + c) * R + r0 + rr;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (r0 + rr + 8 * h >= R) break;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 8 * h + 2 * j;
+      w[j] = static_cast<uint32_t>(tile[(rr + i) * kTrPitch + c]) |
+             (static_cast<uint32_t>(tile[(rr + i + 1) * kTrPitch + c]) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + 8 * h) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Token-major copy for the weight-gradient GEMMs: dst[c][p] (row stride ldp)
+// for c < cols. Column p of routed segment g (g < E) at i = p - poff[g] takes
+// row (perm ? perm[offsets[g] + i] : offsets[g] + i) of src (row stride ld)
+// when i < R_g; column p of the shared segment (g == E) takes row i < T of
+// src_s (row stride ld_s); every other column is zero. Segments start at
+// multiples of 64, so one 64-column tile lies in one segment.
+__global__ __launch_bounds__(256) void token_major_kernel(
+    const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm,
+    const uint16_t* __restrict__ src_s, int64_t ld_s, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ poff, int E, int G, int64_t T, int cols, int64_t ldp,
+    uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTr * kTrPitch];
+  __shared__ const uint16_t* rowp[kTr];
+  __shared__ int gsh;
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.x * kTr, c0 = blockIdx.y * kTr;
+  if (p0 >= poff[G]) return;
+  if (tid == 0) {
+    int lo = 0, hi = G - 1;  // last segment starting at or before p0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
+    }
+    gsh = lo;
+  }
+  __syncthreads();
+  const int g = gsh;
+  if (tid < kTr) {
+    const int64_t i = static_cast<int64_t>(p0) + tid - poff[g];
+    const uint16_t* p = nullptr;
+    if (g < E) {
+      const int base = offsets[g];
+      if (i < offsets[g + 1] - base) {
+        const int64_t row = perm ? perm[base + i] : base + i;
+        p = src + row * ld;
+      }
+    } else if (i < T) {
+      p = src_s + i * ld_s;
+    }
+    rowp[tid] = p;
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 2, cc = (tid & 3) * 16;
+    const uint16_t* sp = rowp[r];
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + r * kTrPitch + cc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (sp) v = *reinterpret_cast<const uint4*>(sp + c0 + cc + 8 * h);
+      t32[4 * h + 0] = v.x;
+      t32[4 * h + 1] = v.y;
+      t32[4 * h + 2] = v.z;
+      t32[4 * h + 3] = v.w;
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, pp = (tid & 3) * 16;
+  uint16_t* out = dst + static_cast<int64_t>(c0 + c) * ldp + p0 + pp;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 8 * h + 2 * j;
+      w[j] = static_cast<uint32_t>(tile[(pp + i) * kTrPitch + c]) |
+             (static_cast<uint32_t>(tile[(pp + i + 1) * kTrPitch + c]) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + 8 * h) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// poff[g]: start of segment g in the token-major operands. Routed segment g
+// spans max(1, ceil(R_g / 64)) * 64 columns (an empty expert keeps one block
+// of zeros, so its weight gradient comes out as zeros from the same GEMM),
+// the shared segment ceil(T / 64) * 64.
+constexpr int kPlanT = 1024;
+__global__ __launch_bounds__(kPlanT) void wgrad_plan_kernel(const int32_t* __restrict__ offsets,
+                                                            int E, int64_t T, int shared,
+                                                            int32_t* __restrict__ poff) {
+  __shared__ int v[kPlanT];
+  const int tid = threadIdx.x;
+  int len = 0;
+  if (tid < E) {
+    const int r = offsets[tid + 1] - offsets[tid];
+    len = max(1, (r + 63) / 64) * 64;
+  } else if (tid == E && shared) {
+    len = static_cast<int>((T + 63) / 64) * 64;
+  }
+  v[tid] = len;
+  __syncthreads();
+  for (int o = 1; o < kPlanT; o <<= 1) {
+    const int add = tid >= o ? v[tid - o] : 0;
+    __syncthreads();
+    v[tid] += add;
+    __syncthreads();
+  }
+  const int G = E + (shared ? 1 : 0);
+  if (tid == 0) poff[0] = 0;
+  if (tid < G) poff[tid + 1] = v[tid];
+}
+
+// ---- gate and router gradients -------------------------------------------
+
+constexpr int kRowT = 256;
+
+__device__ __forceinline__ float block_sum4(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
+// One workgroup per token t: dg_tk = <dy_t, y_perm[inv[t,k]]> (fp32, fixed
+// order), dYp[inv[t,k]] = bf16(g_tk dy_t), then the router gradient of the
+// selected logits du_tk (also scattered to permuted order as du_perm).
+__global__ __launch_bounds__(kRowT) void bwd_gate_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ yperm,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ inv,
+    const float* __restrict__ gate, const float* __restrict__ logits, int K, int E, int d,
+    uint16_t* __restrict__ dyp, float* __restrict__ du, float* __restrict__ du_perm) {
+  __shared__ float red[4];
+  __shared__ float dg[64];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch = d / 8;
+  const uint16_t* dyr = dy + t * d;
+  for (int k = 0; k < K; ++k) {
+    const int64_t r = inv[t * K + k];
+    const float g = gate[t * K + k];
+    const uint16_t* yr = yperm + r * d;
+    uint16_t* outr = dyp + r * d;
+    float acc = 0.0f;
+    for (int ch = tid; ch < nch; ch += kRowT) {
+      const uint4 a = *reinterpret_cast<const uint4*>(dyr + ch * 8);
+      const uint4 b = *reinterpret_cast<const uint4*>(yr + ch * 8);
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = __uint_as_float(aw[j] << 16), a1 = __uint_as_float(aw[j] & 0xFFFF0000u);
+        const float b0 = __uint_as_float(bw[j] << 16), b1 = __uint_as_float(bw[j] & 0xFFFF0000u);
+        acc += a0 * b0;
+        acc += a1 * b1;
+        ow[j] = pack_bf16x2(g * a0, g * a1);
+      }
+      *reinterpret_cast<uint4*>(outr + ch * 8) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+    const float s = block_sum4(acc, red);
+    if (tid == 0) dg[k] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float S = 0.0f, mean = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      S += sigmoid_ieee(logits[t * E + idx[t * K + k]]);
+      mean += gate[t * K + k] * dg[k];
+    }
+    for (int k = 0; k < K; ++k) {
+      const float s = sigmoid_ieee(logits[t * E + idx[t * K + k]]);
+      const float v = S > 0.0f ? (dg[k] - mean) / S * (s * (1.0f - s)) : 0.0f;
+      du[t * K + k] = v;
+      du_perm[inv[t * K + k]] = v;
+    }
+  }
+}
+
+// dx_t = dA_s[t] + sum_k dA[inv[t,k]] + sum_k du_tk Wr[idx[t,k]], fp32 in that
+// order, bf16 out. One workgroup per token.
+__global__ __launch_bounds__(kRowT) void bwd_combine_kernel(
+    const uint16_t* __restrict__ dap, const uint16_t* __restrict__ das,
+    const int32_t* __restrict__ inv, const int32_t* __restrict__ idx,
+    const float* __restrict__ du, const float* __restrict__ wr, int K, int d,
+    uint16_t* __restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  const int nch = d / 8;
+  for (int ch = threadIdx.x; ch < nch; ch += kRowT) {
+    float acc[8];
+    if (das) {
+      const uint4 v = *reinterpret_cast<const uint4*>(das + t * d + ch * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    }
+    for (int k = 0; k < K; ++k) {
+      const int64_t r = inv[t * K + k];
+      const uint4 v = *reinterpret_cast<const uint4*>(dap + r * d + ch * 8);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    for (int k = 0; k < K; ++k) {
+      const float u = du[t * K + k];
+      const float* wrow = wr + static_cast<int64_t>(idx[t * K + k]) * d + ch * 8;
+      const float4 lo = *reinterpret_cast<const float4*>(wrow);
+      const float4 hi = *reinterpret_cast<const float4*>(wrow + 4);
+      acc[0] += u * lo.x; acc[1] += u * lo.y; acc[2] += u * lo.z; acc[3] += u * lo.w;
+      acc[4] += u * hi.x; acc[5] += u * hi.y; acc[6] += u * hi.z; acc[7] += u * hi.w;
+    }
+    *reinterpret_cast<uint4*>(dx + t * d + ch * 8) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
+// dWr[e, j] = sum over the rows r of e's segment, ascending, of
+// du_perm[r] * x[perm[r], j], fp32. Grid (ceil(d / 2048), E); 8 columns per
+// thread.
+__global__ __launch_bounds__(kRowT) void router_wgrad_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, const float* __restrict__ du_perm, int d,
+    float* __restrict__ dwr) {
+  const int e = blockIdx.y;
+  const int ch = blockIdx.x * kRowT + threadIdx.x;
+  if (ch * 8 >= d) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r1 = offsets[e + 1];
+  for (int r = offsets[e]; r < r1; ++r) {
+    const float u = du_perm[r];
+    const uint4 v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(perm[r]) * d + ch * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += u * __uint_as_float(w[j] << 16);
+      acc[2 * j + 1] += u * __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  float* out = dwr + static_cast<int64_t>(e) * d + ch * 8;
+  *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// ---- grouped GEMMs -----------------------------------------------------------
+
+// dH = dYp W2_e per routed group (rows of the group's segment) and dy Ws2 for
+// the shared group, from transposed weight copies W2_e^T [I, d] (so that the
+// contraction over d runs along rows, as in the forward kernels), then the
+// SwiGLU backward from the saved pre-activations: dG = [da | db].
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ GroupTables gt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r0 = tid >> 3;
+  load_group_tables(gt, a.tiles, a.offsets, a.E);
+  const int total = gt.total;
+  const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const i32x4_t rdyp = rsrc4(a.dyp, static_cast<uint32_t>(a.TK) * row_bytes);
+  const i32x4_t rdy = rsrc4(a.dy, static_cast<uint32_t>(a.T) * row_bytes);
+  const int nk = a.d / BK;
+  const int64_t ldg = 2 * static_cast<int64_t>(a.ldh);
+
+  auto next_ops = [&](int tile, int, StreamOps<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int rows_left = c.rows - c.m * C::BM;
+    const int rbase = (c.shared ? 0 : c.rbase) + c.m * C::BM;
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const int lr = r0 + p * C::RPP;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(rbase + lr) * row_bytes : kInvalidRow;
+    }
+    op.ra = c.shared ? rdy : rdyp;
+    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2t)
+                                 : static_cast<const uint16_t*>(a.w2t) +
+                                       static_cast<int64_t>(c.g) * a.I * a.d;
+    op.rb = rsrc4(W, static_cast<uint32_t>(Ig) * row_bytes);
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p) {
+      const int row = c.n * C::BN + r0 + p * C::RPP;
+      op.bo[p] = row < Ig ? static_cast<uint32_t>(row) * row_bytes : kInvalidRow;
+    }
+    swizzle_rows<C>(op.ao);
+    swizzle_rows<C>(op.bo);
+    op.nk = nk;
+  };
+  auto nk_of = [&](int) { return nk; };
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int rows_left = c.rows - c.m * C::BM;
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int row = wm * C::WM + mi * 32 + (lane & 31);
+      if (row >= rows_left) continue;
+      const uint16_t* gp = static_cast<const uint16_t*>(a.gu) + (hrow0 + row) * ldg;
+      uint16_t* dp = static_cast<uint16_t*>(a.dg) + (hrow0 + row) * ldg;
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = c.n * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (col >= Ig) continue;
+          const uint2 av = *reinterpret_cast<const uint2*>(gp + col);
+          const uint2 bv = *reinterpret_cast<const uint2*>(gp + Ig + col);
+          const uint32_t aw[2] = {av.x, av.y}, bw[2] = {bv.x, bv.y};
+          float da[4], db[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t ab = (j & 1) ? (aw[j >> 1] & 0xFFFF0000u) : (aw[j >> 1] << 16);
+            const uint32_t bb = (j & 1) ? (bw[j >> 1] & 0xFFFF0000u) : (bw[j >> 1] << 16);
+            const float x = __uint_as_float(ab), u = __uint_as_float(bb);
+            const float dh = acc[mi][nj][4 * g + j];
+            const float sg = 1.0f / (1.0f + __expf(-x));
+            da[j] = dh * u * (sg * (1.0f + x * (1.0f - sg)));
+            db[j] = dh * (x * sg);
+          }
+          *reinterpret_cast<uint2*>(dp + col) =
+              make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+          *reinterpret_cast<uint2*>(dp + Ig + col) =
+              make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
+        }
+    }
+  };
+  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
+}
+
+// Weight gradients out_g = A_g B_g^T (fp32) per group g: A_g rows m < M_g and
+// B_g rows n < N_g of the token-major operands at, bt (row stride ldp), over
+// the columns [poff[g], poff[g+1]) of segment g. Tiles: ceil(M/BM) x
+// ceil(N/BN) per group, n fastest; routed groups first, the shared group
+// last.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ int sp[kMaxGroups + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r0 = tid >> 3;
+  const int G = w.E + (w.shared ? 1 : 0);
+  for (int i = tid; i <= G; i += C::NT) sp[i] = w.poff[i];
+  __syncthreads();
+  const int tn = (w.N + C::BN - 1) / C::BN, tpr = ((w.M + C::BM - 1) / C::BM) * tn;
+  const int tns = (w.Ns + C::BN - 1) / C::BN;
+  const int total = w.E * tpr + (w.shared ? ((w.Ms + C::BM - 1) / C::BM) * tns : 0);
+  const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
+  const uint32_t row_bytes = static_cast<uint32_t>(w.ldp) * 2u;
+  const i32x4_t ra = rsrc4(w.at, static_cast<uint32_t>(w.a_rows) * row_bytes);
+  const i32x4_t rb = rsrc4(w.bt, static_cast<uint32_t>(w.b_rows) * row_bytes);
+
+  struct Coord {
+    int g, mt, nt, M, N;
+  };
+  auto coord = [&](int tile) {
+    Coord c;
+    if (tile < w.E * tpr) {
+      c.g = tile / tpr;
+      const int rem = tile - c.g * tpr;
+      c.mt = rem / tn;
+      c.nt = rem - c.mt * tn;
+      c.M = w.M;
+      c.N = w.N;
+    } else {
+      const int rem = tile - w.E * tpr;
+      c.g = w.E;
+      c.mt = rem / tns;
+      c.nt = rem - c.mt * tns;
+      c.M = w.Ms;
+      c.N = w.Ns;
+    }
+    return c;
+  };
+  auto next_ops = [&](int tile, int, StreamOps<C>& op) {
+    const Coord c = coord(tile);
+    const uint32_t kbase = static_cast<uint32_t>(sp[c.g]) * 2u;
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const int m = c.mt * C::BM + r0 + p * C::RPP;
+      op.ao[p] = m < c.M ? static_cast<uint32_t>(m) * row_bytes + kbase : kInvalidRow;
+    }
+#pragma unroll
+    for (int p = 0; p < C::B_LOADS; ++p) {
+      const int n = c.nt * C::BN + r0 + p * C::RPP;
+      op.bo[p] = n < c.N ? static_cast<uint32_t>(n) * row_bytes + kbase : kInvalidRow;
+    }
+    op.ra = ra;
+    op.rb = rb;
+    swizzle_rows<C>(op.ao);
+    swizzle_rows<C>(op.bo);
+    op.nk = (sp[c.g + 1] - sp[c.g]) / BK;
+  };
+  auto nk_of = [&](int tile) {
+    const Coord c = coord(tile);
+    return (sp[c.g + 1] - sp[c.g]) / BK;
+  };
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
+    const Coord c = coord(tile);
+    float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int m = c.mt * C::BM + wm * C::WM + mi * 32 + (lane & 31);
+      if (m >= c.M) continue;
+      float* orow = out + static_cast<int64_t>(m) * c.N;
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = c.nt * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (n >= c.N) continue;
+          const f32x16_t& v = acc[mi][nj];
+          *reinterpret_cast<float4*>(orow + n) =
+              make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        }
+    }
+  };
+  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
+}
+
+template <class K>
+int occupancy_of(K kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_bf16(const void* src, int64_t n_mats, int R, int C, void* dst,
+                                 hipStream_t s) {
+  if (n_mats == 0 || R == 0 || C == 0) return hipSuccess;
+  dim3 grid((C + kTr - 1) / kTr, (R + kTr - 1) / kTr, static_cast<unsigned>(n_mats));
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanT), 0, s, offsets, E, T,
+                     shared ? 1 : 0, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_major(const void* src, int64_t ld, const int32_t* perm, const void* src_s,
+                              int64_t ld_s, const int32_t* offsets, const int32_t* poff, int E,
+                              bool shared, int64_t T, int cols, int64_t ldp, void* dst,
+                              hipStream_t s) {
+  if (ldp == 0 || cols == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(ldp / kTr), static_cast<unsigned>(cols / kTr));
+  hipLaunchKernelGGL(token_major_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),
+                     ld, perm, static_cast<const uint16_t*>(src_s), ld_s, offsets, poff, E,
+                     E + (shared ? 1 : 0), T, cols, ldp, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gate(const void* dy, const void* yperm, const int32_t* idx,
+                           const int32_t* inv, const float* gate, const float* logits, int64_t T,
+                           int K, int E, int d, void* dyp, float* du, float* du_perm,
+                           hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_gate_kernel, dim3(static_cast<unsigned>(T)), dim3(kRowT), 0, s,
+                     static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(yperm), idx,
+                     inv, gate, logits, K, E, d, static_cast<uint16_t*>(dyp), du, du_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_combine(const void* dap, const void* das, const int32_t* inv,
+                              const int32_t* idx, const float* du, const float* wr, int64_t T,
+                              int K, int d, void* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3(static_cast<unsigned>(T)), dim3(kRowT), 0, s,
+                     static_cast<const uint16_t*>(dap), static_cast<const uint16_t*>(das), inv,
+                     idx, du, wr, K, d, static_cast<uint16_t*>(dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const void* x, const int32_t* perm, const int32_t* offsets,
+                               const float* du_perm, int E, int d, float* dwr, hipStream_t s) {
+  dim3 grid((d / 8 + kRowT - 1) / kRowT, E);
+  hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(kRowT), 0, s,
+                     static_cast<const uint16_t*>(x), perm, offsets, du_perm, d, dwr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s) {
+  using C = TilePrefill;
+  static int occ = 0;
+  if (!occ) occ = occupancy_of(dgrad2_bf16_kernel<C>, C::NT);
+  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
+  hipLaunchKernelGGL(dgrad2_bf16_kernel<C>, dim3(g), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s) {
+  using C = TilePrefill;
+  static int occ = 0;
+  if (!occ) occ = occupancy_of(wgrad_bf16_kernel<C>, C::NT);
+  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
+  hipLaunchKernelGGL(wgrad_bf16_kernel<C>, dim3(g), dim3(C::NT), 0, s, w);
+  return hipGetLastError();
+}
+
+}  // namespace dsmoe

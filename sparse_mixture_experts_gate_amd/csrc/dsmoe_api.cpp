@@ -305,7 +305,8 @@ moe_status run_gate(const moe_layer_desc* d, const void* x, const float* w_route
 moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
                    const int32_t* perm, const void* x_perm, const float* x_perm_scale,
                    const int32_t* offsets, void* y_perm, void* y_shared, void* ws,
-                   const FfnLayout& L, bool profile, bool planned, hipStream_t s) {
+                   const FfnLayout& L, bool profile, bool planned, hipStream_t s,
+                   void* h_out = nullptr, void* gu_out = nullptr) {
   if (d->T == 0) return MOE_OK;
   int32_t* tiles1 = at<int32_t>(ws, L.tiles1);
   int32_t* tiles2 = at<int32_t>(ws, L.tiles2);
@@ -331,8 +332,9 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   a.ws2 = w->ws2;
   a.w2_scale = w->w2_scale;
   a.ws2_scale = w->ws2_scale;
-  a.H = at<void>(ws, L.H);
+  a.H = h_out ? h_out : at<void>(ws, L.H);
   a.H_scale = at<float>(ws, L.Hs);
+  a.gu = gu_out;
   a.yperm = y_perm;
   a.yshared = y_shared;
   if (!planned)
@@ -360,6 +362,75 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
     HIP_TRY(launch_ffn_f32(a, s, mid), "expert ffn (fp32)");
   if (profile) HIP_TRY(prof_record(4, s), "profile event");
   return MOE_OK;
+}
+
+// ---- training ---------------------------------------------------------------
+
+// Upper bound of the padded token columns of the weight-gradient operands:
+// every routed segment rounds up to a multiple of 64 (an empty one keeps 64),
+// the shared segment too.
+int64_t wgrad_pmax(const moe_layer_desc* d) {
+  const int64_t TK = d->T * d->top_k;
+  const int64_t P = TK + 64 * int64_t(d->n_experts) + (d->shared_inter > 0 ? d->T + 63 : 0);
+  return ((P + 63) / 64) * 64;
+}
+
+moe_status validate_train(const moe_layer_desc* d) {
+  moe_status st = validate_desc(d);
+  if (st) return st;
+  if (d->act_dtype != MOE_DT_BF16 || d->w_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "training supports bf16 activations and weights only");
+  // 32-bit byte offsets of the backward's buffers
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  const int64_t TK = d->T * d->top_k;
+  const int64_t ldh = std::max(d->inter, d->shared_inter);
+  if (TK * d->d * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*K*d*2 must be < 2^31 bytes for training");
+  if ((TK + d->T) * 2 * ldh * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*2*max(I,Is)*2 must be < 2^31 bytes for training");
+  if (wgrad_pmax(d) * std::max<int64_t>(d->d, 2 * ldh) * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "the token-major gradient operands exceed 2^31 bytes");
+  return MOE_OK;
+}
+
+moe_status check_saved(const moe_layer_desc* d, const moe_saved* sv) {
+  if (!sv) return fail(MOE_ERR_INVALID_ARGUMENT, "saved is NULL");
+  return check_ptrs({{sv->logits, "saved.logits"}, {sv->topk_idx, "saved.topk_idx"},
+                     {sv->topk_gate, "saved.topk_gate"}, {sv->counts, "saved.counts"},
+                     {sv->offsets, "saved.offsets"}, {sv->perm, "saved.perm"},
+                     {sv->inv, "saved.inv"}, {sv->h, "saved.h"}, {sv->gu, "saved.gu"},
+                     {sv->y_perm, "saved.y_perm"}});
+}
+
+struct BwdLayout {
+  int ldh;
+  int64_t pmax;
+  size_t tiles_h, tiles_d, poff, dyp, du, du_perm, dg, dap, das, xt, dyt, ht, dgt, bytes;
+};
+
+BwdLayout bwd_layout(const moe_layer_desc* d) {
+  BwdLayout L{};
+  const int64_t T = d->T, TK = d->T * d->top_k;
+  const int E = d->n_experts;
+  L.ldh = std::max(d->inter, d->shared_inter);
+  L.pmax = wgrad_pmax(d);
+  const int64_t hrows = TK + (d->shared_inter > 0 ? T : 0);
+  Carver c;
+  L.tiles_h = c.take(sizeof(int32_t) * (E + 2));
+  L.tiles_d = c.take(sizeof(int32_t) * (E + 2));
+  L.poff = c.take(sizeof(int32_t) * (E + 2));
+  L.dyp = c.take(size_t(TK) * d->d * 2);
+  L.du = c.take(sizeof(float) * size_t(TK));
+  L.du_perm = c.take(sizeof(float) * size_t(TK));
+  L.dg = c.take(size_t(hrows) * 2 * L.ldh * 2);
+  L.dap = c.take(size_t(TK) * d->d * 2);
+  L.das = c.take(d->shared_inter > 0 ? size_t(T) * d->d * 2 : 0);
+  L.xt = c.take(size_t(d->d) * L.pmax * 2);
+  L.dyt = c.take(size_t(d->d) * L.pmax * 2);
+  L.ht = c.take(size_t(L.ldh) * L.pmax * 2);
+  L.dgt = c.take(size_t(2 * L.ldh) * L.pmax * 2);
+  L.bytes = c.off;
+  return L;
 }
 
 }  // namespace
@@ -629,6 +700,252 @@ moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, 
   moe_status st = check_ptrs({{src, "src"}, {q, "q"}, {scale, "scale"}});
   if (st) return st;
   HIP_TRY(launch_quant_rows(src, src_dtype, nullptr, n, cols, q, scale, stream), "quantize rows");
+  return MOE_OK;
+}
+
+moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const float* w_router,
+                             const float* bias, const moe_weights* w, void* y,
+                             const moe_saved* sv, int32_t* near_tie, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status st = validate_train(desc);
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (!sv) return fail(MOE_ERR_INVALID_ARGUMENT, "saved is NULL");
+  if (desc->T == 0) {
+    st = check_ptrs({{sv->counts, "saved.counts"}, {sv->offsets, "saved.offsets"}});
+    if (st) return st;
+    st = zero_counts(desc, sv->counts, near_tie, stream);
+    if (st) return st;
+    HIP_TRY(launch_fill_i32(sv->offsets, desc->n_experts + 1, 0, stream), "zero offsets");
+    return MOE_OK;
+  }
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {bias, "bias"}, {y, "y"}, {ws, "ws"}});
+  if (st) return st;
+  st = check_saved(desc, sv);
+  if (st) return st;
+  st = check_opt({{near_tie, "near_tie"}});
+  if (st) return st;
+  const FwdLayout L = fwd_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_forward_train needs %zu workspace bytes, got %zu",
+                L.bytes, ws_bytes);
+  void* gws = at<void>(ws, L.gate_base);
+  void* fws = at<void>(ws, L.ffn_base);
+  void* yshared = desc->shared_inter > 0 ? at<void>(ws, L.yshared) : nullptr;
+  st = run_gate(desc, x, w_router, bias, sv->logits, sv->topk_idx, sv->topk_gate, sv->counts,
+                near_tie, gws, L.gate, stream);
+  if (st) return st;
+  HIP_TRY(launch_plan(sv->counts, nullptr, sv->offsets, at<int32_t>(fws, L.ffn.tiles1),
+                      at<int32_t>(fws, L.ffn.tiles2), plan_params(desc, L.ffn.tiling), stream),
+          "plan");
+  HIP_TRY(launch_permute(sv->topk_idx, sv->offsets, desc->T, desc->top_k, desc->n_experts,
+                         sv->perm, sv->inv, stream),
+          "permute");
+  st = run_ffn(desc, w, x, sv->perm, nullptr, nullptr, sv->offsets, sv->y_perm, yshared, fws,
+               L.ffn, false, true, stream, sv->h, sv->gu);
+  if (st) return st;
+  HIP_TRY(launch_combine(sv->y_perm, sv->inv, sv->topk_gate, yshared, y, desc->T, desc->top_k,
+                         desc->d, desc->act_dtype, stream),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_transpose_weights(const moe_layer_desc* desc, const moe_weights* w,
+                                 const moe_weights_t* wt, hipStream_t stream) {
+  moe_status st = validate_train(desc);
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (!wt) return fail(MOE_ERR_INVALID_ARGUMENT, "wt is NULL");
+  st = check_ptrs({{wt->w13_t, "w13_t"}, {wt->w2_t, "w2_t"}});
+  if (st) return st;
+  const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
+  if (Is > 0) {
+    st = check_ptrs({{wt->ws13_t, "ws13_t"}, {wt->ws2_t, "ws2_t"}});
+    if (st) return st;
+  }
+  HIP_TRY(launch_transpose_bf16(w->w13, E, 2 * I, d, wt->w13_t, stream), "transpose w13");
+  HIP_TRY(launch_transpose_bf16(w->w2, E, d, I, wt->w2_t, stream), "transpose w2");
+  if (Is > 0) {
+    HIP_TRY(launch_transpose_bf16(w->ws13, 1, 2 * Is, d, wt->ws13_t, stream), "transpose ws13");
+    HIP_TRY(launch_transpose_bf16(w->ws2, 1, d, Is, wt->ws2_t, stream), "transpose ws2");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes) {
+  moe_status st = validate_train(desc);
+  if (st) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = bwd_layout(desc).bytes;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* w_router,
+                        const moe_weights_t* wt, const moe_saved* sv, const void* dy, void* dx,
+                        const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_train(desc);
+  if (st) return st;
+  const int64_t T = desc->T, TK = T * desc->top_k;
+  const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
+  const int K = desc->top_k;
+  const bool shared = Is > 0;
+  if (!g) return fail(MOE_ERR_INVALID_ARGUMENT, "grads is NULL");
+  st = check_ptrs({{g->dw13, "dw13"}, {g->dw2, "dw2"}, {g->dw_router, "dw_router"}});
+  if (st) return st;
+  if (shared) {
+    st = check_ptrs({{g->dws13, "dws13"}, {g->dws2, "dws2"}});
+    if (st) return st;
+  }
+  if (T == 0) {
+    // no token: every weight gradient is zero
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw13), int64_t(E) * 2 * I * d, 0, stream),
+            "zero dw13");
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw2), int64_t(E) * d * I, 0, stream),
+            "zero dw2");
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw_router), int64_t(E) * d, 0, stream),
+            "zero dw_router");
+    if (shared) {
+      HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dws13), int64_t(2) * Is * d, 0, stream),
+              "zero dws13");
+      HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dws2), int64_t(d) * Is, 0, stream),
+              "zero dws2");
+    }
+    return MOE_OK;
+  }
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {dy, "dy"}, {dx, "dx"}, {ws, "ws"}});
+  if (st) return st;
+  if (!wt) return fail(MOE_ERR_INVALID_ARGUMENT, "wt is NULL");
+  st = check_ptrs({{wt->w13_t, "w13_t"}, {wt->w2_t, "w2_t"}});
+  if (st) return st;
+  if (shared) {
+    st = check_ptrs({{wt->ws13_t, "ws13_t"}, {wt->ws2_t, "ws2_t"}});
+    if (st) return st;
+  }
+  st = check_saved(desc, sv);
+  if (st) return st;
+  const BwdLayout L = bwd_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_backward needs %zu workspace bytes, got %zu",
+                L.bytes, ws_bytes);
+  int32_t* tiles_h = at<int32_t>(ws, L.tiles_h);
+  int32_t* tiles_d = at<int32_t>(ws, L.tiles_d);
+  int32_t* poff = at<int32_t>(ws, L.poff);
+  void* dyp = at<void>(ws, L.dyp);
+  float* du = at<float>(ws, L.du);
+  float* du_perm = at<float>(ws, L.du_perm);
+  void* dgb = at<void>(ws, L.dg);
+  void* dap = at<void>(ws, L.dap);
+  void* das = shared ? at<void>(ws, L.das) : nullptr;
+  void* xt = at<void>(ws, L.xt);
+  void* dyt = at<void>(ws, L.dyt);
+  void* ht = at<void>(ws, L.ht);
+  void* dgt = at<void>(ws, L.dgt);
+  const int ldh = L.ldh;
+
+  // tile tables: 128-row tiles over 256-column tiles of Ig (dgrad2) and d (dgrad1)
+  PlanParams pp{};
+  pp.T = T;
+  pp.E = E;
+  pp.K = K;
+  pp.d = d;
+  pp.I = I;
+  pp.Is = Is;
+  pp.bm1 = 128;
+  pp.bnh1 = 256;
+  pp.bm2 = 128;
+  pp.bn2 = 256;
+  HIP_TRY(launch_plan(nullptr, sv->offsets, nullptr, tiles_h, tiles_d, pp, stream), "plan");
+  HIP_TRY(launch_wgrad_plan(sv->offsets, E, T, shared, poff, stream), "wgrad plan");
+  HIP_TRY(launch_bwd_gate(dy, sv->y_perm, sv->topk_idx, sv->inv, sv->topk_gate, sv->logits, T, K,
+                          E, d, dyp, du, du_perm, stream),
+          "gate gradients");
+  BwdArgs b{};
+  b.offsets = sv->offsets;
+  b.tiles = tiles_h;
+  b.T = T;
+  b.TK = TK;
+  b.E = E;
+  b.d = d;
+  b.I = I;
+  b.Is = Is;
+  b.ldh = ldh;
+  b.dyp = dyp;
+  b.dy = dy;
+  b.w2t = wt->w2_t;
+  b.ws2t = wt->ws2_t;
+  b.gu = sv->gu;
+  b.dg = dgb;
+  HIP_TRY(launch_dgrad2_bf16(b, stream), "dgrad of the down projection");
+  FfnArgs a{};
+  a.offsets = sv->offsets;
+  a.tiles2 = tiles_d;
+  a.T = T;
+  a.TK = TK;
+  a.E = E;
+  a.d = d;
+  a.I = 2 * I;
+  a.Is = 2 * Is;
+  a.ldh = 2 * ldh;
+  a.H = dgb;
+  a.w2 = wt->w13_t;
+  a.ws2 = wt->ws13_t;
+  a.yperm = dap;
+  a.yshared = das;
+  HIP_TRY(launch_gemm2_bf16(a, stream), "dgrad of the gate/up projection");
+  HIP_TRY(launch_bwd_combine(dap, das, sv->inv, sv->topk_idx, du, w_router, T, K, d, dx, stream),
+          "input gradient");
+  HIP_TRY(launch_router_wgrad(x, sv->perm, sv->offsets, du_perm, E, d, g->dw_router, stream),
+          "router weight gradient");
+  // token-major operands of the weight-gradient GEMMs
+  const int64_t P = L.pmax;
+  const uint16_t* h16 = static_cast<const uint16_t*>(sv->h);
+  const uint16_t* dg16 = static_cast<const uint16_t*>(dgb);
+  HIP_TRY(launch_token_major(x, d, sv->perm, x, d, sv->offsets, poff, E, shared, T, d, P, xt,
+                             stream),
+          "token-major x");
+  HIP_TRY(launch_token_major(dyp, d, nullptr, dy, d, sv->offsets, poff, E, shared, T, d, P, dyt,
+                             stream),
+          "token-major dy");
+  HIP_TRY(launch_token_major(h16, ldh, nullptr, h16 + TK * ldh, ldh, sv->offsets, poff, E, shared,
+                             T, ldh, P, ht, stream),
+          "token-major h");
+  HIP_TRY(launch_token_major(dg16, 2 * ldh, nullptr, dg16 + TK * 2 * ldh, 2 * ldh, sv->offsets,
+                             poff, E, shared, T, 2 * ldh, P, dgt, stream),
+          "token-major dG");
+  WgradArgs w1{};
+  w1.poff = poff;
+  w1.E = E;
+  w1.shared = shared;
+  w1.ldp = P;
+  w1.at = dgt;
+  w1.bt = xt;
+  w1.a_rows = 2 * ldh;
+  w1.b_rows = d;
+  w1.M = 2 * I;
+  w1.N = d;
+  w1.Ms = 2 * Is;
+  w1.Ns = d;
+  w1.out = g->dw13;
+  w1.out_s = g->dws13;
+  HIP_TRY(launch_wgrad_bf16(w1, stream), "weight gradient of the gate/up projection");
+  WgradArgs w2{};
+  w2.poff = poff;
+  w2.E = E;
+  w2.shared = shared;
+  w2.ldp = P;
+  w2.at = dyt;
+  w2.bt = ht;
+  w2.a_rows = d;
+  w2.b_rows = ldh;
+  w2.M = d;
+  w2.N = I;
+  w2.Ms = d;
+  w2.Ns = Is;
+  w2.out = g->dw2;
+  w2.out_s = g->dws2;
+  HIP_TRY(launch_wgrad_bf16(w2, stream), "weight gradient of the down projection");
   return MOE_OK;
 }
 

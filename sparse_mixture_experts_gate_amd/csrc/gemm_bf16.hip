@@ -17,85 +17,11 @@
 #include "device_common.h"
 #include "internal.h"
 #include "tile_schedule.h"
+#include "gemm_bf16_core.h"
 
 namespace dsmoe {
 
 namespace {
-
-constexpr int BK = 64;  // k elements per stage: 128 bytes per row
-
-// BM x BN output tile in waves of WM x WN; NST LDS stages in the load ring
-// (loads run NST - 1 k-steps ahead).
-template <int BM_, int BN_, int WM_, int WN_, int NST_ = 3>
-struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_;
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int NWAVES = WAVES_M * WAVES_N;
-  static constexpr int NT = NWAVES * 64;
-  static constexpr int MI = WM / 32, NJ = WN / 32;
-  static constexpr int RPP = NT / 8;  // rows covered by one pass of 16-byte loads
-  static constexpr int A_LOADS = BM / RPP;
-  static constexpr int B_LOADS = BN / RPP;
-  static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
-  // waves per SIMD the register budget is sized for
-  static constexpr int MINW = (WM * WN >= 64 * 128) ? 1 : 2;
-  static constexpr int LDS_ELEMS = NST * STAGE;
-  static_assert(NST >= 3, "loads run at least two steps ahead");
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA sub-tiles");
-};
-
-using TilePrefill = Tile<128, 256, 64, 64>;  // 8 waves, 144 KB LDS
-// decode streams weights: one 2-wave workgroup per CU with a 7-stage ring
-// keeps six steps (120 KB) of loads in flight per CU
-using TileDecode = Tile<32, 128, 32, 64, 7>;
-
-// LDS element offset of 16-byte chunk `ch` (0..7) of row `r`. The chunk is
-// XOR-swizzled with (r >> 1) & 7: the 16 lanes that one 128-bit LDS access
-// serves together read 16 consecutive rows at one logical chunk, and with two
-// 128-byte rows per 64-bank line this spreads them over all 64 banks.
-__device__ __forceinline__ int lds_off(int r, int ch) {
-  return r * BK + ((ch ^ ((r >> 1) & 7)) << 3);
-}
-
-template <class C, bool SWIGLU>
-__device__ __forceinline__ int b_local_row(int wn, int nj) {
-  if constexpr (SWIGLU) {
-    constexpr int half = C::BN / 2, hw = C::WN / 2, njh = C::NJ / 2;
-    return nj < njh ? wn * hw + nj * 32 : half + wn * hw + (nj - njh) * 32;
-  } else {
-    return wn * C::WN + nj * 32;
-  }
-}
-
-// Global byte offsets of one thread's rows with the chunk swizzle folded in:
-// lane (row r, 16-byte position ch) fetches logical chunk ch ^ swizzle(r), so
-// the LDS image of a stage is the swizzled layout lds_off describes.
-template <class C, int N>
-__device__ __forceinline__ void swizzle_rows(uint32_t (&o)[N]) {
-  const int ch = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int p = 0; p < N; ++p)
-    o[p] += static_cast<uint32_t>((ch ^ (((r0 + p * C::RPP) >> 1) & 7)) * 16);
-}
-
-// Issues one k-step of A and B rows (byte offsets ao, bo plus ka, kb) from
-// global memory straight into ring stage st: no registers hold tiles in flight
-// and no LDS store instructions are issued. This wave's 8 rows of each load
-// pass start at row 8 * wave.
-template <class C>
-__device__ __forceinline__ void stage_issue(uint32_t lds0, int st, int wave, i32x4_t ra,
-                                            const uint32_t (&ao)[C::A_LOADS], uint32_t ka,
-                                            i32x4_t rb, const uint32_t (&bo)[C::B_LOADS],
-                                            uint32_t kb) {
-  const uint32_t a_base =
-      __builtin_amdgcn_readfirstlane(lds0 + (st * C::STAGE + wave * 8 * BK) * 2);
-  const uint32_t b_base = a_base + C::BM * BK * 2;
-#pragma unroll
-  for (int p = 0; p < C::A_LOADS; ++p) dma16(ra, ao[p] + ka, a_base + p * C::RPP * BK * 2);
-#pragma unroll
-  for (int p = 0; p < C::B_LOADS; ++p) dma16(rb, bo[p] + kb, b_base + p * C::RPP * BK * 2);
-}
 
 // acc += one 64-wide k-step of the tile in ring stage st. Within the step the
 // LDS fragments of the next 16-wide sub-step are read while the current one
@@ -140,20 +66,6 @@ __device__ __forceinline__ void stage_mma(const uint16_t* lds, int st, int wm, i
     }
   }
 }
-
-template <class C>
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::MI][C::NJ]) {
-#pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
-}
-
-// loads of the NST - 2 newest steps that may stay in flight at a wait
-template <class C>
-constexpr int kInflight = (C::A_LOADS + C::B_LOADS) * (C::NST - 2);
 
 // acc = A * B^T over k in [k_begin, k_end) (multiples of 64) for one tile.
 // Operands come from buffers (ra, rb) through a 32-bit byte offset per thread
@@ -211,157 +123,14 @@ __device__ __forceinline__ void gemm_tile(uint16_t* lds, i32x4_t ra,
   __syncthreads();
 }
 
-// Operands of one tile's k-stream: buffer resources, per-thread row byte
-// offsets (swizzle folded in) and the number of 64-wide k-steps.
-template <class C>
-struct StreamOps {
-  i32x4_t ra, rb;
-  uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
-  int nk;
-};
-
-// The persistent grouped GEMMs run every tile of a workgroup (tiles first,
-// first + nb, ... below total) as one k-stream through the NST-stage ring:
-// the first steps of a tile are loaded during the previous tile's last
-// steps, so the ring never drains at a tile boundary, and a tile's epilogue
-// (stores straight from registers, no LDS) runs while the next tile's first
-// stages land.
-//   next_ops(tile, index, ops): operands of the index-th tile of the issue
-//     side (called once per tile, in order, after the previous tile's last
-//     step was issued);
-//   nk_of(tile): k-steps of a tile;
-//   epilogue(tile, acc): stores a finished tile (acc in the SWAP layout).
-// Vector-memory waits count only this stream's loads: every step issues the
-// same loads (once the tiles run out, the last step is loaded again into
-// stages nobody reads), so with loads NST - 1 steps ahead at most the newest
-// kInflight<C> may be in flight when a stage is read; extra loads or stores
-// issued in between only make such a wait stronger.
-// Within a step, the fragments of sub-step kk + 1 are read while sub-step kk
-// multiplies; the step's barrier sits before its last sub-step, whose
-// fragments are already in registers, so that the next stage's first
-// fragments are read while those MFMAs run.
-template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue>
-__device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
-                                            NextOps&& next_ops, NkOf&& nk_of,
-                                            Epilogue&& epilogue) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  constexpr int NST = C::NST;
-  constexpr int INFLIGHT = kInflight<C>;
-  static_assert(INFLIGHT <= 63, "vmcnt range");
-  static_assert(BK / 16 == 4, "four MFMA sub-steps per k-step");
-  const uint32_t lds0 = lds_addr(lds);
-
-  // issue side
-  StreamOps<C> op;
-  int ti = first, ki = 0, index = 0;
-  bool more = true;
-  next_ops(ti, index, op);
-  auto issue = [&](int st) {
-    const uint32_t kb = static_cast<uint32_t>(ki) * (BK * 2);
-    stage_issue<C>(lds0, st, wave, op.ra, op.ao, kb, op.rb, op.bo, kb);
-    if (more) ++ki;
-  };
-  auto advance = [&]() {
-    if (!more || ki < op.nk) return;
-    ki = 0;
-    ti += nb;
-    if (ti < total) {
-      next_ops(ti, ++index, op);
-    } else {
-      more = false;
-      ki = op.nk - 1;
-    }
-  };
-
-  // fragments of sub-step kk of stage st
-  bf16x8_t af[2][C::MI], bfr[2][C::NJ];
-  auto fetch = [&](int st, int kk, int buf) {
-    const uint16_t* As = lds + st * C::STAGE;
-    const uint16_t* Bs = As + C::BM * BK;
-    const int chk = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj)
-      bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
-          Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
-          As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
-  };
-  f32x16_t acc[C::MI][C::NJ];
-  // the weight fragment goes first: acc holds the transposed tile
-  auto mma = [&](int buf) {
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][nj], af[buf][mi],
-                                                              acc[mi][nj], 0, 0, 0);
-  };
-
-#pragma unroll
-  for (int j = 0; j < NST - 1; ++j) {
-    issue(j);
-    advance();
-  }
-  vm_wait<INFLIGHT>();  // stage 0 has landed
-  lds_barrier();
-
-  // compute side
-  int st = 0, st_issue = NST - 1;
-  fetch(st, 0, 0);
-  for (int tc = first; tc < total; tc += nb) {
-    zero_acc<C>(acc);
-    const int nkc = nk_of(tc);
-    for (int kc = 0; kc < nkc; ++kc) {
-      issue(st_issue);  // into the stage read in the previous step
-      fetch(st, 1, 1);
-      // fragment reads go out before the MFMAs that do not need them (the
-      // scheduler would otherwise reuse their registers and serialize)
-      __builtin_amdgcn_sched_barrier(0);
-      mma(0);
-      advance();
-      fetch(st, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(1);
-      fetch(st, 3, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(0);
-      // this wave's part of the next stage has landed; the barrier makes
-      // every wave's part visible and frees the stage whose last fragments
-      // are now in registers
-      vm_wait<INFLIGHT>();
-      lds_barrier();
-      st = st == NST - 1 ? 0 : st + 1;
-      st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
-      fetch(st, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(1);
-    }
-    epilogue(tc, acc);
-  }
-  // the reloads past the last step land before the workgroup ends
-  vm_wait<0>();
-}
-
-// Row (within the tile) of accumulator element r of a 32x32 sub-tile, for
-// this lane; the lane's column is lane % 32.
-__device__ __forceinline__ int acc_row(int lane, int r) {
-  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
-// Four bf16 values as one 8-byte word.
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-}
 
 // H = silu(A W1^T) * (A W3^T) per group. Routed rows of A are gathered
 // through perm: the token indices of a tile are brought into an LDS slot by
 // the same asynchronous loads as the operands, one tile ahead, so that the
-// tile loop issues no compiler-visible global loads.
-template <class C>
+// tile loop issues no compiler-visible global loads. TRAIN also stores the
+// pre-activations (bf16) for the backward: row r of a.gu holds A W1^T in
+// columns [0, Ig) and A W3^T in [Ig, 2 Ig), row stride 2 ldh.
+template <class C, bool TRAIN>
 __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   __shared__ GroupTables gt;
@@ -469,6 +238,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
               pack_bf16x4(silu_f32(gv[4 * g]) * uv[4 * g], silu_f32(gv[4 * g + 1]) * uv[4 * g + 1],
                           silu_f32(gv[4 * g + 2]) * uv[4 * g + 2],
                           silu_f32(gv[4 * g + 3]) * uv[4 * g + 3]);
+          if constexpr (TRAIN) {
+            uint16_t* gp = static_cast<uint16_t*>(a.gu) + (hrow0 + row) * 2 * a.ldh + col;
+            *reinterpret_cast<uint2*>(gp) =
+                pack_bf16x4(gv[4 * g], gv[4 * g + 1], gv[4 * g + 2], gv[4 * g + 3]);
+            *reinterpret_cast<uint2*>(gp + Ig) =
+                pack_bf16x4(uv[4 * g], uv[4 * g + 1], uv[4 * g + 2], uv[4 * g + 3]);
+          }
         }
     }
   };
@@ -627,16 +403,16 @@ int occupancy_blocks(K kernel, int threads) {
   return nb;
 }
 
-template <class C1, class C2>
+template <class C1, class C2, bool TRAIN>
 hipError_t launch_ffn_bf16_cfg(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
-  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C1>, C1::NT);
+  if (!occ1) occ1 = occupancy_blocks(ffn1_bf16_kernel<C1, TRAIN>, C1::NT);
   if (!occ2) occ2 = occupancy_blocks(ffn2_bf16_kernel<C2>, C2::NT);
   const int cus = device_cu_count();
   // persistent grids, multiples of 8 for the XCD remap
   const int g1 = ((cus * occ1 + 7) / 8) * 8;
   const int g2 = ((cus * occ2 + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn1_bf16_kernel<C1>), dim3(g1), dim3(C1::NT), 0, s, a);
+  hipLaunchKernelGGL((ffn1_bf16_kernel<C1, TRAIN>), dim3(g1), dim3(C1::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;
@@ -661,8 +437,21 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid) {
-  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode>(a, s, mid);
-  return launch_ffn_bf16_cfg<TilePrefill, TilePrefill>(a, s, mid);
+  if (a.gu) {
+    if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode, true>(a, s, mid);
+    return launch_ffn_bf16_cfg<TilePrefill, TilePrefill, true>(a, s, mid);
+  }
+  if (t.variant == 1) return launch_ffn_bf16_cfg<TileDecode, TileDecode, false>(a, s, mid);
+  return launch_ffn_bf16_cfg<TilePrefill, TilePrefill, false>(a, s, mid);
+}
+
+hipError_t launch_gemm2_bf16(const FfnArgs& a, hipStream_t s) {
+  using C = TilePrefill;
+  static int occ = 0;
+  if (!occ) occ = occupancy_blocks(ffn2_bf16_kernel<C>, C::NT);
+  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
+  hipLaunchKernelGGL((ffn2_bf16_kernel<C>), dim3(g), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
 }
 
 int router_splits(int64_t T, int d, int E, int act_dtype) {

@@ -77,6 +77,7 @@ struct FfnArgs {
   const float* ws13_scale;
   void* H;                 // [TK + T, ldh]
   float* H_scale;          // fp8: [TK + T, ldh/128]
+  void* gu;                // bf16 training forward: pre-activations [TK + T, 2 ldh], or NULL
   // GEMM2
   const void* w2;
   const void* ws2;
@@ -97,7 +98,57 @@ GemmTiling choose_tiling_fp8(double rows_per_expert);
 // `mid` (may be NULL) is recorded between the gate/up and the down GEMM.
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s, hipEvent_t mid);
+// The down-projection kernel alone with 128 x 256 tiles over a.tiles2:
+// per group, rows of a.H [.., ldh] (K = a.I, or a.Is for the shared group)
+// times the group's [d, K] weight a.w2 (a.ws2) -> a.yperm / a.yshared.
+hipError_t launch_gemm2_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
+
+// ---- backward (backward.hip), bf16 activations and weights ------------------
+struct BwdArgs {
+  const int32_t* offsets;  // [E+1]
+  const int32_t* tiles;    // [E+2] tile prefix for 128-row tiles over Ig/256 column tiles
+  int64_t T, TK;
+  int E, d, I, Is, ldh;
+  const void* dyp;         // [TK, d] gated output gradients of the routed rows
+  const void* dy;          // [T, d] output gradient (shared rows)
+  const void* w2t;         // [E, I, d] transposed down projections
+  const void* ws2t;        // [Is, d]
+  const void* gu;          // [TK + T, 2 ldh] saved pre-activations
+  void* dg;                // [TK + T, 2 ldh] OUT: [da | db]
+};
+struct WgradArgs {
+  const int32_t* poff;     // [G+1] segment starts in the token-major operands
+  int E;
+  bool shared;             // a shared group follows the E routed ones
+  int64_t ldp;             // row stride (elements) of at and bt
+  const void* at;          // [a_rows, ldp] bf16
+  const void* bt;          // [b_rows, ldp] bf16
+  int64_t a_rows, b_rows;
+  int M, N;                // routed group output [M, N]
+  int Ms, Ns;              // shared group output [Ms, Ns]
+  float* out;              // [E, M, N]
+  float* out_s;            // [Ms, Ns]
+};
+hipError_t launch_transpose_bf16(const void* src, int64_t n_mats, int R, int C, void* dst,
+                                 hipStream_t s);
+hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
+                             hipStream_t s);
+hipError_t launch_token_major(const void* src, int64_t ld, const int32_t* perm, const void* src_s,
+                              int64_t ld_s, const int32_t* offsets, const int32_t* poff, int E,
+                              bool shared, int64_t T, int cols, int64_t ldp, void* dst,
+                              hipStream_t s);
+hipError_t launch_bwd_gate(const void* dy, const void* yperm, const int32_t* idx,
+                           const int32_t* inv, const float* gate, const float* logits, int64_t T,
+                           int K, int E, int d, void* dyp, float* du, float* du_perm,
+                           hipStream_t s);
+hipError_t launch_bwd_combine(const void* dap, const void* das, const int32_t* inv,
+                              const int32_t* idx, const float* du, const float* wr, int64_t T,
+                              int K, int d, void* dx, hipStream_t s);
+hipError_t launch_router_wgrad(const void* x, const int32_t* perm, const int32_t* offsets,
+                               const float* du_perm, int E, int d, float* dwr, hipStream_t s);
+hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
 // ---- elementwise (elementwise.hip) -----------------------------------------
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,

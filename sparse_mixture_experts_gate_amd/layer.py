@@ -81,3 +81,68 @@ class MoELayer:
     def bias_update(self, counts: torch.Tensor, T: int, gamma: float | None = None, stream=None):
         L.moe_bias_update(self.desc(T), counts, self.wl.gamma if gamma is None else gamma,
                           self.bias, stream)
+
+    # ---- training (bf16 activations and weights) ----------------------------
+    def alloc_saved(self, T: int) -> dict:
+        wl, dev = self.wl, self.device
+        TK = T * wl.K
+        ldh = max(wl.I, wl.Is)
+        hrows = TK + (T if wl.Is else 0)
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        return {"logits": torch.empty(T, wl.E, dtype=f32, device=dev),
+                "topk_idx": torch.empty(T, wl.K, dtype=i32, device=dev),
+                "topk_gate": torch.empty(T, wl.K, dtype=f32, device=dev),
+                "counts": torch.empty(wl.E, dtype=i32, device=dev),
+                "offsets": torch.empty(wl.E + 1, dtype=i32, device=dev),
+                "perm": torch.empty(TK, dtype=i32, device=dev),
+                "inv": torch.empty(T, wl.K, dtype=i32, device=dev),
+                "h": torch.empty(hrows, ldh, dtype=bf, device=dev),
+                "gu": torch.empty(hrows, 2 * ldh, dtype=bf, device=dev),
+                "y_perm": torch.empty(TK, wl.d, dtype=bf, device=dev)}
+
+    def forward_train(self, x: torch.Tensor, saved: dict | None = None, stream=None) -> tuple:
+        """y [T, d] and the tensors the backward needs (moe_forward_train)."""
+        T = x.shape[0]
+        saved = self.alloc_saved(T) if saved is None else saved
+        y = torch.empty(T, self.wl.d, dtype=torch.bfloat16, device=self.device)
+        near_tie = torch.empty(1, dtype=torch.int32, device=self.device)
+        L.moe_forward_train(self.desc(T), x, self.w_router, self.bias, self.weights, y,
+                            L.make_saved(**saved), near_tie, self.workspace(T), stream)
+        return y, saved
+
+    def transpose_weights(self, stream=None) -> dict:
+        """Transposed bf16 weight copies for the backward (moe_transpose_weights)."""
+        wl, dev, bf = self.wl, self.device, torch.bfloat16
+        wt = {"w13_t": torch.empty(wl.E, wl.d, 2 * wl.I, dtype=bf, device=dev),
+              "w2_t": torch.empty(wl.E, wl.I, wl.d, dtype=bf, device=dev),
+              "ws13_t": torch.empty(wl.d, 2 * wl.Is, dtype=bf, device=dev) if wl.Is else None,
+              "ws2_t": torch.empty(wl.Is, wl.d, dtype=bf, device=dev) if wl.Is else None}
+        L.moe_transpose_weights(self.desc(0), self.weights, L.make_weights_t(**wt), stream)
+        self._wt = wt
+        return wt
+
+    def alloc_grads(self) -> dict:
+        wl, dev, f32 = self.wl, self.device, torch.float32
+        return {"dw13": torch.empty(wl.E, 2 * wl.I, wl.d, dtype=f32, device=dev),
+                "dw2": torch.empty(wl.E, wl.d, wl.I, dtype=f32, device=dev),
+                "dws13": torch.empty(2 * wl.Is, wl.d, dtype=f32, device=dev) if wl.Is else None,
+                "dws2": torch.empty(wl.d, wl.Is, dtype=f32, device=dev) if wl.Is else None,
+                "dw_router": torch.empty(wl.E, wl.d, dtype=f32, device=dev)}
+
+    def backward_workspace(self, T: int) -> torch.Tensor:
+        need = L.moe_backward_workspace_size(self.desc(T))
+        if getattr(self, "_bws", None) is None or self._bws.numel() < need:
+            self._bws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._bws
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, saved: dict, wt: dict | None = None,
+                 grads: dict | None = None, stream=None) -> tuple:
+        """dx [T, d] bf16 and the fp32 weight gradients (moe_backward)."""
+        T = x.shape[0]
+        wt = self._wt if wt is None else wt
+        grads = self.alloc_grads() if grads is None else grads
+        dx = torch.empty(T, self.wl.d, dtype=torch.bfloat16, device=self.device)
+        L.moe_backward(self.desc(T), x, self.w_router, L.make_weights_t(**wt),
+                       L.make_saved(**saved), dy, dx, L.make_grads(**grads),
+                       self.backward_workspace(T), stream)
+        return dx, grads

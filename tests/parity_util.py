@@ -21,6 +21,16 @@ def row_rel_err(y, ref) -> float:
     return float((num / den).max())
 
 
+def mat_rel_err(y, ref) -> float:
+    """max|y - ref| / max|ref| over a whole matrix. Used for weight gradients:
+    each entry is a sum over tokens whose terms cancel, so a row of one can be
+    small next to its terms and the row-normalized metric would measure the
+    cancellation rather than the arithmetic."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(y - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
 class LazyHost:
     """Indexable host view of a device tensor [E, ...]: expert e is copied to
     the host (as fp32) when the oracle asks for it, and not kept."""

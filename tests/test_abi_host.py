@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(L):
         "moe_workspace_size", "moe_gate", "moe_route_from_logits", "moe_permute",
         "moe_expert_ffn", "moe_combine", "moe_bias_update", "deepseek_moe_forward",
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
-        "moe_last_error", "moe_abi_version", "moe_profile_events"}
+        "moe_last_error", "moe_abi_version", "moe_profile_events", "moe_forward_train",
+        "moe_transpose_weights", "moe_backward_workspace_size", "moe_backward"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
@@ -125,3 +126,44 @@ def test_product_path_has_no_oracle_import():
     code = ("import sys; import sparse_mixture_experts_gate_amd as m; "
             "assert 'oracle' not in sys.modules and not any(k.startswith('oracle.') for k in sys.modules)")
     subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
+
+
+def test_training_entry_points_validate_before_launch(L):
+    lib = L.lib()
+    good = ctypes.c_void_p(4096)
+    n = ctypes.c_size_t(0)
+    d = _desc(L)
+    assert lib.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # holds at least dY_perm, dG and the four token-major operands
+    assert n.value >= 64 * 2 * 256 * 2 + 64 * 3 * 256 * 2
+    # fp32 and fp8 layers have no training path
+    for kw in (dict(act_dtype=0, w_dtype=0), dict(w_dtype=2)):
+        assert lib.moe_backward_workspace_size(ctypes.byref(_desc(L, **kw)), ctypes.byref(n)) == 2
+    w = L.MoeWeights(4096, 4096, 4096, 4096, None, None, None, None)
+    sv = L.MoeSaved(*([4096] * 10))
+    # forward_train: NULL saved, then a misaligned saved tensor
+    st = lib.moe_forward_train(ctypes.byref(d), good, good, good, ctypes.byref(w), good, None,
+                               None, good, 1 << 30, None)
+    assert st == 1 and b"saved is NULL" in lib.moe_last_error()
+    bad = L.MoeSaved(*([4096] * 7 + [4100] + [4096] * 2))
+    st = lib.moe_forward_train(ctypes.byref(d), good, good, good, ctypes.byref(w), good,
+                               ctypes.byref(bad), None, good, 1 << 30, None)
+    assert st == 3 and b"saved.h" in lib.moe_last_error()
+    st = lib.moe_forward_train(ctypes.byref(d), good, good, good, ctypes.byref(w), good,
+                               ctypes.byref(sv), None, good, 16, None)
+    assert st == 4
+    # transpose: missing shared copies when Is > 0
+    wt = L.MoeWeightsT(4096, 4096, None, None)
+    assert lib.moe_transpose_weights(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wt), None) == 1
+    # backward: NULL grads, NULL dy, small workspace
+    wt = L.MoeWeightsT(4096, 4096, 4096, 4096)
+    g = L.MoeGrads(4096, 4096, 4096, 4096, 4096)
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), good,
+                          good, None, good, 1 << 30, None)
+    assert st == 1 and b"grads is NULL" in lib.moe_last_error()
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), None,
+                          good, ctypes.byref(g), good, 1 << 30, None)
+    assert st == 1 and b"dy is NULL" in lib.moe_last_error()
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), good,
+                          good, ctypes.byref(g), good, 16, None)
+    assert st == 4 and b"workspace" in lib.moe_last_error()
