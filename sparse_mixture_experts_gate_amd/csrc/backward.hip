@@ -415,8 +415,14 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
 // Weight gradients out_g = A_g B_g^T (fp32) per group g: A_g rows m < M_g and
 // B_g rows n < N_g of the token-major operands at, bt (row stride ldp), over
 // the columns [poff[g], poff[g+1]) of segment g. Tiles: ceil(M/BM) x
-// ceil(N/BN) per group, n fastest; routed groups first, the shared group
-// last.
+// ceil(N/BN) per group, routed groups first, the shared group last. Inside a
+// group, tiles go in rows of kSuperM m-tiles, m fastest within a row: the 32
+// consecutive tiles one XCD runs at a time (8 m-tiles x 4 n-tiles) then read
+// 8 A panels and 4 B panels, the fewest panel bytes for 32 tiles, where an
+// n-fastest order reads one A panel against every B panel of the expert,
+// more than the L2 keeps, once per m-tile.
+constexpr int kSuperM = 8;
+
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
@@ -438,26 +444,34 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
   const i32x4_t ra = rsrc4(w.at, static_cast<uint32_t>(w.a_rows) * row_bytes);
   const i32x4_t rb = rsrc4(w.bt, static_cast<uint32_t>(w.b_rows) * row_bytes);
 
+  const int tm = tpr / tn, tms = (w.Ms + C::BM - 1) / C::BM;
   struct Coord {
     int g, mt, nt, M, N;
   };
   auto coord = [&](int tile) {
     Coord c;
+    int rem, ntm, ntn;
     if (tile < w.E * tpr) {
       c.g = tile / tpr;
-      const int rem = tile - c.g * tpr;
-      c.mt = rem / tn;
-      c.nt = rem - c.mt * tn;
+      rem = tile - c.g * tpr;
       c.M = w.M;
       c.N = w.N;
+      ntm = tm;
+      ntn = tn;
     } else {
-      const int rem = tile - w.E * tpr;
+      rem = tile - w.E * tpr;
       c.g = w.E;
-      c.mt = rem / tns;
-      c.nt = rem - c.mt * tns;
       c.M = w.Ms;
       c.N = w.Ns;
+      ntm = tms;
+      ntn = tns;
     }
+    const int per_row = kSuperM * ntn;
+    const int gr = rem / per_row;
+    const int r2 = rem - gr * per_row;
+    const int sm = min(kSuperM, ntm - gr * kSuperM);
+    c.nt = r2 / sm;
+    c.mt = gr * kSuperM + (r2 - c.nt * sm);
     return c;
   };
   auto next_ops = [&](int tile, int, StreamOps<C>& op) {
@@ -483,27 +497,37 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
     const Coord c = coord(tile);
     return (sp[c.g + 1] - sp[c.g]) / BK;
   };
+  // acc in the unswapped layout: lane l owns column l % 32 of each 32 x 32
+  // product, so one register across the wave stores two 128-byte row pieces.
+  // Buffer stores with out-of-range offsets for the masked entries: every
+  // call issues exactly MI * NJ * 16 stores (no branch can skip one), which
+  // lets them drain during the next tile's first step.
   auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const Coord c = coord(tile);
     float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        out, 0, static_cast<int>(static_cast<uint32_t>(c.M) * c.N * 4u), 0x00020000);
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      const int m = c.mt * C::BM + wm * C::WM + mi * 32 + (lane & 31);
-      if (m >= c.M) continue;
-      float* orow = out + static_cast<int64_t>(m) * c.N;
+    for (int nj = 0; nj < C::NJ; ++nj) {
+      const int n = c.nt * C::BN + wn * C::WN + nj * 32 + (lane & 31);
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
+      for (int mi = 0; mi < C::MI; ++mi) {
+        const int m0 = c.mt * C::BM + wm * C::WM + mi * 32;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = c.nt * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
-          if (n >= c.N) continue;
-          const f32x16_t& v = acc[mi][nj];
-          *reinterpret_cast<float4*>(orow + n) =
-              make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + acc_row(lane, r);
+          const uint32_t off = (m < c.M && n < c.N)
+                                   ? (static_cast<uint32_t>(m) * c.N + n) * 4u
+                                   : kInvalidRow;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0, 0);
         }
+      }
     }
   };
-  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
+  constexpr int kStores = C::MI * C::NJ * 16;
+  constexpr int kPost = kInflight<C> + kStores < 63 ? kInflight<C> + kStores : 63;
+  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, false, kPost>(
+      lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 template <class K>

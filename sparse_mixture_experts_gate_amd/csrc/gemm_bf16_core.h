@@ -121,7 +121,17 @@ struct StreamOps {
 //     side (called once per tile, in order, after the previous tile's last
 //     step was issued);
 //   nk_of(tile): k-steps of a tile;
-//   epilogue(tile, acc): stores a finished tile (acc in the SWAP layout).
+//   epilogue(tile, acc): stores a finished tile. With SWAP (the default) the
+//     weight fragment goes first and acc holds the transposed tile: lane l
+//     owns output row l % 32 and, per group of four registers, four adjacent
+//     columns; without it lane l owns output column l % 32 and rows
+//     acc_row(l, r), so that one register across the wave is two 128-byte
+//     row pieces (full cache lines for fp32 outputs).
+// POST >= 0 lets the epilogue's stores drain during the next tile's first
+// step: that step's wait allows POST operations in flight instead of
+// kInflight<C>, which is exact only if every epilogue call issues at least
+// POST - kInflight<C> vector-memory instructions (the stage that step needs
+// was loaded before them).
 // Vector-memory waits count only this stream's loads: every step issues the
 // same loads (once the tiles run out, the last step is loaded again into
 // stages nobody reads), so with loads NST - 1 steps ahead at most the newest
@@ -131,7 +141,8 @@ struct StreamOps {
 // multiplies; the step's barrier sits before its last sub-step, whose
 // fragments are already in registers, so that the next stage's first
 // fragments are read while those MFMAs run.
-template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue>
+template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, bool SWAP = true,
+          int POST = -1>
 __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
                                             NextOps&& next_ops, NkOf&& nk_of,
                                             Epilogue&& epilogue) {
@@ -182,14 +193,18 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
           As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
   };
   f32x16_t acc[C::MI][C::NJ];
-  // the weight fragment goes first: acc holds the transposed tile
   auto mma = [&](int buf) {
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][nj], af[buf][mi],
-                                                              acc[mi][nj], 0, 0, 0);
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        if constexpr (SWAP)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][nj], af[buf][mi],
+                                                                acc[mi][nj], 0, 0, 0);
+        else
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bfr[buf][nj],
+                                                                acc[mi][nj], 0, 0, 0);
+      }
   };
 
 #pragma unroll
@@ -223,7 +238,15 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
       // this wave's part of the next stage has landed; the barrier makes
       // every wave's part visible and frees the stage whose last fragments
       // are now in registers
-      vm_wait<INFLIGHT>();
+      if constexpr (POST >= 0) {
+        static_assert(POST >= INFLIGHT && POST <= 63, "vmcnt range");
+        if (kc == 0 && tc != first)
+          vm_wait<POST>();
+        else
+          vm_wait<INFLIGHT>();
+      } else {
+        vm_wait<INFLIGHT>();
+      }
       lds_barrier();
       st = st == NST - 1 ? 0 : st + 1;
       st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
