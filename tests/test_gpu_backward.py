@@ -156,3 +156,78 @@ def test_backward_single_token_and_zero_tokens():
     for k, v in g0.items():
         if v is not None:
             assert not v.any(), k
+
+
+def test_backward_v3_sampled():
+    """The V3 prefill layer (T = 8192, d = 7168, 256 experts in 8 groups,
+    K = 8, I = Is = 2048) in the launch configuration the benchmark times;
+    the oracle computes sampled outputs one by one: the input gradient of
+    sampled tokens (each needs only its own experts), the weight gradients
+    of a hot and a cold expert (all their tokens), the router-weight
+    gradient of the cold expert, and rows of the shared expert's gradients."""
+    wl = CONFIGS["v3_prefill_bf16"]
+    _log("backward V3 sampled: running the layer")
+    P, layer, y, sv, wt, dy, dx, gr = _run(wl)
+    x = host(P["x"])
+    wr = host(P["w_router"])
+    logits = host(sv["logits"])
+    idx = host(sv["topk_idx"])
+    dyh = host(dy)
+    w13, w2 = LazyHost(P["w13"]), LazyHost(P["w2"])
+    ws13, ws2 = host(P["ws13"]), host(P["ws2"])
+    tol = TOL["bf16"]
+    # input gradient of sampled tokens
+    rng = np.random.default_rng(5)
+    for t in rng.choice(wl.T, size=3, replace=False):
+        t = int(t)
+        ref = O.layer_backward(x[t:t + 1], wr, logits[t:t + 1], idx[t:t + 1], w13, w2, ws13, ws2,
+                               dyh[t:t + 1])
+        e = row_rel_err(host(dx[t:t + 1]), ref.dx)
+        _log(f"  token {t}: dx {e:.2e}")
+        assert e <= tol
+    # weight gradients of a hot and a cold expert
+    counts = host(sv["counts"])
+    hot = int(np.argmax(counts))
+    cold = int(np.argmin(np.where(counts >= 8, counts, 1 << 30)))
+    s_sel = 1.0 / (1.0 + np.exp(-np.take_along_axis(logits.astype(np.float64), idx, 1)))
+    g = s_sel / s_sel.sum(1, keepdims=True)
+    for e in (hot, cold):
+        rows, slots = np.nonzero(idx == e)
+        dXe, dW13e, dW2e, _ = O.swiglu_expert_backward(x[rows], w13[e], w2[e],
+                                                       g[rows, slots][:, None] * dyh[rows])
+        e13 = mat_rel_err(host(gr["dw13"][e]), dW13e)
+        e2 = mat_rel_err(host(gr["dw2"][e]), dW2e)
+        _log(f"  expert {e} ({len(rows)} tokens): dw13 {e13:.2e} dw2 {e2:.2e}")
+        assert e13 <= tol and e2 <= tol
+    # router-weight gradient of the cold expert: every token routed to it,
+    # with all of that token's experts (the gates' normalisation couples them)
+    rows = np.nonzero((idx == cold).any(axis=1))[0]
+    ref = O.layer_backward(x[rows], wr, logits[rows], idx[rows], w13, w2, None, None, dyh[rows])
+    er = mat_rel_err(host(gr["dw_router"][cold]), ref.dw_router[cold])
+    _log(f"  router row {cold} ({len(rows)} tokens): {er:.2e}")
+    assert er <= tol
+    # rows of the shared expert's gradients: dWs2[j] = sum_t dy[t, j] h_s[t],
+    # dWs13[m] = sum_t dG_s[t, m] x_t for sampled j, m
+    Is = wl.Is
+    xd = x.astype(np.float64)
+    for m in (0, 777, Is - 1):
+        a = xd @ ws13[m].astype(np.float64)
+        b = xd @ ws13[Is + m].astype(np.float64)
+        sa = 1.0 / (1.0 + np.exp(-a))
+        dh = dyh.astype(np.float64) @ ws2[:, m].astype(np.float64)
+        da = dh * b * sa * (1.0 + a * (1.0 - sa))
+        db = dh * a * sa
+        for row, dgc in ((m, da), (Is + m, db)):
+            ref_row = dgc @ xd
+            er = mat_rel_err(host(gr["dws13"][row]), ref_row)
+            assert er <= tol, (row, er)
+    hs = None
+    for j in (3, 4000, wl.d - 1):
+        if hs is None:
+            A = xd @ ws13[:Is].T.astype(np.float64)
+            B = xd @ ws13[Is:].T.astype(np.float64)
+            hs = A / (1.0 + np.exp(-A)) * B
+        ref_row = dyh[:, j].astype(np.float64) @ hs
+        er = mat_rel_err(host(gr["dws2"][j]), ref_row)
+        assert er <= tol, (j, er)
+    _log("  shared-expert rows ok")
