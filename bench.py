@@ -191,9 +191,8 @@ def cpu_baseline(wl, P, n_tokens: int) -> dict:
 
 def time_train(layer, x, steps: int, warmup: int) -> dict:
     """Training forward (moe_forward_train) and backward (moe_backward) back to
-    back per step, each bracketed by HIP events on the current stream; the
-    weight transposes (moe_transpose_weights, once per weight update) timed
-    on their own. dy is a seeded bf16 N(0, 1) tensor."""
+    back per step, each bracketed by HIP events on the current stream. dy is
+    a seeded bf16 N(0, 1) tensor."""
     import torch
     T, d = x.shape
     g = torch.Generator(device=x.device)
@@ -201,28 +200,22 @@ def time_train(layer, x, steps: int, warmup: int) -> dict:
     dy = torch.randn(T, d, generator=g, device=x.device).to(torch.bfloat16)
     sv = layer.alloc_saved(T)
     grads = layer.alloc_grads()
-    wt = layer.transpose_weights()
     for _ in range(warmup):
         layer.forward_train(x, sv)
-        layer.backward(x, dy, sv, wt, grads)
+        layer.backward(x, dy, sv, grads)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record()
         layer.forward_train(x, sv)
         ev[i][1].record()
-        layer.backward(x, dy, sv, wt, grads)
+        layer.backward(x, dy, sv, grads)
         ev[i][2].record()
-    tr = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    tr[0].record()
-    for _ in range(3):
-        layer.transpose_weights()
-    tr[1].record()
     torch.cuda.synchronize()
     fwd = [e[0].elapsed_time(e[1]) for e in ev]
     bwd = [e[1].elapsed_time(e[2]) for e in ev]
     return {"fwd_train_ms": percentiles(fwd)["median"], "bwd_ms": percentiles(bwd)["median"],
-            "bwd_ms_pctl": percentiles(bwd), "transpose_ms": tr[0].elapsed_time(tr[1]) / 3}
+            "bwd_ms_pctl": percentiles(bwd)}
 
 
 def train_record(wl, T: int, r: dict) -> dict:
@@ -232,7 +225,7 @@ def train_record(wl, T: int, r: dict) -> dict:
     bwd_fl = 2.0 * fwd_fl
     tf = bwd_fl / (r["bwd_ms"] / 1e3)
     return {"T": T, "fwd_train_ms": r["fwd_train_ms"], "bwd_ms": r["bwd_ms"],
-            "bwd_ms_pctl": r["bwd_ms_pctl"], "transpose_weights_ms": r["transpose_ms"],
+            "bwd_ms_pctl": r["bwd_ms_pctl"],
             "bwd_gemm_tflop": bwd_fl / 1e12, "bwd_tflops": tf / 1e12,
             "bwd_mfma_frac": tf / MFMA_PEAK["bf16"],
             "train_step_tokens_per_s": T / ((r["fwd_train_ms"] + r["bwd_ms"]) / 1e3)}
@@ -279,7 +272,7 @@ def main() -> int:
         log(f"timing the training step of {wl.name}: warmup {args.warmup}, steps {args.steps}")
         rec = train_record(wl, wl.T, time_train(layer, P["x"], args.steps, args.warmup))
         log(f"train: forward {rec['fwd_train_ms']:.3f} ms, backward {rec['bwd_ms']:.3f} ms "
-            f"({rec['bwd_tflops']:.0f} TFLOP/s), weight transposes {rec['transpose_weights_ms']:.3f} ms")
+            f"({rec['bwd_tflops']:.0f} TFLOP/s)")
         print(json.dumps({"train_bf16": rec, "workload": wl.name}), flush=True)
         return 0
     log(f"timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
@@ -330,8 +323,8 @@ def main() -> int:
         tr = train_record(wl, wl.T, time_train(layer, P["x"], 5, 2))
         extra["train_bf16"] = tr
         log(f"train: forward {tr['fwd_train_ms']:.3f} ms, backward {tr['bwd_ms']:.3f} ms "
-            f"({tr['bwd_tflops']:.0f} TFLOP/s), weight transposes {tr['transpose_weights_ms']:.3f} ms")
-        layer._wt = layer._bws = None
+            f"({tr['bwd_tflops']:.0f} TFLOP/s)")
+        layer._bws = None
         torch.cuda.empty_cache()
         try:
             wl8 = CONFIGS["v3_fp8"]

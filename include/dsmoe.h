@@ -261,20 +261,6 @@ moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const fl
                              const moe_saved* saved, int32_t* near_tie, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* Transposed bf16 copies of the expert weights, read by the backward's
- * input-gradient GEMMs (whose contraction runs over the weights' output
- * rows): w13_t [E, d, 2I], w2_t [E, I, d], ws13_t [d, 2Is], ws2_t [Is, d].
- * To be refreshed whenever the weights change. */
-typedef struct moe_weights_t {
-  void* w13_t;
-  void* w2_t;
-  void* ws13_t;
-  void* ws2_t;
-} moe_weights_t;
-
-moe_status moe_transpose_weights(const moe_layer_desc* desc, const moe_weights* w,
-                                 const moe_weights_t* wt, hipStream_t stream);
-
 /* Gradients of the layer (fp32, device pointers, fully overwritten):
  *   dw13 [E, 2I, d], dw2 [E, d, I], dws13 [2Is, d], dws2 [d, Is]
  *   (the shared ones NULL when Is == 0), dw_router [E, d]. An expert that
@@ -293,12 +279,11 @@ moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes
 /* Backward of the layer from the output gradient dy [T, d] bf16:
  *   dx [T, d] bf16 OUT, the input gradient (experts, shared expert and router);
  *   g  OUT, the weight gradients;
- * x, w_router: the forward's inputs; wt: moe_transpose_weights of the
- * forward's weights; saved: what moe_forward_train wrote. */
+ * x, w_router, w: the forward's inputs (the weights in their forward layout);
+ * saved: what moe_forward_train wrote. */
 moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* w_router,
-                        const moe_weights_t* wt, const moe_saved* saved, const void* dy,
-                        void* dx, const moe_grads* g, void* ws, size_t ws_bytes,
-                        hipStream_t stream);
+                        const moe_weights* w, const moe_saved* saved, const void* dy, void* dx,
+                        const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Timing hook for benchmarks (thread-local setting). With n_events >= 6,
  * deepseek_moe_forward records events[0..5] on its stream: before the router,

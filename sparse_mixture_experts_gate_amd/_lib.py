@@ -48,10 +48,6 @@ class MoeSaved(ctypes.Structure):
                  "y_perm")]
 
 
-class MoeWeightsT(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w13_t", "w2_t", "ws13_t", "ws2_t")]
-
-
 class MoeGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("dw13", "dw2", "dws13", "dws2", "dw_router")]
 
@@ -88,10 +84,9 @@ def lib() -> ctypes.CDLL:
             "moe_profile_events": [ctypes.POINTER(ctypes.c_void_p), I32],
             "moe_forward_train": [D, P, P, P, W, P, ctypes.POINTER(MoeSaved), P, P,
                                   ctypes.c_size_t, P],
-            "moe_transpose_weights": [D, W, ctypes.POINTER(MoeWeightsT), P],
             "moe_backward_workspace_size": [D, ctypes.POINTER(ctypes.c_size_t)],
-            "moe_backward": [D, P, P, ctypes.POINTER(MoeWeightsT), ctypes.POINTER(MoeSaved), P, P,
-                             ctypes.POINTER(MoeGrads), P, ctypes.c_size_t, P],
+            "moe_backward": [D, P, P, W, ctypes.POINTER(MoeSaved), P, P, ctypes.POINTER(MoeGrads),
+                             P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -228,10 +223,6 @@ def make_saved(**tensors) -> MoeSaved:
     return _struct(MoeSaved, **tensors)
 
 
-def make_weights_t(w13_t, w2_t, ws13_t=None, ws2_t=None) -> MoeWeightsT:
-    return _struct(MoeWeightsT, w13_t=w13_t, w2_t=w2_t, ws13_t=ws13_t, ws2_t=ws2_t)
-
-
 def make_grads(dw13, dw2, dws13, dws2, dw_router) -> MoeGrads:
     return _struct(MoeGrads, dw13=dw13, dw2=dw2, dws13=dws13, dws2=dws2, dw_router=dw_router)
 
@@ -244,12 +235,6 @@ def moe_forward_train(desc, x, w_router, bias, weights: MoeWeights, y, saved: Mo
            "moe_forward_train")
 
 
-def moe_transpose_weights(desc, weights: MoeWeights, wt: MoeWeightsT, stream=None):
-    _check(lib().moe_transpose_weights(ctypes.byref(desc), ctypes.byref(weights),
-                                       ctypes.byref(wt), _stream(stream)),
-           "moe_transpose_weights")
-
-
 def moe_backward_workspace_size(desc: MoeLayerDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().moe_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
@@ -257,8 +242,8 @@ def moe_backward_workspace_size(desc: MoeLayerDesc) -> int:
     return n.value
 
 
-def moe_backward(desc, x, w_router, wt: MoeWeightsT, saved: MoeSaved, dy, dx, grads: MoeGrads, ws,
-                 stream=None):
-    _check(lib().moe_backward(ctypes.byref(desc), _p(x), _p(w_router), ctypes.byref(wt),
+def moe_backward(desc, x, w_router, weights: MoeWeights, saved: MoeSaved, dy, dx, grads: MoeGrads,
+                 ws, stream=None):
+    _check(lib().moe_backward(ctypes.byref(desc), _p(x), _p(w_router), ctypes.byref(weights),
                               ctypes.byref(saved), _p(dy), _p(dx), ctypes.byref(grads), _p(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_backward")

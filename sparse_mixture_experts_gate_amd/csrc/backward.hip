@@ -12,8 +12,10 @@
 //            du_tk = (dg_tk - sum_j g_tj dg_tj) / S_t * s_tk (1 - s_tk);
 //   dgrad2:  dH = dYp W2_e (shared: dy Ws2), then the SwiGLU backward
 //            da = dH b silu'(a), db = dH silu(a) from the saved a, b;
-//   dgrad1:  dA = [da | db] [W1_e; W3_e] (the forward's down-GEMM kernel on
-//            transposed weight copies);
+//   dgrad1:  dA = [da | db] [W1_e; W3_e];
+//            both contract over the weights' output rows and read the
+//            weights in their forward layout as k-major operands (LDS
+//            transpose reads, see gemm_bf16_core.h);
 //   combine: dx_t = dA_s[t] + sum_k dA[inv[t,k]] + sum_k du_tk Wr[e_tk];
 //   router:  dWr[e] = sum over e's rows of du x;
 //   wgrad:   dW13_e = [da | db]_e^T A_e, dW2_e = dYp_e^T H_e, as GEMMs whose
@@ -29,52 +31,11 @@ namespace dsmoe {
 
 namespace {
 
-// ---- transposes ------------------------------------------------------------
+// ---- token-major copies --------------------------------------------------
 
 constexpr int kTr = 64;       // tile edge
 constexpr int kTrPitch = 66;  // LDS row pitch (elements): 132-byte rows keep the
                               // four 16-row groups of a column read on distinct banks
-
-// dst[b][c][r] = src[b][r][c] for r < R, c < C (R, C multiples of 8).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
-                                                             int R, int C,
-                                                             uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTr * kTrPitch];
-  const int tid = threadIdx.x;
-  const int64_t mat = static_cast<int64_t>(blockIdx.z) * R * C;
-  const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr;
-  {
-    const int r = tid >> 2, cc = (tid & 3) * 16;
-    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + r * kTrPitch + cc);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int c = c0 + cc + 8 * h;
-      if (r0 + r < R && c < C)
-        v = *reinterpret_cast<const uint4*>(src + mat + static_cast<int64_t>(r0 + r) * C + c);
-      t32[4 * h + 0] = v.x;
-      t32[4 * h + 1] = v.y;
-      t32[4 * h + 2] = v.z;
-      t32[4 * h + 3] = v.w;
-    }
-  }
-  __syncthreads();
-  const int c = tid >> 2, rr = (tid & 3) * 16;
-  if (c0 + c >= C) return;
-  uint16_t* out = dst + mat + static_cast<int64_t>(c0 + c) * R + r0 + rr;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (r0 + rr + 8 * h >= R) break;
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 8 * h + 2 * j;
-      w[j] = static_cast<uint32_t>(tile[(rr + i) * kTrPitch + c]) |
-             (static_cast<uint32_t>(tile[(rr + i + 1) * kTrPitch + c]) << 16);
-    }
-    *reinterpret_cast<uint4*>(out + 8 * h) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
 
 // Token-major copy for the weight-gradient GEMMs: dst[c][p] (row stride ldp)
 // for c < cols. Column p of routed segment g (g < E) at i = p - poff[g] takes
@@ -324,9 +285,9 @@ __global__ __launch_bounds__(kRowT) void router_wgrad_kernel(
 // ---- grouped GEMMs -----------------------------------------------------------
 
 // dH = dYp W2_e per routed group (rows of the group's segment) and dy Ws2 for
-// the shared group, from transposed weight copies W2_e^T [I, d] (so that the
-// contraction over d runs along rows, as in the forward kernels), then the
-// SwiGLU backward from the saved pre-activations: dG = [da | db].
+// the shared group, W2 read in its forward layout [d, I] as a k-major
+// operand, then the SwiGLU backward from the saved pre-activations:
+// dG = [da | db].
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
@@ -357,17 +318,16 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
       op.ao[p] = lr < rows_left ? static_cast<uint32_t>(rbase + lr) * row_bytes : kInvalidRow;
     }
     op.ra = c.shared ? rdy : rdyp;
-    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2t)
-                                 : static_cast<const uint16_t*>(a.w2t) +
-                                       static_cast<int64_t>(c.g) * a.I * a.d;
-    op.rb = rsrc4(W, static_cast<uint32_t>(Ig) * row_bytes);
-#pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) {
-      const int row = c.n * C::BN + r0 + p * C::RPP;
-      op.bo[p] = row < Ig ? static_cast<uint32_t>(row) * row_bytes : kInvalidRow;
-    }
     swizzle_rows<C>(op.ao);
-    swizzle_rows<C>(op.bo);
+    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2)
+                                 : static_cast<const uint16_t*>(a.w2) +
+                                       static_cast<int64_t>(c.g) * a.d * a.I;
+    const uint32_t ld_bytes = static_cast<uint32_t>(Ig) * 2u;
+    op.rb = rsrc4(W, static_cast<uint32_t>(a.d) * ld_bytes);
+    // columns past Ig (last column tile) read neighbouring data or zeros;
+    // they only reach output columns that are not stored
+    kmajor_offsets<C>(op.bo, c.n * C::BN, ld_bytes);
+    op.kstep_b = BK * ld_bytes;
     op.nk = nk;
   };
   auto nk_of = [&](int) { return nk; };
@@ -409,7 +369,79 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
         }
     }
   };
-  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
+  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, true, -1, true>(
+      lds, first, nb, total, next_ops, nk_of, epilogue);
+}
+
+// dA = [da | db] [W1_e; W3_e] per routed group and the same with the shared
+// weights for the shared rows: the contraction runs over the 2 Ig rows of
+// W13 [2Ig, d], read in its forward layout as a k-major operand. bf16 out.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINW) void dgrad1_bf16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ GroupTables gt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r0 = tid >> 3;
+  load_group_tables(gt, a.tiles, a.offsets, a.E);
+  const int total = gt.total;
+  const int nb = gridDim.x;
+  const int first = xcd_logical_block(blockIdx.x, nb);
+  if (first >= total) return;
+  const uint32_t grow_bytes = static_cast<uint32_t>(a.ldh) * 4u;  // rows of [da | db]
+  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
+  const i32x4_t rg = rsrc4(a.dg, static_cast<uint32_t>(hrows) * grow_bytes);
+  const uint32_t ld_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
+
+  auto next_ops = [&](int tile, int, StreamOps<C>& op) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int Ig = c.shared ? a.Is : a.I;
+    const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    const int rows_left = c.rows - c.m * C::BM;
+#pragma unroll
+    for (int p = 0; p < C::A_LOADS; ++p) {
+      const int lr = r0 + p * C::RPP;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * grow_bytes : kInvalidRow;
+    }
+    op.ra = rg;
+    swizzle_rows<C>(op.ao);
+    const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws13)
+                                 : static_cast<const uint16_t*>(a.w13) +
+                                       static_cast<int64_t>(c.g) * 2 * a.I * a.d;
+    op.rb = rsrc4(W, static_cast<uint32_t>(2 * Ig) * ld_bytes);
+    kmajor_offsets<C>(op.bo, c.n * C::BN, ld_bytes);
+    op.kstep_b = BK * ld_bytes;
+    op.nk = 2 * Ig / BK;
+  };
+  auto nk_of = [&](int tile) { return 2 * (tile >= shared_first ? a.Is : a.I) / BK; };
+  auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    const int rows_left = c.rows - c.m * C::BM;
+    uint16_t* out = c.shared ? static_cast<uint16_t*>(a.das) +
+                                   static_cast<int64_t>(c.m) * C::BM * a.d
+                             : static_cast<uint16_t*>(a.dap) +
+                                   (static_cast<int64_t>(c.rbase) + c.m * C::BM) * a.d;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const int row = wm * C::WM + mi * 32 + (lane & 31);
+      if (row >= rows_left) continue;
+      uint16_t* yp = out + static_cast<int64_t>(row) * a.d;
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = c.n * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
+          if (col >= a.d) continue;
+          const f32x16_t& v = acc[mi][nj];
+          *reinterpret_cast<uint2*>(yp + col) = pack_bf16x4(v[4 * g], v[4 * g + 1],
+                                                            v[4 * g + 2], v[4 * g + 3]);
+        }
+    }
+  };
+  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, true, -1, true>(
+      lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 // Weight gradients out_g = A_g B_g^T (fp32) per group g: A_g rows m < M_g and
@@ -540,15 +572,6 @@ int occupancy_of(K kernel, int threads) {
 
 }  // namespace
 
-hipError_t launch_transpose_bf16(const void* src, int64_t n_mats, int R, int C, void* dst,
-                                 hipStream_t s) {
-  if (n_mats == 0 || R == 0 || C == 0) return hipSuccess;
-  dim3 grid((C + kTr - 1) / kTr, (R + kTr - 1) / kTr, static_cast<unsigned>(n_mats));
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s,
-                     static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
-  return hipGetLastError();
-}
-
 hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
                              hipStream_t s) {
   hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanT), 0, s, offsets, E, T,
@@ -603,6 +626,15 @@ hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s) {
   if (!occ) occ = occupancy_of(dgrad2_bf16_kernel<C>, C::NT);
   const int g = ((device_cu_count() * occ + 7) / 8) * 8;
   hipLaunchKernelGGL(dgrad2_bf16_kernel<C>, dim3(g), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s) {
+  using C = TilePrefill;
+  static int occ = 0;
+  if (!occ) occ = occupancy_of(dgrad1_bf16_kernel<C>, C::NT);
+  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
+  hipLaunchKernelGGL(dgrad1_bf16_kernel<C>, dim3(g), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }
 

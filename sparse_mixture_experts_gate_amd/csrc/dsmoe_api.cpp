@@ -751,29 +751,6 @@ moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const fl
   return MOE_OK;
 }
 
-moe_status moe_transpose_weights(const moe_layer_desc* desc, const moe_weights* w,
-                                 const moe_weights_t* wt, hipStream_t stream) {
-  moe_status st = validate_train(desc);
-  if (st) return st;
-  st = check_weights(desc, w);
-  if (st) return st;
-  if (!wt) return fail(MOE_ERR_INVALID_ARGUMENT, "wt is NULL");
-  st = check_ptrs({{wt->w13_t, "w13_t"}, {wt->w2_t, "w2_t"}});
-  if (st) return st;
-  const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
-  if (Is > 0) {
-    st = check_ptrs({{wt->ws13_t, "ws13_t"}, {wt->ws2_t, "ws2_t"}});
-    if (st) return st;
-  }
-  HIP_TRY(launch_transpose_bf16(w->w13, E, 2 * I, d, wt->w13_t, stream), "transpose w13");
-  HIP_TRY(launch_transpose_bf16(w->w2, E, d, I, wt->w2_t, stream), "transpose w2");
-  if (Is > 0) {
-    HIP_TRY(launch_transpose_bf16(w->ws13, 1, 2 * Is, d, wt->ws13_t, stream), "transpose ws13");
-    HIP_TRY(launch_transpose_bf16(w->ws2, 1, d, Is, wt->ws2_t, stream), "transpose ws2");
-  }
-  return MOE_OK;
-}
-
 moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes) {
   moe_status st = validate_train(desc);
   if (st) return st;
@@ -783,7 +760,7 @@ moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes
 }
 
 moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* w_router,
-                        const moe_weights_t* wt, const moe_saved* sv, const void* dy, void* dx,
+                        const moe_weights* w, const moe_saved* sv, const void* dy, void* dx,
                         const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = validate_train(desc);
   if (st) return st;
@@ -816,13 +793,8 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   }
   st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {dy, "dy"}, {dx, "dx"}, {ws, "ws"}});
   if (st) return st;
-  if (!wt) return fail(MOE_ERR_INVALID_ARGUMENT, "wt is NULL");
-  st = check_ptrs({{wt->w13_t, "w13_t"}, {wt->w2_t, "w2_t"}});
+  st = check_weights(desc, w);
   if (st) return st;
-  if (shared) {
-    st = check_ptrs({{wt->ws13_t, "ws13_t"}, {wt->ws2_t, "ws2_t"}});
-    if (st) return st;
-  }
   st = check_saved(desc, sv);
   if (st) return st;
   const BwdLayout L = bwd_layout(desc);
@@ -873,27 +845,17 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   b.ldh = ldh;
   b.dyp = dyp;
   b.dy = dy;
-  b.w2t = wt->w2_t;
-  b.ws2t = wt->ws2_t;
+  b.w2 = w->w2;
+  b.ws2 = w->ws2;
+  b.w13 = w->w13;
+  b.ws13 = w->ws13;
   b.gu = sv->gu;
   b.dg = dgb;
+  b.dap = dap;
+  b.das = das;
   HIP_TRY(launch_dgrad2_bf16(b, stream), "dgrad of the down projection");
-  FfnArgs a{};
-  a.offsets = sv->offsets;
-  a.tiles2 = tiles_d;
-  a.T = T;
-  a.TK = TK;
-  a.E = E;
-  a.d = d;
-  a.I = 2 * I;
-  a.Is = 2 * Is;
-  a.ldh = 2 * ldh;
-  a.H = dgb;
-  a.w2 = wt->w13_t;
-  a.ws2 = wt->ws13_t;
-  a.yperm = dap;
-  a.yshared = das;
-  HIP_TRY(launch_gemm2_bf16(a, stream), "dgrad of the gate/up projection");
+  b.tiles = tiles_d;
+  HIP_TRY(launch_dgrad1_bf16(b, stream), "dgrad of the gate/up projection");
   HIP_TRY(launch_bwd_combine(dap, das, sv->inv, sv->topk_idx, du, w_router, T, K, d, dx, stream),
           "input gradient");
   HIP_TRY(launch_router_wgrad(x, sv->perm, sv->offsets, du_perm, E, d, g->dw_router, stream),

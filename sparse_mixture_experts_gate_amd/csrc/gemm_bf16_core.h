@@ -109,7 +109,67 @@ struct StreamOps {
   i32x4_t ra, rb;
   uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
   int nk;
+  uint32_t kstep_b;  // k-major B only: bytes between consecutive k-steps
 };
+
+// ---- k-major B operand (weights [K, N] row-major, read without a transpose)
+//
+// Stage image: BK rows (k) of BN elements (n); 16-byte chunk c of row k
+// sits at position c ^ (4 (k & 3)). Every load pass keeps the same LDS
+// placement as the row-major stage (one 16-byte chunk per thread, threads
+// in order), so only the thread -> (k, chunk) assignment differs: thread t
+// of pass p loads row p * (NT * 8 / BN) + t / (BN / 8), logical chunk
+// (t % (BN / 8)) ^ (4 (row & 3)).
+//
+// Fragments come from ds_read_b64_tr_b16: in each 16-lane group, lane i
+// receives element i % 4 of the 8-byte pieces that lanes 4j + i / 4
+// (j = 0..3) address. With lane 4j + q of the group pointing at row k + j,
+// columns n + 4q .. n + 4q + 3, lane i gets column n + i at rows k .. k + 3;
+// two reads give the 8 consecutive k of a 32x32x16 MFMA operand. The
+// swizzle puts the four rows of one read on distinct banks.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <class C>
+__device__ __forceinline__ uint32_t kmajor_chunk(int t) {
+  constexpr int CPR = C::BN / 8;  // chunks per row
+  const int row = t / CPR;
+  return static_cast<uint32_t>((t % CPR) ^ (4 * (row & 3)));
+}
+
+// Global byte offsets of thread t's k-major B chunks for k-step 0: row r of
+// pass p is k = r, at `ld_bytes` per k; `col0` is the tile's first column.
+template <class C>
+__device__ __forceinline__ void kmajor_offsets(uint32_t (&o)[C::B_LOADS], int col0,
+                                               uint32_t ld_bytes) {
+  constexpr int CPR = C::BN / 8, RPASS = C::NT / CPR;
+  static_assert(C::NT % CPR == 0 && C::B_LOADS * RPASS == BK, "passes cover the k-step");
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < C::B_LOADS; ++p) {
+    const int k = p * RPASS + t / CPR;
+    o[p] = static_cast<uint32_t>(k) * ld_bytes +
+           static_cast<uint32_t>(col0 + kmajor_chunk<C>(t) * 8) * 2u;
+  }
+}
+
+// The MFMA operand of columns [n0, n0 + 32) and k [k0, k0 + 16) (lane l:
+// column n0 + l % 32, k0 + 8 (l / 32) .. + 7) from a k-major stage at LDS
+// byte address bs.
+template <class C>
+__device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t bs, int n0, int k0, int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  const int n = n0 + 16 * (g & 1) + 4 * q;
+  const int k = k0 + 8 * (g >> 1) + j;
+  const int chunk = (n >> 3) ^ (4 * j);  // k & 3 == j
+  const uint32_t a0 = bs + static_cast<uint32_t>(k * C::BN + chunk * 8 + (n & 4)) * 2u;
+  const uint32_t a1 = a0 + 4u * C::BN * 2u;  // rows k + 4: same swizzle
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a1);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // The persistent grouped GEMMs run every tile of a workgroup (tiles first,
 // first + nb, ... below total) as one k-stream through the NST-stage ring:
@@ -142,7 +202,7 @@ struct StreamOps {
 // fragments are already in registers, so that the next stage's first
 // fragments are read while those MFMAs run.
 template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, bool SWAP = true,
-          int POST = -1>
+          int POST = -1, bool BKM = false>
 __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
                                             NextOps&& next_ops, NkOf&& nk_of,
                                             Epilogue&& epilogue) {
@@ -161,8 +221,9 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
   bool more = true;
   next_ops(ti, index, op);
   auto issue = [&](int st) {
-    const uint32_t kb = static_cast<uint32_t>(ki) * (BK * 2);
-    stage_issue<C>(lds0, st, wave, op.ra, op.ao, kb, op.rb, op.bo, kb);
+    const uint32_t ka = static_cast<uint32_t>(ki) * (BK * 2);
+    const uint32_t kb = BKM ? static_cast<uint32_t>(ki) * op.kstep_b : ka;
+    stage_issue<C>(lds0, st, wave, op.ra, op.ao, ka, op.rb, op.bo, kb);
     if (more) ++ki;
   };
   auto advance = [&]() {
@@ -184,9 +245,13 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
     const uint16_t* Bs = As + C::BM * BK;
     const int chk = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj)
-      bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
-          Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
+    for (int nj = 0; nj < C::NJ; ++nj) {
+      if constexpr (BKM)
+        bfr[buf][nj] = frag_kmajor<C>(lds_addr(Bs), b_local_row<C, SWIGLU>(wn, nj), kk * 16, lane);
+      else
+        bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
+            Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
+    }
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
       af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(

@@ -107,15 +107,19 @@ hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, 
 // ---- backward (backward.hip), bf16 activations and weights ------------------
 struct BwdArgs {
   const int32_t* offsets;  // [E+1]
-  const int32_t* tiles;    // [E+2] tile prefix for 128-row tiles over Ig/256 column tiles
+  const int32_t* tiles;    // [E+2] tile prefix of the kernel's 128 x 256 tiles
   int64_t T, TK;
   int E, d, I, Is, ldh;
   const void* dyp;         // [TK, d] gated output gradients of the routed rows
   const void* dy;          // [T, d] output gradient (shared rows)
-  const void* w2t;         // [E, I, d] transposed down projections
-  const void* ws2t;        // [Is, d]
+  const void* w2;          // [E, d, I] down projections, as in the forward
+  const void* ws2;         // [d, Is]
+  const void* w13;         // [E, 2I, d] gate/up projections, as in the forward
+  const void* ws13;        // [2Is, d]
   const void* gu;          // [TK + T, 2 ldh] saved pre-activations
-  void* dg;                // [TK + T, 2 ldh] OUT: [da | db]
+  void* dg;                // [TK + T, 2 ldh] [da | db] (OUT of dgrad2, IN of dgrad1)
+  void* dap;               // [TK, d] OUT of dgrad1: input gradients of the routed rows
+  void* das;               // [T, d] OUT of dgrad1: the shared expert's
 };
 struct WgradArgs {
   const int32_t* poff;     // [G+1] segment starts in the token-major operands
@@ -130,8 +134,6 @@ struct WgradArgs {
   float* out;              // [E, M, N]
   float* out_s;            // [Ms, Ns]
 };
-hipError_t launch_transpose_bf16(const void* src, int64_t n_mats, int R, int C, void* dst,
-                                 hipStream_t s);
 hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
                              hipStream_t s);
 hipError_t launch_token_major(const void* src, int64_t ld, const int32_t* perm, const void* src_s,
@@ -148,6 +150,7 @@ hipError_t launch_bwd_combine(const void* dap, const void* das, const int32_t* i
 hipError_t launch_router_wgrad(const void* x, const int32_t* perm, const int32_t* offsets,
                                const float* du_perm, int E, int d, float* dwr, hipStream_t s);
 hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
 // ---- elementwise (elementwise.hip) -----------------------------------------

@@ -110,17 +110,6 @@ class MoELayer:
                             L.make_saved(**saved), near_tie, self.workspace(T), stream)
         return y, saved
 
-    def transpose_weights(self, stream=None) -> dict:
-        """Transposed bf16 weight copies for the backward (moe_transpose_weights)."""
-        wl, dev, bf = self.wl, self.device, torch.bfloat16
-        wt = {"w13_t": torch.empty(wl.E, wl.d, 2 * wl.I, dtype=bf, device=dev),
-              "w2_t": torch.empty(wl.E, wl.I, wl.d, dtype=bf, device=dev),
-              "ws13_t": torch.empty(wl.d, 2 * wl.Is, dtype=bf, device=dev) if wl.Is else None,
-              "ws2_t": torch.empty(wl.Is, wl.d, dtype=bf, device=dev) if wl.Is else None}
-        L.moe_transpose_weights(self.desc(0), self.weights, L.make_weights_t(**wt), stream)
-        self._wt = wt
-        return wt
-
     def alloc_grads(self) -> dict:
         wl, dev, f32 = self.wl, self.device, torch.float32
         return {"dw13": torch.empty(wl.E, 2 * wl.I, wl.d, dtype=f32, device=dev),
@@ -135,14 +124,13 @@ class MoELayer:
             self._bws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._bws
 
-    def backward(self, x: torch.Tensor, dy: torch.Tensor, saved: dict, wt: dict | None = None,
-                 grads: dict | None = None, stream=None) -> tuple:
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, saved: dict, grads: dict | None = None,
+                 stream=None) -> tuple:
         """dx [T, d] bf16 and the fp32 weight gradients (moe_backward)."""
         T = x.shape[0]
-        wt = self._wt if wt is None else wt
         grads = self.alloc_grads() if grads is None else grads
         dx = torch.empty(T, self.wl.d, dtype=torch.bfloat16, device=self.device)
-        L.moe_backward(self.desc(T), x, self.w_router, L.make_weights_t(**wt),
+        L.moe_backward(self.desc(T), x, self.w_router, self.weights,
                        L.make_saved(**saved), dy, dx, L.make_grads(**grads),
                        self.backward_workspace(T), stream)
         return dx, grads

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
         "moe_expert_ffn", "moe_combine", "moe_bias_update", "deepseek_moe_forward",
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
         "moe_last_error", "moe_abi_version", "moe_profile_events", "moe_forward_train",
-        "moe_transpose_weights", "moe_backward_workspace_size", "moe_backward"}
+        "moe_backward_workspace_size", "moe_backward"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
@@ -152,18 +152,18 @@ def test_training_entry_points_validate_before_launch(L):
     st = lib.moe_forward_train(ctypes.byref(d), good, good, good, ctypes.byref(w), good,
                                ctypes.byref(sv), None, good, 16, None)
     assert st == 4
-    # transpose: missing shared copies when Is > 0
-    wt = L.MoeWeightsT(4096, 4096, None, None)
-    assert lib.moe_transpose_weights(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wt), None) == 1
-    # backward: NULL grads, NULL dy, small workspace
-    wt = L.MoeWeightsT(4096, 4096, 4096, 4096)
+    # backward: NULL grads, NULL dy, missing shared weights, small workspace
     g = L.MoeGrads(4096, 4096, 4096, 4096, 4096)
-    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), good,
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(w), ctypes.byref(sv), good,
                           good, None, good, 1 << 30, None)
     assert st == 1 and b"grads is NULL" in lib.moe_last_error()
-    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), None,
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(w), ctypes.byref(sv), None,
                           good, ctypes.byref(g), good, 1 << 30, None)
     assert st == 1 and b"dy is NULL" in lib.moe_last_error()
-    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(wt), ctypes.byref(sv), good,
+    w_noshared = L.MoeWeights(4096, 4096, None, None, None, None, None, None)
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(w_noshared), ctypes.byref(sv),
+                          good, good, ctypes.byref(g), good, 1 << 30, None)
+    assert st == 1 and b"ws13 is NULL" in lib.moe_last_error()
+    st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(w), ctypes.byref(sv), good,
                           good, ctypes.byref(g), good, 16, None)
     assert st == 4 and b"workspace" in lib.moe_last_error()

@@ -1,8 +1,8 @@
 """GPU parity of the layer's training path against the fp64 backward oracle,
 through the C ABI: the training forward (same output as the inference
-forward, plus the saved tensors), the weight transposes (exact copies) and
-the backward (input, expert-weight, shared-expert and router-weight
-gradients within the bf16 tolerance, on the GPU's own routing).
+forward, plus the saved tensors) and the backward (input, expert-weight,
+shared-expert and router-weight gradients within the bf16 tolerance, on the
+GPU's own routing).
 
 Tolerance: the stated bf16 bound, 2e-2. The input gradient dx is compared
 row by row (a row is a token, as for the forward's outputs); every weight
@@ -47,11 +47,10 @@ def _run(wl, T=None):
     P = make_inputs(wl, DEV, T=T)
     layer = M.MoELayer(wl, P)
     y, sv = layer.forward_train(P["x"])
-    wt = layer.transpose_weights()
     dy = _dy(wl, P["x"].shape[0])
     dx, gr = layer.backward(P["x"], dy, sv)
     torch.cuda.synchronize()
-    return P, layer, y, sv, wt, dy, dx, gr
+    return P, layer, y, sv, dy, dx, gr
 
 
 def _oracle(wl, P, sv, dy):
@@ -86,7 +85,7 @@ def _check_grads(wl, sv, dx, gr, ref):
 def test_backward_parity(name):
     wl = TRAIN_SMALL if name == "train_small" else TRAIN_MED
     _log(f"backward parity {name} T={wl.T}")
-    P, layer, y, sv, wt, dy, dx, gr = _run(wl)
+    P, layer, y, sv, dy, dx, gr = _run(wl)
     # the training forward is the inference forward plus saved tensors
     out = layer.forward(P["x"])
     torch.cuda.synchronize()
@@ -98,12 +97,6 @@ def test_backward_parity(name):
     pr = O.permute(rr.idx, wl.E)
     assert np.array_equal(host(sv["offsets"]), pr.offsets)
     assert np.array_equal(host(sv["perm"]), pr.perm)
-    # the transposes are exact copies
-    assert torch.equal(wt["w13_t"], P["w13"].transpose(1, 2).contiguous())
-    assert torch.equal(wt["w2_t"], P["w2"].transpose(1, 2).contiguous())
-    if wl.Is:
-        assert torch.equal(wt["ws13_t"], P["ws13"].t().contiguous())
-        assert torch.equal(wt["ws2_t"], P["ws2"].t().contiguous())
     # saved pre-activations: [x W1^T | x W3^T] of each routed row, then shared
     x = host(P["x"]).astype(np.float64)
     gu = host(sv["gu"])
@@ -132,7 +125,7 @@ def test_backward_empty_experts_and_no_shared():
     # shared expert
     wl = TRAIN_SMALL.with_(name="train_sparse", E=24, G=1, M=1, K=2, Is=0, n_clusters=3, T=130)
     _log("backward parity: empty experts, no shared expert")
-    P, layer, y, sv, wt, dy, dx, gr = _run(wl)
+    P, layer, y, sv, dy, dx, gr = _run(wl)
     counts = host(sv["counts"])
     assert (counts == 0).sum() >= 4
     ref = _oracle(wl, P, sv, dy)
@@ -142,7 +135,7 @@ def test_backward_empty_experts_and_no_shared():
 def test_backward_single_token_and_zero_tokens():
     wl = TRAIN_SMALL
     _log("backward parity: T = 1")
-    P, layer, y, sv, wt, dy, dx, gr = _run(wl, T=1)
+    P, layer, y, sv, dy, dx, gr = _run(wl, T=1)
     ref = _oracle(wl, P, sv, dy)
     _check_grads(wl, sv, dx, gr, ref)
     _log("backward: T = 0 zero-fills the weight gradients")
@@ -167,7 +160,7 @@ def test_backward_v3_sampled():
     gradient of the cold expert, and rows of the shared expert's gradients."""
     wl = CONFIGS["v3_prefill_bf16"]
     _log("backward V3 sampled: running the layer")
-    P, layer, y, sv, wt, dy, dx, gr = _run(wl)
+    P, layer, y, sv, dy, dx, gr = _run(wl)
     x = host(P["x"])
     wr = host(P["w_router"])
     logits = host(sv["logits"])
