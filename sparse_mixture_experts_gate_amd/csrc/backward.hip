@@ -266,17 +266,31 @@ __global__ __launch_bounds__(kRowT) void router_wgrad_kernel(
   const int ch = blockIdx.x * kRowT + threadIdx.x;
   if (ch * 8 >= d) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int r1 = offsets[e + 1];
-  for (int r = offsets[e]; r < r1; ++r) {
-    const float u = du_perm[r];
-    const uint4 v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(perm[r]) * d + ch * 8);
+  auto add_row = [&](float u, uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[2 * j] += u * __uint_as_float(w[j] << 16);
       acc[2 * j + 1] += u * __uint_as_float(w[j] & 0xFFFF0000u);
     }
+  };
+  const uint16_t* xc = x + ch * 8;
+  const int r1 = offsets[e + 1];
+  int r = offsets[e];
+  // four rows in flight per iteration; they are added in row order
+  for (; r + 4 <= r1; r += 4) {
+    uint4 v[4];
+    float u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(perm[r + i]) * d);
+      u[i] = du_perm[r + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) add_row(u[i], v[i]);
   }
+  for (; r < r1; ++r)
+    add_row(du_perm[r], *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(perm[r]) * d));
   float* out = dwr + static_cast<int64_t>(e) * d + ch * 8;
   *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
