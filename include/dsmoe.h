@@ -254,7 +254,7 @@ typedef struct moe_saved {
 } moe_saved;
 
 /* deepseek_moe_forward that also fills `saved` (every field required; h and
- * gu only when Is > 0 covers the shared rows too). Same workspace as
+ * gu have TK + T rows when Is > 0, TK rows otherwise). Same workspace as
  * deepseek_moe_forward. */
 moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const float* w_router,
                              const float* bias, const moe_weights* w, void* y,
