@@ -234,7 +234,7 @@ def train_record(wl, T: int, r: dict) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
