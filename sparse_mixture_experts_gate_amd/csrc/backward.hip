@@ -19,8 +19,9 @@
 //   combine: dx_t = dA_s[t] + sum_k dA[inv[t,k]] + sum_k du_tk Wr[e_tk];
 //   router:  dWr[e] = sum over e's rows of du x;
 //   wgrad:   dW13_e = [da | db]_e^T A_e, dW2_e = dYp_e^T H_e, as GEMMs whose
-//            contraction runs over the expert's tokens, on token-major copies
-//            of the operands with every segment padded to 64 tokens.
+//            contraction runs over the expert's tokens: both operands are
+//            read k-major from their row layouts (A_e from a gathered copy
+//            of x), each bounded to the expert's rows.
 #include "device_common.h"
 #include "internal.h"
 #include "tile_schedule.h"
@@ -30,114 +31,6 @@
 namespace dsmoe {
 
 namespace {
-
-// ---- token-major copies --------------------------------------------------
-
-constexpr int kTr = 64;       // tile edge
-constexpr int kTrPitch = 66;  // LDS row pitch (elements): 132-byte rows keep the
-                              // four 16-row groups of a column read on distinct banks
-
-// Token-major copy for the weight-gradient GEMMs: dst[c][p] (row stride ldp)
-// for c < cols. Column p of routed segment g (g < E) at i = p - poff[g] takes
-// row (perm ? perm[offsets[g] + i] : offsets[g] + i) of src (row stride ld)
-// when i < R_g; column p of the shared segment (g == E) takes row i < T of
-// src_s (row stride ld_s); every other column is zero. Segments start at
-// multiples of 64, so one 64-column tile lies in one segment.
-__global__ __launch_bounds__(256) void token_major_kernel(
-    const uint16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm,
-    const uint16_t* __restrict__ src_s, int64_t ld_s, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ poff, int E, int G, int64_t T, int cols, int64_t ldp,
-    uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTr * kTrPitch];
-  __shared__ const uint16_t* rowp[kTr];
-  __shared__ int gsh;
-  const int tid = threadIdx.x;
-  const int p0 = blockIdx.x * kTr, c0 = blockIdx.y * kTr;
-  if (p0 >= poff[G]) return;
-  if (tid == 0) {
-    int lo = 0, hi = G - 1;  // last segment starting at or before p0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
-    }
-    gsh = lo;
-  }
-  __syncthreads();
-  const int g = gsh;
-  if (tid < kTr) {
-    const int64_t i = static_cast<int64_t>(p0) + tid - poff[g];
-    const uint16_t* p = nullptr;
-    if (g < E) {
-      const int base = offsets[g];
-      if (i < offsets[g + 1] - base) {
-        const int64_t row = perm ? perm[base + i] : base + i;
-        p = src + row * ld;
-      }
-    } else if (i < T) {
-      p = src_s + i * ld_s;
-    }
-    rowp[tid] = p;
-  }
-  __syncthreads();
-  {
-    const int r = tid >> 2, cc = (tid & 3) * 16;
-    const uint16_t* sp = rowp[r];
-    uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + r * kTrPitch + cc);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (sp) v = *reinterpret_cast<const uint4*>(sp + c0 + cc + 8 * h);
-      t32[4 * h + 0] = v.x;
-      t32[4 * h + 1] = v.y;
-      t32[4 * h + 2] = v.z;
-      t32[4 * h + 3] = v.w;
-    }
-  }
-  __syncthreads();
-  const int c = tid >> 2, pp = (tid & 3) * 16;
-  uint16_t* out = dst + static_cast<int64_t>(c0 + c) * ldp + p0 + pp;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 8 * h + 2 * j;
-      w[j] = static_cast<uint32_t>(tile[(pp + i) * kTrPitch + c]) |
-             (static_cast<uint32_t>(tile[(pp + i + 1) * kTrPitch + c]) << 16);
-    }
-    *reinterpret_cast<uint4*>(out + 8 * h) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// poff[g]: start of segment g in the token-major operands. Routed segment g
-// spans max(1, ceil(R_g / 64)) * 64 columns (an empty expert keeps one block
-// of zeros, so its weight gradient comes out as zeros from the same GEMM),
-// the shared segment ceil(T / 64) * 64.
-constexpr int kPlanT = 1024;
-__global__ __launch_bounds__(kPlanT) void wgrad_plan_kernel(const int32_t* __restrict__ offsets,
-                                                            int E, int64_t T, int shared,
-                                                            int32_t* __restrict__ poff) {
-  __shared__ int v[kPlanT];
-  const int tid = threadIdx.x;
-  int len = 0;
-  if (tid < E) {
-    const int r = offsets[tid + 1] - offsets[tid];
-    len = max(1, (r + 63) / 64) * 64;
-  } else if (tid == E && shared) {
-    len = static_cast<int>((T + 63) / 64) * 64;
-  }
-  v[tid] = len;
-  __syncthreads();
-  for (int o = 1; o < kPlanT; o <<= 1) {
-    const int add = tid >= o ? v[tid - o] : 0;
-    __syncthreads();
-    v[tid] += add;
-    __syncthreads();
-  }
-  const int G = E + (shared ? 1 : 0);
-  if (tid == 0) poff[0] = 0;
-  if (tid < G) poff[tid + 1] = v[tid];
-}
 
 // ---- gate and router gradients -------------------------------------------
 
@@ -340,7 +233,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
     op.rb = rsrc4(W, static_cast<uint32_t>(a.d) * ld_bytes);
     // columns past Ig (last column tile) read neighbouring data or zeros;
     // they only reach output columns that are not stored
-    kmajor_offsets<C>(op.bo, c.n * C::BN, ld_bytes);
+    kmajor_offsets<C::BN, C::B_LOADS, C::NT>(op.bo, c.n * C::BN, ld_bytes);
     op.kstep_b = BK * ld_bytes;
     op.nk = nk;
   };
@@ -425,7 +318,7 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad1_bf16_kernel(BwdArgs a) 
                                  : static_cast<const uint16_t*>(a.w13) +
                                        static_cast<int64_t>(c.g) * 2 * a.I * a.d;
     op.rb = rsrc4(W, static_cast<uint32_t>(2 * Ig) * ld_bytes);
-    kmajor_offsets<C>(op.bo, c.n * C::BN, ld_bytes);
+    kmajor_offsets<C::BN, C::B_LOADS, C::NT>(op.bo, c.n * C::BN, ld_bytes);
     op.kstep_b = BK * ld_bytes;
     op.nk = 2 * Ig / BK;
   };
@@ -458,41 +351,39 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad1_bf16_kernel(BwdArgs a) 
       lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
-// Weight gradients out_g = A_g B_g^T (fp32) per group g: A_g rows m < M_g and
-// B_g rows n < N_g of the token-major operands at, bt (row stride ldp), over
-// the columns [poff[g], poff[g+1]) of segment g. Tiles: ceil(M/BM) x
-// ceil(N/BN) per group, routed groups first, the shared group last. Inside a
-// group, tiles go in rows of kSuperM m-tiles, m fastest within a row: the 32
-// consecutive tiles one XCD runs at a time (8 m-tiles x 4 n-tiles) then read
-// 8 A panels and 4 B panels, the fewest panel bytes for 32 tiles, where an
-// n-fastest order reads one A panel against every B panel of the expert,
-// more than the L2 keeps, once per m-tile.
+// Weight gradients out_g = A_g^T B_g (fp32) per group g, contracting over
+// the group's rows (tokens): A_g = rows offsets[g] .. offsets[g+1] - 1 of a
+// (the shared group: rows 0 .. T - 1 of a_s), columns m < M_g; B_g likewise
+// from b / b_s, columns n < N_g. Both operands are k-major (a k-step is 64
+// consecutive rows) and read by transpose reads. Each group's operands are
+// buffer resources that start at the group's first row and end at its last,
+// so the rows of the last k-step past the segment read as zeros in hardware
+// (an empty group reads one k-step of zeros and stores zeros).
+// Tiles: ceil(M/BM) x ceil(N/BN) per group, routed groups first, the shared
+// group last; inside a group, rows of kSuperM m-tiles, m fastest: the 32
+// consecutive tiles one XCD runs at a time read 8 A panels and 4 B panels,
+// where an n-fastest order reads one A panel against every B panel of the
+// expert, more than the L2 keeps, once per m-tile.
 constexpr int kSuperM = 8;
 
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  __shared__ int sp[kMaxGroups + 1];
+  __shared__ int soff[kMaxGroups + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int r0 = tid >> 3;
-  const int G = w.E + (w.shared ? 1 : 0);
-  for (int i = tid; i <= G; i += C::NT) sp[i] = w.poff[i];
+  for (int i = tid; i <= w.E; i += C::NT) soff[i] = w.offsets[i];
   __syncthreads();
-  const int tn = (w.N + C::BN - 1) / C::BN, tpr = ((w.M + C::BM - 1) / C::BM) * tn;
-  const int tns = (w.Ns + C::BN - 1) / C::BN;
-  const int total = w.E * tpr + (w.shared ? ((w.Ms + C::BM - 1) / C::BM) * tns : 0);
+  const int tn = (w.N + C::BN - 1) / C::BN, tm = (w.M + C::BM - 1) / C::BM, tpr = tm * tn;
+  const int tns = (w.Ns + C::BN - 1) / C::BN, tms = (w.Ms + C::BM - 1) / C::BM;
+  const int total = w.E * tpr + (w.shared ? tms * tns : 0);
   const int nb = gridDim.x;
   const int first = xcd_logical_block(blockIdx.x, nb);
   if (first >= total) return;
-  const uint32_t row_bytes = static_cast<uint32_t>(w.ldp) * 2u;
-  const i32x4_t ra = rsrc4(w.at, static_cast<uint32_t>(w.a_rows) * row_bytes);
-  const i32x4_t rb = rsrc4(w.bt, static_cast<uint32_t>(w.b_rows) * row_bytes);
 
-  const int tm = tpr / tn, tms = (w.Ms + C::BM - 1) / C::BM;
   struct Coord {
-    int g, mt, nt, M, N;
+    int g, mt, nt, M, N, rows, row0;
   };
   auto coord = [&](int tile) {
     Coord c;
@@ -502,6 +393,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
       rem = tile - c.g * tpr;
       c.M = w.M;
       c.N = w.N;
+      // wave-uniform: the operands' buffer descriptors live in scalar registers
+      c.row0 = __builtin_amdgcn_readfirstlane(soff[c.g]);
+      c.rows = __builtin_amdgcn_readfirstlane(soff[c.g + 1]) - c.row0;
       ntm = tm;
       ntn = tn;
     } else {
@@ -509,6 +403,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
       c.g = w.E;
       c.M = w.Ms;
       c.N = w.Ns;
+      c.row0 = 0;
+      c.rows = static_cast<int>(w.T);
       ntm = tms;
       ntn = tns;
     }
@@ -520,29 +416,23 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
     c.mt = gr * kSuperM + (r2 - c.nt * sm);
     return c;
   };
+  auto k_steps = [](int rows) { return rows > BK ? (rows + BK - 1) / BK : 1; };
   auto next_ops = [&](int tile, int, StreamOps<C>& op) {
     const Coord c = coord(tile);
-    const uint32_t kbase = static_cast<uint32_t>(sp[c.g]) * 2u;
-#pragma unroll
-    for (int p = 0; p < C::A_LOADS; ++p) {
-      const int m = c.mt * C::BM + r0 + p * C::RPP;
-      op.ao[p] = m < c.M ? static_cast<uint32_t>(m) * row_bytes + kbase : kInvalidRow;
-    }
-#pragma unroll
-    for (int p = 0; p < C::B_LOADS; ++p) {
-      const int n = c.nt * C::BN + r0 + p * C::RPP;
-      op.bo[p] = n < c.N ? static_cast<uint32_t>(n) * row_bytes + kbase : kInvalidRow;
-    }
-    op.ra = ra;
-    op.rb = rb;
-    swizzle_rows<C>(op.ao);
-    swizzle_rows<C>(op.bo);
-    op.nk = (sp[c.g + 1] - sp[c.g]) / BK;
+    const bool sh = c.g == w.E;
+    const uint16_t* A = static_cast<const uint16_t*>(sh ? w.a_s : w.a);
+    const uint16_t* B = static_cast<const uint16_t*>(sh ? w.b_s : w.b);
+    const int64_t lda = sh ? w.lda_s : w.lda, ldb = sh ? w.ldb_s : w.ldb;
+    const uint32_t la = static_cast<uint32_t>(lda) * 2u, lb = static_cast<uint32_t>(ldb) * 2u;
+    op.ra = rsrc4(A + c.row0 * lda, static_cast<uint32_t>(c.rows) * la);
+    op.rb = rsrc4(B + c.row0 * ldb, static_cast<uint32_t>(c.rows) * lb);
+    kmajor_offsets<C::BM, C::A_LOADS, C::NT>(op.ao, c.mt * C::BM, la);
+    kmajor_offsets<C::BN, C::B_LOADS, C::NT>(op.bo, c.nt * C::BN, lb);
+    op.kstep_a = BK * la;
+    op.kstep_b = BK * lb;
+    op.nk = k_steps(c.rows);
   };
-  auto nk_of = [&](int tile) {
-    const Coord c = coord(tile);
-    return (sp[c.g + 1] - sp[c.g]) / BK;
-  };
+  auto nk_of = [&](int tile) { return k_steps(coord(tile).rows); };
   // acc in the unswapped layout: lane l owns column l % 32 of each 32 x 32
   // product, so one register across the wave stores two 128-byte row pieces.
   // Buffer stores with out-of-range offsets for the masked entries: every
@@ -572,8 +462,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
   };
   constexpr int kStores = C::MI * C::NJ * 16;
   constexpr int kPost = kInflight<C> + kStores < 63 ? kInflight<C> + kStores : 63;
-  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, false, kPost>(
-      lds, first, nb, total, next_ops, nk_of, epilogue);
+  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, false, kPost,
+              true, true>(lds, first, nb, total, next_ops, nk_of, epilogue);
 }
 
 template <class K>
@@ -585,25 +475,6 @@ int occupancy_of(K kernel, int threads) {
 }
 
 }  // namespace
-
-hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanT), 0, s, offsets, E, T,
-                     shared ? 1 : 0, poff);
-  return hipGetLastError();
-}
-
-hipError_t launch_token_major(const void* src, int64_t ld, const int32_t* perm, const void* src_s,
-                              int64_t ld_s, const int32_t* offsets, const int32_t* poff, int E,
-                              bool shared, int64_t T, int cols, int64_t ldp, void* dst,
-                              hipStream_t s) {
-  if (ldp == 0 || cols == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(ldp / kTr), static_cast<unsigned>(cols / kTr));
-  hipLaunchKernelGGL(token_major_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),
-                     ld, perm, static_cast<const uint16_t*>(src_s), ld_s, offsets, poff, E,
-                     E + (shared ? 1 : 0), T, cols, ldp, static_cast<uint16_t*>(dst));
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_gate(const void* dy, const void* yperm, const int32_t* idx,
                            const int32_t* inv, const float* gate, const float* logits, int64_t T,

@@ -366,15 +366,6 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
 
 // ---- training ---------------------------------------------------------------
 
-// Upper bound of the padded token columns of the weight-gradient operands:
-// every routed segment rounds up to a multiple of 64 (an empty one keeps 64),
-// the shared segment too.
-int64_t wgrad_pmax(const moe_layer_desc* d) {
-  const int64_t TK = d->T * d->top_k;
-  const int64_t P = TK + 64 * int64_t(d->n_experts) + (d->shared_inter > 0 ? d->T + 63 : 0);
-  return ((P + 63) / 64) * 64;
-}
-
 moe_status validate_train(const moe_layer_desc* d) {
   moe_status st = validate_desc(d);
   if (st) return st;
@@ -388,8 +379,6 @@ moe_status validate_train(const moe_layer_desc* d) {
     return fail(MOE_ERR_UNSUPPORTED, "T*K*d*2 must be < 2^31 bytes for training");
   if ((TK + d->T) * 2 * ldh * 2 > lim)
     return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*2*max(I,Is)*2 must be < 2^31 bytes for training");
-  if (wgrad_pmax(d) * std::max<int64_t>(d->d, 2 * ldh) * 2 > lim)
-    return fail(MOE_ERR_UNSUPPORTED, "the token-major gradient operands exceed 2^31 bytes");
   return MOE_OK;
 }
 
@@ -404,8 +393,7 @@ moe_status check_saved(const moe_layer_desc* d, const moe_saved* sv) {
 
 struct BwdLayout {
   int ldh;
-  int64_t pmax;
-  size_t tiles_h, tiles_d, poff, dyp, du, du_perm, dg, dap, das, xt, dyt, ht, dgt, bytes;
+  size_t tiles_h, tiles_d, dyp, du, du_perm, dg, dap, das, xperm, bytes;
 };
 
 BwdLayout bwd_layout(const moe_layer_desc* d) {
@@ -413,22 +401,17 @@ BwdLayout bwd_layout(const moe_layer_desc* d) {
   const int64_t T = d->T, TK = d->T * d->top_k;
   const int E = d->n_experts;
   L.ldh = std::max(d->inter, d->shared_inter);
-  L.pmax = wgrad_pmax(d);
   const int64_t hrows = TK + (d->shared_inter > 0 ? T : 0);
   Carver c;
   L.tiles_h = c.take(sizeof(int32_t) * (E + 2));
   L.tiles_d = c.take(sizeof(int32_t) * (E + 2));
-  L.poff = c.take(sizeof(int32_t) * (E + 2));
   L.dyp = c.take(size_t(TK) * d->d * 2);
   L.du = c.take(sizeof(float) * size_t(TK));
   L.du_perm = c.take(sizeof(float) * size_t(TK));
   L.dg = c.take(size_t(hrows) * 2 * L.ldh * 2);
   L.dap = c.take(size_t(TK) * d->d * 2);
   L.das = c.take(d->shared_inter > 0 ? size_t(T) * d->d * 2 : 0);
-  L.xt = c.take(size_t(d->d) * L.pmax * 2);
-  L.dyt = c.take(size_t(d->d) * L.pmax * 2);
-  L.ht = c.take(size_t(L.ldh) * L.pmax * 2);
-  L.dgt = c.take(size_t(2 * L.ldh) * L.pmax * 2);
+  L.xperm = c.take(size_t(TK) * d->d * 2);
   L.bytes = c.off;
   return L;
 }
@@ -803,17 +786,13 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
                 L.bytes, ws_bytes);
   int32_t* tiles_h = at<int32_t>(ws, L.tiles_h);
   int32_t* tiles_d = at<int32_t>(ws, L.tiles_d);
-  int32_t* poff = at<int32_t>(ws, L.poff);
   void* dyp = at<void>(ws, L.dyp);
   float* du = at<float>(ws, L.du);
   float* du_perm = at<float>(ws, L.du_perm);
   void* dgb = at<void>(ws, L.dg);
   void* dap = at<void>(ws, L.dap);
   void* das = shared ? at<void>(ws, L.das) : nullptr;
-  void* xt = at<void>(ws, L.xt);
-  void* dyt = at<void>(ws, L.dyt);
-  void* ht = at<void>(ws, L.ht);
-  void* dgt = at<void>(ws, L.dgt);
+  void* xperm = at<void>(ws, L.xperm);
   const int ldh = L.ldh;
 
   // tile tables: 128-row tiles over 256-column tiles of Ig (dgrad2) and d (dgrad1)
@@ -829,7 +808,6 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   pp.bm2 = 128;
   pp.bn2 = 256;
   HIP_TRY(launch_plan(nullptr, sv->offsets, nullptr, tiles_h, tiles_d, pp, stream), "plan");
-  HIP_TRY(launch_wgrad_plan(sv->offsets, E, T, shared, poff, stream), "wgrad plan");
   HIP_TRY(launch_bwd_gate(dy, sv->y_perm, sv->topk_idx, sv->inv, sv->topk_gate, sv->logits, T, K,
                           E, d, dyp, du, du_perm, stream),
           "gate gradients");
@@ -860,31 +838,22 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
           "input gradient");
   HIP_TRY(launch_router_wgrad(x, sv->perm, sv->offsets, du_perm, E, d, g->dw_router, stream),
           "router weight gradient");
-  // token-major operands of the weight-gradient GEMMs
-  const int64_t P = L.pmax;
-  const uint16_t* h16 = static_cast<const uint16_t*>(sv->h);
+  // weight gradients: contractions over each expert's rows; A_e of the
+  // gate/up projection is x gathered into the routed order
+  HIP_TRY(launch_gather_rows(x, T, sv->perm, TK, int64_t(d) * 2, xperm, stream), "gather x");
   const uint16_t* dg16 = static_cast<const uint16_t*>(dgb);
-  HIP_TRY(launch_token_major(x, d, sv->perm, x, d, sv->offsets, poff, E, shared, T, d, P, xt,
-                             stream),
-          "token-major x");
-  HIP_TRY(launch_token_major(dyp, d, nullptr, dy, d, sv->offsets, poff, E, shared, T, d, P, dyt,
-                             stream),
-          "token-major dy");
-  HIP_TRY(launch_token_major(h16, ldh, nullptr, h16 + TK * ldh, ldh, sv->offsets, poff, E, shared,
-                             T, ldh, P, ht, stream),
-          "token-major h");
-  HIP_TRY(launch_token_major(dg16, 2 * ldh, nullptr, dg16 + TK * 2 * ldh, 2 * ldh, sv->offsets,
-                             poff, E, shared, T, 2 * ldh, P, dgt, stream),
-          "token-major dG");
+  const uint16_t* h16 = static_cast<const uint16_t*>(sv->h);
   WgradArgs w1{};
-  w1.poff = poff;
+  w1.offsets = sv->offsets;
   w1.E = E;
+  w1.T = T;
   w1.shared = shared;
-  w1.ldp = P;
-  w1.at = dgt;
-  w1.bt = xt;
-  w1.a_rows = 2 * ldh;
-  w1.b_rows = d;
+  w1.a = dg16;
+  w1.a_s = dg16 + TK * 2 * ldh;
+  w1.lda = w1.lda_s = 2 * int64_t(ldh);
+  w1.b = xperm;
+  w1.b_s = x;
+  w1.ldb = w1.ldb_s = d;
   w1.M = 2 * I;
   w1.N = d;
   w1.Ms = 2 * Is;
@@ -893,14 +862,16 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   w1.out_s = g->dws13;
   HIP_TRY(launch_wgrad_bf16(w1, stream), "weight gradient of the gate/up projection");
   WgradArgs w2{};
-  w2.poff = poff;
+  w2.offsets = sv->offsets;
   w2.E = E;
+  w2.T = T;
   w2.shared = shared;
-  w2.ldp = P;
-  w2.at = dyt;
-  w2.bt = ht;
-  w2.a_rows = d;
-  w2.b_rows = ldh;
+  w2.a = dyp;
+  w2.a_s = dy;
+  w2.lda = w2.lda_s = d;
+  w2.b = h16;
+  w2.b_s = h16 + TK * ldh;
+  w2.ldb = w2.ldb_s = ldh;
   w2.M = d;
   w2.N = I;
   w2.Ms = d;

@@ -109,17 +109,17 @@ struct StreamOps {
   i32x4_t ra, rb;
   uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
   int nk;
-  uint32_t kstep_b;  // k-major B only: bytes between consecutive k-steps
+  uint32_t kstep_a, kstep_b;  // k-major operands only: bytes between k-steps
 };
 
-// ---- k-major B operand (weights [K, N] row-major, read without a transpose)
+// ---- k-major operands ([K, N] row-major: the k-step is BK consecutive rows)
 //
-// Stage image: BK rows (k) of BN elements (n); 16-byte chunk c of row k
-// sits at position c ^ (4 (k & 3)). Every load pass keeps the same LDS
-// placement as the row-major stage (one 16-byte chunk per thread, threads
-// in order), so only the thread -> (k, chunk) assignment differs: thread t
-// of pass p loads row p * (NT * 8 / BN) + t / (BN / 8), logical chunk
-// (t % (BN / 8)) ^ (4 (row & 3)).
+// Stage image of a k-major operand of width W (BN for B, BM for A): BK rows
+// (k) of W elements; 16-byte chunk c of row k sits at position c ^ (4 (k & 3)).
+// Every load pass keeps the LDS placement of the row-major stage (one
+// 16-byte chunk per thread, threads in order), so only the thread ->
+// (k, chunk) assignment differs: thread t of pass p loads row
+// p * (NT * 8 / W) + t / (W / 8), logical chunk (t % (W / 8)) ^ (4 (row & 3)).
 //
 // Fragments come from ds_read_b64_tr_b16: in each 16-lane group, lane i
 // receives element i % 4 of the 8-byte pieces that lanes 4j + i / 4
@@ -130,40 +130,33 @@ struct StreamOps {
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-template <class C>
-__device__ __forceinline__ uint32_t kmajor_chunk(int t) {
-  constexpr int CPR = C::BN / 8;  // chunks per row
-  const int row = t / CPR;
-  return static_cast<uint32_t>((t % CPR) ^ (4 * (row & 3)));
-}
-
-// Global byte offsets of thread t's k-major B chunks for k-step 0: row r of
-// pass p is k = r, at `ld_bytes` per k; `col0` is the tile's first column.
-template <class C>
-__device__ __forceinline__ void kmajor_offsets(uint32_t (&o)[C::B_LOADS], int col0,
-                                               uint32_t ld_bytes) {
-  constexpr int CPR = C::BN / 8, RPASS = C::NT / CPR;
-  static_assert(C::NT % CPR == 0 && C::B_LOADS * RPASS == BK, "passes cover the k-step");
+// Global byte offsets of thread t's chunks of a k-major operand of width W
+// for k-step 0 (row r of the step at r * ld_bytes; `col0` is the tile's
+// first column); LOADS passes of NT threads.
+template <int W, int LOADS, int NT>
+__device__ __forceinline__ void kmajor_offsets(uint32_t (&o)[LOADS], int col0, uint32_t ld_bytes) {
+  constexpr int CPR = W / 8, RPASS = NT / CPR;
+  static_assert(NT % CPR == 0 && LOADS * RPASS == BK, "passes cover the k-step");
   const int t = threadIdx.x;
+  const int row = t / CPR;
+  const uint32_t chunk = static_cast<uint32_t>((t % CPR) ^ (4 * (row & 3)));
 #pragma unroll
-  for (int p = 0; p < C::B_LOADS; ++p) {
-    const int k = p * RPASS + t / CPR;
-    o[p] = static_cast<uint32_t>(k) * ld_bytes +
-           static_cast<uint32_t>(col0 + kmajor_chunk<C>(t) * 8) * 2u;
-  }
+  for (int p = 0; p < LOADS; ++p)
+    o[p] = static_cast<uint32_t>(p * RPASS + row) * ld_bytes +
+           static_cast<uint32_t>(col0 + chunk * 8) * 2u;
 }
 
 // The MFMA operand of columns [n0, n0 + 32) and k [k0, k0 + 16) (lane l:
-// column n0 + l % 32, k0 + 8 (l / 32) .. + 7) from a k-major stage at LDS
-// byte address bs.
-template <class C>
-__device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t bs, int n0, int k0, int lane) {
+// column n0 + l % 32, k0 + 8 (l / 32) .. + 7) from a k-major stage of width
+// W at LDS byte address base.
+template <int W>
+__device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t base, int n0, int k0, int lane) {
   const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
   const int n = n0 + 16 * (g & 1) + 4 * q;
   const int k = k0 + 8 * (g >> 1) + j;
   const int chunk = (n >> 3) ^ (4 * j);  // k & 3 == j
-  const uint32_t a0 = bs + static_cast<uint32_t>(k * C::BN + chunk * 8 + (n & 4)) * 2u;
-  const uint32_t a1 = a0 + 4u * C::BN * 2u;  // rows k + 4: same swizzle
+  const uint32_t a0 = base + static_cast<uint32_t>(k * W + chunk * 8 + (n & 4)) * 2u;
+  const uint32_t a1 = a0 + 4u * W * 2u;  // rows k + 4: same swizzle
   const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a0);
   const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a1);
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
@@ -187,6 +180,8 @@ __device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t bs, int n0, int k0, int
 //     columns; without it lane l owns output column l % 32 and rows
 //     acc_row(l, r), so that one register across the wave is two 128-byte
 //     row pieces (full cache lines for fp32 outputs).
+// BKM / AKM: B / A is k-major (offsets from kmajor_offsets, advanced by
+// ops.kstep_b / ops.kstep_a per k-step, fragments by transpose reads).
 // POST >= 0 lets the epilogue's stores drain during the next tile's first
 // step: that step's wait allows POST operations in flight instead of
 // kInflight<C>, which is exact only if every epilogue call issues at least
@@ -202,7 +197,7 @@ __device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t bs, int n0, int k0, int
 // fragments are already in registers, so that the next stage's first
 // fragments are read while those MFMAs run.
 template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, bool SWAP = true,
-          int POST = -1, bool BKM = false>
+          int POST = -1, bool BKM = false, bool AKM = false>
 __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
                                             NextOps&& next_ops, NkOf&& nk_of,
                                             Epilogue&& epilogue) {
@@ -221,8 +216,9 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
   bool more = true;
   next_ops(ti, index, op);
   auto issue = [&](int st) {
-    const uint32_t ka = static_cast<uint32_t>(ki) * (BK * 2);
-    const uint32_t kb = BKM ? static_cast<uint32_t>(ki) * op.kstep_b : ka;
+    const uint32_t kn = static_cast<uint32_t>(ki) * (BK * 2);
+    const uint32_t ka = AKM ? static_cast<uint32_t>(ki) * op.kstep_a : kn;
+    const uint32_t kb = BKM ? static_cast<uint32_t>(ki) * op.kstep_b : kn;
     stage_issue<C>(lds0, st, wave, op.ra, op.ao, ka, op.rb, op.bo, kb);
     if (more) ++ki;
   };
@@ -247,15 +243,20 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) {
       if constexpr (BKM)
-        bfr[buf][nj] = frag_kmajor<C>(lds_addr(Bs), b_local_row<C, SWIGLU>(wn, nj), kk * 16, lane);
+        bfr[buf][nj] =
+            frag_kmajor<C::BN>(lds_addr(Bs), b_local_row<C, SWIGLU>(wn, nj), kk * 16, lane);
       else
         bfr[buf][nj] = *reinterpret_cast<const bf16x8_t*>(
             Bs + lds_off(b_local_row<C, SWIGLU>(wn, nj) + (lane & 31), chk));
     }
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
-          As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
+    for (int mi = 0; mi < C::MI; ++mi) {
+      if constexpr (AKM)
+        af[buf][mi] = frag_kmajor<C::BM>(lds_addr(As), wm * C::WM + mi * 32, kk * 16, lane);
+      else
+        af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(
+            As + lds_off(wm * C::WM + mi * 32 + (lane & 31), chk));
+    }
   };
   f32x16_t acc[C::MI][C::NJ];
   auto mma = [&](int buf) {

@@ -122,24 +122,20 @@ struct BwdArgs {
   void* das;               // [T, d] OUT of dgrad1: the shared expert's
 };
 struct WgradArgs {
-  const int32_t* poff;     // [G+1] segment starts in the token-major operands
+  const int32_t* offsets;  // [E+1] segment starts of the routed rows
   int E;
-  bool shared;             // a shared group follows the E routed ones
-  int64_t ldp;             // row stride (elements) of at and bt
-  const void* at;          // [a_rows, ldp] bf16
-  const void* bt;          // [b_rows, ldp] bf16
-  int64_t a_rows, b_rows;
-  int M, N;                // routed group output [M, N]
-  int Ms, Ns;              // shared group output [Ms, Ns]
+  int64_t T;
+  bool shared;             // a shared group (rows 0 .. T-1 of a_s, b_s) follows
+  const void* a;           // routed rows [TK, lda] bf16 (row = token)
+  const void* a_s;         // shared rows [T, lda_s]
+  const void* b;           // routed rows [TK, ldb]
+  const void* b_s;         // shared rows [T, ldb_s]
+  int64_t lda, lda_s, ldb, ldb_s;
+  int M, N;                // routed group output [M, N]: A columns x B columns
+  int Ms, Ns;              // shared group output
   float* out;              // [E, M, N]
   float* out_s;            // [Ms, Ns]
 };
-hipError_t launch_wgrad_plan(const int32_t* offsets, int E, int64_t T, bool shared, int32_t* poff,
-                             hipStream_t s);
-hipError_t launch_token_major(const void* src, int64_t ld, const int32_t* perm, const void* src_s,
-                              int64_t ld_s, const int32_t* offsets, const int32_t* poff, int E,
-                              bool shared, int64_t T, int cols, int64_t ldp, void* dst,
-                              hipStream_t s);
 hipError_t launch_bwd_gate(const void* dy, const void* yperm, const int32_t* idx,
                            const int32_t* inv, const float* gate, const float* logits, int64_t T,
                            int K, int E, int d, void* dyp, float* du, float* du_perm,
