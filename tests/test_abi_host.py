@@ -134,7 +134,7 @@ def test_training_entry_points_validate_before_launch(L):
     n = ctypes.c_size_t(0)
     d = _desc(L)
     assert lib.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    # holds at least dY_perm, dG and the four token-major operands
+    # holds at least the gated output gradients [T*K, d] and [da | db] [T*(K+1), 2 max(I, Is)]
     assert n.value >= 64 * 2 * 256 * 2 + 64 * 3 * 256 * 2
     # fp32 and fp8 layers have no training path
     for kw in (dict(act_dtype=0, w_dtype=0), dict(w_dtype=2)):
