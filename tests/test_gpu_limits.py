@@ -114,3 +114,32 @@ def test_backward_at_size_limit():
     e2 = mat_rel_err(host(gr["dw2"][e]), dW2)
     _log(f"  expert {e} ({len(toks)} tokens): dw13 {e13:.2e} dw2 {e2:.2e}")
     assert e13 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_fp8_forward_at_size_limit():
+    # FP8 weights: H is one byte per element, so x (T * d * 2 bytes) binds
+    wl = WIDE.with_(name="limit_fp8", w="fp8")
+    T = _largest_T(wl, L.lib().moe_workspace_size)
+    assert T * wl.d * 2 < (1 << 31) and (T + 1) * wl.d * 2 >= (1 << 31) - 1
+    _log(f"fp8 forward at the size limit: T = {T}")
+    wl = wl.with_(T=T)
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    out = layer.forward(P["x"])
+    torch.cuda.synchronize()
+    logits, idx = host(out["logits"]), host(out["topk_idx"])
+    rr = O.route(logits, host(P["bias"]), **route_args(wl))
+    assert np.array_equal(idx, rr.idx)
+    pr = O.permute(rr.idx, wl.E)
+    rows = _sample(T, pr.perm)
+    q13 = [O.quantize_blocks_128(host(P["w13"][e])) for e in range(wl.E)]
+    q2 = [O.quantize_blocks_128(host(P["w2"][e])) for e in range(wl.E)]
+    ws13q, ws13s = O.quantize_blocks_128(host(P["ws13"]))
+    ws2q, ws2s = O.quantize_blocks_128(host(P["ws2"]))
+    x = host(P["x"][torch.as_tensor(rows, device=DEV)])
+    ref = O.layer_output_fp8(x, rr.idx[rows], rr.gate[rows], [q[0] for q in q13],
+                             [q[1] for q in q13], [q[0] for q in q2], [q[1] for q in q2],
+                             ws13q, ws13s, ws2q, ws2s)
+    err = row_rel_err(host(out["y"][torch.as_tensor(rows, device=DEV)]), ref)
+    _log(f"  tokens {rows.tolist()}: max row-rel err {err:.2e}")
+    assert err <= TOL["fp8"]
