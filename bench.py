@@ -189,6 +189,56 @@ def cpu_baseline(wl, P, n_tokens: int) -> dict:
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def achievable_peaks() -> dict:
+    """Microbenchmarked peaks of this GPU (libdsmoe_microbench.so, hand-written
+    HIP kernels): streaming reads far beyond the 256 MB Infinity Cache, once
+    into registers (4 GiB) and once over the layer's own LDS-DMA load path
+    (2 GiB), and back-to-back independent MFMAs with operands in registers,
+    bf16 32x32x16 and FP8 32x32x64. Each is the best of 3 timed launches
+    after a warm-up launch."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "libdsmoe_microbench.so")
+    mb = ctypes.CDLL(path)
+    mb.dsmoe_mb_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    mb.dsmoe_mb_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    mb.dsmoe_mb_hbm_dma.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    blocks = cus * 16
+    sink = torch.empty(blocks * 256 * 4, dtype=torch.uint8, device="cuda")
+
+    def best(launch, reps=3):
+        launch()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = launch()
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"microbenchmark launch failed: {rc}")
+            times.append(a.elapsed_time(b) / 1e3)
+        return min(times)
+
+    t_read = best(lambda: mb.dsmoe_mb_hbm_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                               stream))
+    dma_bytes = (2 << 30) - 1024
+    t_dma = best(lambda: mb.dsmoe_mb_hbm_dma(buf.data_ptr(), dma_bytes, cus * 4, stream))
+    del buf
+    res = {"hbm_read_GBps": nbytes / t_read / 1e9, "hbm_dma_GBps": dma_bytes / t_dma / 1e9}
+    for name, fp8, iters, flops in (("mfma_bf16_TFLOPs", 0, 20000, 32768.0),
+                                    ("mfma_fp8_TFLOPs", 1, 10000, 131072.0)):
+        t = best(lambda: mb.dsmoe_mb_mfma(fp8, iters, blocks, sink.data_ptr(), stream))
+        res[name] = blocks * 4 * iters * 8 * flops / t / 1e12
+    return res
+
+
 def time_train(layer, x, steps: int, warmup: int) -> dict:
     """Training forward (moe_forward_train) and backward (moe_backward) back to
     back per step, each bracketed by HIP events on the current stream. dy is
@@ -298,6 +348,15 @@ def main() -> int:
                  "ms_per_launch": g1_ms, "alg_bytes_per_launch": alg["g1_bytes"],
                  "alg_flops_per_launch": alg["g1_flops"],
                  "mfma_frac": g1_fl / MFMA_PEAK[wl.w], "hbm_frac": g1_bw / HBM_PEAK})
+    if not args.no_extra:
+        ach = achievable_peaks()
+        log("achievable: " + json.dumps({k: round(v, 1) for k, v in ach.items()}))
+        if bound == "hbm":
+            hbm_ach = max(ach["hbm_read_GBps"], ach["hbm_dma_GBps"])
+            roof.update({"achievable_peak": hbm_ach, "frac_of_achievable": g1_bw / 1e9 / hbm_ach})
+        else:
+            key = "mfma_fp8_TFLOPs" if wl.w == "fp8" else "mfma_bf16_TFLOPs"
+            roof.update({"achievable_peak": ach[key], "frac_of_achievable": g1_fl / 1e12 / ach[key]})
     layer_mfma = alg["layer_flops"] / (ms / 1e3) / MFMA_PEAK[wl.w]
     layer_hbm = alg["layer_bytes"] / (ms / 1e3) / HBM_PEAK
     log(f"{wl.name}: {ms:.3f} ms/step, {tok_s/1e6:.3f} M tok/s, layer MFMA {layer_mfma:.1%}, "
@@ -308,6 +367,8 @@ def main() -> int:
              "layer_mfma_frac": layer_mfma, "layer_hbm_frac": layer_hbm,
              "n_touched_experts": n_touched, "near_tie_tokens": near,
              "near_tie_frac": near / wl.T, "max_over_mean_load": float(counts.max()) / (wl.T * wl.K / wl.E)}
+    if not args.no_extra:
+        extra["achievable_peaks"] = ach
     if not args.no_extra and wl.name == "v3_prefill_bf16":
         dec = {}
         for T in (16, 64, 256):
