@@ -36,6 +36,9 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .moe_oracle import sigmoid_f32
+
+F32 = np.float32
 F64 = np.float64
 
 __all__ = ["swiglu_expert_backward", "layer_backward", "LayerGrads"]
@@ -87,7 +90,9 @@ def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
                    experts=None) -> LayerGrads:
     """Gradients of L = sum <dy, y> for the layer with the selection fixed to
     ``topk_idx`` [T, K]; the gates are recomputed in fp64 from the fp32
-    ``logits`` [T, E] (g = s / S over the selected s). ``w13[e]``, ``w2[e]``
+    ``logits`` [T, E] (g = s / S over the selected s), except for tokens whose
+    fp32 score sum is zero (every selected logit below about -87), where the
+    forward's gates are the constant 1/K and the logits get no gradient. ``w13[e]``, ``w2[e]``
     may be lazy containers. ``experts`` (optional) restricts the routed weight
     gradients to those expert ids (the others stay zero); dx, dg and du need
     every routed expert of every token, so it is only for weight-gradient
@@ -102,7 +107,13 @@ def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
     E = wr.shape[0]
     s = _sigmoid64(np.take_along_axis(u, idx, axis=1))   # [T, K] selected scores
     S = s.sum(axis=1)
-    safe = S > 0
+    # the forward's rule: where the fp32 sum of the fp32 scores (slot order)
+    # is zero, the gates are the constant 1/K, so nothing flows to the logits
+    s32 = sigmoid_f32(np.take_along_axis(np.asarray(logits, F32), idx, axis=1))
+    S32 = np.zeros(T, F32)
+    for k in range(K):
+        S32 = (S32 + s32[:, k]).astype(F32)
+    safe = S32 > 0
     g = np.where(safe[:, None], s / np.where(safe, S, 1.0)[:, None], 1.0 / K)
 
     dx = np.zeros((T, d), F64)

@@ -224,3 +224,29 @@ def test_backward_v3_sampled():
         er = mat_rel_err(host(gr["dws2"][j]), ref_row)
         assert er <= tol, (j, er)
     _log("  shared-expert rows ok")
+
+
+def test_backward_zero_score_sum():
+    # every logit below -100: the fp32 scores are all zero, the forward's gates
+    # are the constant 1/K, so the router and the logits get no gradient while
+    # the experts still train with weight 1/K
+    wl = TRAIN_SMALL.with_(name="train_saturated", T=200)
+    _log("backward parity: zero score sum (gates 1/K)")
+    P = make_inputs(wl, DEV)
+    P["x"] = (P["x"].float().abs() + 0.5).to(torch.bfloat16).contiguous()
+    ramp = 1.0 + 0.01 * torch.arange(wl.E, device=DEV, dtype=torch.float32)
+    P["w_router"] = (-(200.0 / wl.d) * ramp[:, None]
+                     * torch.ones(wl.E, wl.d, device=DEV)).to(P["w_router"].dtype).contiguous()
+    layer = M.MoELayer(wl, P)
+    y, sv = layer.forward_train(P["x"])
+    dy = _dy(wl, wl.T)
+    dx, gr = layer.backward(P["x"], dy, sv)
+    torch.cuda.synchronize()
+    assert host(sv["logits"]).max() < -100.0
+    assert np.all(host(sv["topk_gate"]) == np.float32(1.0 / wl.K))
+    rr = O.route(host(sv["logits"]), host(P["bias"]), **route_args(wl))
+    assert np.array_equal(host(sv["topk_idx"]), rr.idx)
+    ref = _oracle(wl, P, sv, dy)
+    assert not ref.dw_router.any()
+    assert not host(gr["dw_router"]).any()
+    _check_grads(wl, sv, dx, gr, ref)

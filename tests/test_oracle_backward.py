@@ -136,3 +136,24 @@ def test_single_expert_dense_swiglu_backward():
     assert np.allclose(gr.dx, dX, rtol=0, atol=1e-13)
     assert np.array_equal(gr.dw13[0], dW13) and np.array_equal(gr.dw2[0], dW2)
     assert np.all(np.abs(gr.du) <= 1e-15)
+
+
+def test_zero_score_sum_gives_constant_gates():
+    # every selected logit far below -87: the fp32 scores underflow, the
+    # forward's gates are the constant 1/K, so the logits and the router get
+    # no gradient while the experts still do (with weight 1/K each)
+    p = _tiny(seed=13, T=5, d=8, E=6, K=2)
+    u = np.full((5, 6), -120.0)
+    gr = oracle.layer_backward(p["x"], p["wr"], u, p["idx"], p["w13"], p["w2"], p["ws13"],
+                               p["ws2"], p["dy"])
+    assert np.all(gr.du == 0) and np.all(gr.dw_router == 0)
+    e = int(p["idx"][0, 0])
+    dX, _, _, Y = oracle.swiglu_expert_backward(p["x"][:1], p["w13"][e], p["w2"][e],
+                                                 p["dy"][:1] / 2)
+    assert np.isclose(gr.dg[0, 0], np.sum(p["dy"][:1] * Y), rtol=1e-12)
+    # one logit back in range: the gates are s / S again and gradients flow
+    u[:, :] = -120.0
+    u[np.arange(5), p["idx"][:, 0]] = 0.5
+    gr2 = oracle.layer_backward(p["x"], p["wr"], u, p["idx"], p["w13"], p["w2"], p["ws13"],
+                                p["ws2"], p["dy"])
+    assert np.max(np.abs(gr2.du)) > 0
