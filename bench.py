@@ -149,13 +149,18 @@ def decode_record(wl, T: int, nt: int, warm: dict, cold: dict) -> dict:
 
 def traffic_record(kernel: str, workload: str):
     """HBM traffic measured by rocprofv3 counters for `kernel`, valid only while
-    the kernel source is unchanged since the counters were taken."""
+    the kernel's sources (every file its code comes from) are unchanged since
+    the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    # one digest over every source file of the kernel (comma-separated names)
+    h = hashlib.sha256()
+    for name in rec["source"].split(","):
+        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", name),
+                      "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
@@ -209,7 +214,7 @@ def achievable_peaks() -> dict:
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = 4 << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-    blocks = cus * 16
+    blocks = cus * 32
     sink = torch.empty(blocks * 256 * 4, dtype=torch.uint8, device="cuda")
 
     def best(launch, reps=3):
@@ -229,7 +234,7 @@ def achievable_peaks() -> dict:
     t_read = best(lambda: mb.dsmoe_mb_hbm_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
                                                stream))
     dma_bytes = (2 << 30) - 1024
-    t_dma = best(lambda: mb.dsmoe_mb_hbm_dma(buf.data_ptr(), dma_bytes, cus * 4, stream))
+    t_dma = best(lambda: mb.dsmoe_mb_hbm_dma(buf.data_ptr(), dma_bytes, cus * 5, stream))
     del buf
     res = {"hbm_read_GBps": nbytes / t_read / 1e9, "hbm_dma_GBps": dma_bytes / t_dma / 1e9}
     for name, fp8, iters, flops in (("mfma_bf16_TFLOPs", 0, 20000, 32768.0),

@@ -4,14 +4,15 @@
       Markdown table of a `rocprofv3 --kernel-trace --stats` run.
 
   python profile_summary.py traffic <fetch_counter_collection.csv>
-      <write_counter_collection.csv> <kernel-substring> <name> <workload> <source.hip>
+      <write_counter_collection.csv> <kernel-substring> <name> <workload> <sources>
       <out-dir> <command-fetch> <command-write>
       HBM bytes per dispatch of a kernel from FETCH_SIZE and WRITE_SIZE runs
       (KiB per dispatch), each scaled by what the same counter reads for the
       plain 1 GiB device copies (`__amd_rocclr_copyBuffer`) that
       `bench.py --calibrate-copy` runs first: the copy reads and writes
-      exactly 1 GiB. Writes <out-dir>/traffic_<name>_<workload>.json (read by
-      bench.py while the kernel source is unchanged) and a markdown summary.
+      exactly 1 GiB. <sources>: the kernel's files under csrc/, comma-separated.
+      Writes <out-dir>/traffic_<name>_<workload>.json (read by bench.py while
+      those files are unchanged) and a markdown summary.
 
   python profile_summary.py kernels <kernel_stats.csv> <fetch csv> <write csv>
       <mfma csv> <workload> <commands-file>
@@ -82,6 +83,17 @@ def _select(per, sub: str):
     return hits[0]
 
 
+def sources_sha256(source: str) -> str:
+    """One SHA-256 over the kernel's source files (comma-separated names under
+    csrc/, hashed in the order given), so that a change to any of them marks
+    the counters as stale. bench.py computes the same digest."""
+    h = hashlib.sha256()
+    for name in source.split(","):
+        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", name),
+                      "rb").read())
+    return h.hexdigest()
+
+
 def traffic(fetch_csv, write_csv, sub, name, workload, source, out_dir, cmd_f, cmd_w):
     pf, pw = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
     # the calibration copies are the three largest copy dispatches of each run
@@ -93,9 +105,8 @@ def traffic(fetch_csv, write_csv, sub, name, workload, source, out_dir, cmd_f, c
     _, wv = _select(pw, sub)
     rd = sum(fv) / len(fv) * f_scale * 1024
     wr = sum(wv) / len(wv) * w_scale * 1024
-    src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", source)
     rec = {"kernel": kname, "workload": workload, "source": source,
-           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "source_sha256": sources_sha256(source),
            "fetch_scale": f_scale, "write_scale": w_scale,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "bytes_per_launch": rd + wr, "dispatches": len(fv)}

@@ -29,10 +29,13 @@ namespace {
 constexpr int BK8 = 128;  // E4M3 elements (bytes) per row per stage = one scale block
 
 // BM x BN tile in waves of WM x WN; NST LDS stages in the load ring (loads run
-// NST - 1 k blocks ahead).
-template <int BM_, int BN_, int WM_, int WN_, int NST_ = 3>
+// NST - 1 k blocks ahead). B_NT: weight tiles are loaded with the
+// non-temporal policy (decode, where each weight slab is read by one tile;
+// where several m-tiles of an expert share a slab through L2 it costs 30%).
+template <int BM_, int BN_, int WM_, int WN_, int NST_ = 3, bool B_NT_ = false>
 struct Tile8 {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_;
+  static constexpr bool B_NT = B_NT_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -52,8 +55,8 @@ struct Tile8 {
 
 using T8Gate = Tile8<128, 256, 64, 64>;        // 8 waves, H tile 128 x 128, 144 KB ring
 using T8Down = Tile8<128, 256, 64, 64>;        // 8 waves, 144 KB ring
-using T8GateDec = Tile8<32, 256, 32, 64, 4>;   // 4 waves, 144 KB ring
-using T8DownDec = Tile8<32, 128, 32, 64, 6>;   // 2 waves, 120 KB ring
+using T8GateDec = Tile8<32, 256, 32, 64, 4, true>;   // 4 waves, 144 KB ring
+using T8DownDec = Tile8<32, 128, 32, 64, 6, true>;   // 2 waves, 120 KB ring
 
 // Byte offset of 16-byte chunk `ch` of row `r`, swizzled with (r >> 1) & 7 so
 // that the 32 rows x 2 chunks one 128-bit fragment read serves spread over all
@@ -120,7 +123,12 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
 #pragma unroll
   for (int p = 0; p < C::A_LOADS; ++p) dma16(op.ra, op.ao[p] + off, a_base + p * C::RPP * BK8);
 #pragma unroll
-  for (int p = 0; p < C::B_LOADS; ++p) dma16(op.rb, op.bo[p] + off, b_base + p * C::RPP * BK8);
+  for (int p = 0; p < C::B_LOADS; ++p) {
+    if constexpr (C::B_NT)
+      dma16_nt(op.rb, op.bo[p] + off, b_base + p * C::RPP * BK8);
+    else
+      dma16(op.rb, op.bo[p] + off, b_base + p * C::RPP * BK8);
+  }
   const uint32_t kb4 = static_cast<uint32_t>(kb) * 4u;
   dma4(op.rsa, op.sa_off + kb4, __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
   const uint32_t sb_base =

@@ -12,16 +12,17 @@
 
 namespace {
 
-using dsmoe::dma16;
+using dsmoe::dma16_nt;
 using dsmoe::i32x4_t;
 using dsmoe::lds_addr;
 using dsmoe::rsrc4;
 using dsmoe::vm_wait;
 
 // The layer's load path: 16-byte buffer loads straight into LDS (one 1 KB
-// piece per wave and instruction), each wave cycling over 8 slots of its own
-// 8 KB LDS ring, at most 24 loads in flight; workgroup b reads pieces b,
-// b + nb, ... of the buffer (bytes < 2^31).
+// piece per wave and instruction, non-temporal like the decode GEMMs' weight
+// loads), each wave cycling over 8 slots of its own 8 KB LDS ring, at most 24
+// loads in flight; workgroup b reads pieces b, b + nb, ... of the buffer
+// (bytes < 2^31). Five workgroups per CU fill its LDS and read fastest.
 __global__ __launch_bounds__(256) void hbm_dma_kernel(const void* src, uint32_t bytes) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][8][1024];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void hbm_dma_kernel(const void* src, uint32_t 
   for (; p + 7 * nw < pieces; p += 8 * nw) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      dma16(r, (p + u * nw) * 1024u + lane * 16u,
+      dma16_nt(r, (p + u * nw) * 1024u + lane * 16u,
             __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][slot][0])));
       slot = (slot + 1) & 7;
     }

@@ -110,6 +110,12 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// The same with the non-temporal policy, for data read once (weights
+// streamed past the caches).
+__device__ __forceinline__ void dma16_nt(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
