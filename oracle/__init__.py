@@ -8,3 +8,4 @@ sides see is the seeded input data.
 """
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_backward import *  # noqa: F401,F403
+from .seq_balance import *  # noqa: F401,F403
