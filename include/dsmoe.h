@@ -285,6 +285,43 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
                         const moe_weights* w, const moe_saved* saved, const void* dy, void* dx,
                         const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Sequence-level balance loss of the router
+ *
+ * The training-techniques article (mhpq.cn "DeepSeek-V3 高效训练关键技术全景
+ * 解析" §1.2) adds a per-sequence balance loss so that the tokens of one
+ * sequence do not concentrate on a few experts, and gives no formula. For
+ * each sequence of seq_len = L consecutive tokens (T = n_seq * L), with the
+ * layer's fp32 logits u and its selection topk_idx:
+ *   s = sigmoid(u) over all E experts, s'_ti = s_ti / sum_j s_tj (1/E for a
+ *   token whose fp32 scores are all zero: it then gets no gradient);
+ *   P_i = mean over the sequence of s'_ti;
+ *   f_i = E / (K L) * (routed slots of expert i in the sequence), which is 1
+ *   at perfect balance; loss = alpha * sum_i f_i P_i.
+ * f is piecewise constant, so the gradient flows through P to u, and from
+ * u = x W_r^T to x and W_r. The gradients are those of the sum of the
+ * sequences' losses. bf16 activations only (MOE_ERR_UNSUPPORTED otherwise);
+ * the two products du^T x and du W_r run on bf16 copies of du and W_r with
+ * fp32 accumulation. */
+
+/* Bytes of workspace moe_seq_balance_loss needs for `desc` and seq_len.
+ * Host only. */
+moe_status moe_seq_balance_workspace_size(const moe_layer_desc* desc, int32_t seq_len,
+                                          size_t* bytes);
+
+/* seq_len >= 1 dividing T; alpha finite. In (device pointers):
+ *   x [T, d] bf16, w_router [E, d] fp32, logits [T, E] fp32 and topk_idx
+ *   [T, K] int32 (entries in [0, E)) as the forward wrote them.
+ * Out (fully overwritten):
+ *   loss [T / seq_len] fp32, one value per sequence;
+ *   dlogits [T, E] fp32, dloss/du (optional, NULL to skip);
+ *   dx [T, d] fp32, dloss/dx;  dw_router [E, d] fp32, dloss/dW_r.
+ * T == 0: only dw_router is written (zeros); the T-sized pointers may be
+ * NULL. */
+moe_status moe_seq_balance_loss(const moe_layer_desc* desc, int32_t seq_len, float alpha,
+                                const void* x, const float* w_router, const float* logits,
+                                const int32_t* topk_idx, float* loss, float* dlogits, float* dx,
+                                float* dw_router, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Timing hook for benchmarks (thread-local setting). With n_events >= 6,
  * deepseek_moe_forward records events[0..5] on its stream: before the router,
  * after routing, right before the gate/up GEMM, after it, after the down GEMM

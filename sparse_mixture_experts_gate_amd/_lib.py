@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
             "moe_backward_workspace_size": [D, ctypes.POINTER(ctypes.c_size_t)],
             "moe_backward": [D, P, P, W, ctypes.POINTER(MoeSaved), P, P, ctypes.POINTER(MoeGrads),
                              P, ctypes.c_size_t, P],
+            "moe_seq_balance_workspace_size": [D, I32, ctypes.POINTER(ctypes.c_size_t)],
+            "moe_seq_balance_loss": [D, I32, F, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -247,3 +249,18 @@ def moe_backward(desc, x, w_router, weights: MoeWeights, saved: MoeSaved, dy, dx
     _check(lib().moe_backward(ctypes.byref(desc), _p(x), _p(w_router), ctypes.byref(weights),
                               ctypes.byref(saved), _p(dy), _p(dx), ctypes.byref(grads), _p(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_backward")
+
+
+def moe_seq_balance_workspace_size(desc: MoeLayerDesc, seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_seq_balance_workspace_size(ctypes.byref(desc), seq_len, ctypes.byref(n)),
+           "moe_seq_balance_workspace_size")
+    return n.value
+
+
+def moe_seq_balance_loss(desc, seq_len: int, alpha: float, x, w_router, logits, topk_idx, loss,
+                         dlogits, dx, dw_router, ws, stream=None):
+    _check(lib().moe_seq_balance_loss(ctypes.byref(desc), seq_len, alpha, _p(x), _p(w_router),
+                                      _p(logits), _p(topk_idx), _p(loss), _p(dlogits), _p(dx),
+                                      _p(dw_router), _p(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "moe_seq_balance_loss")

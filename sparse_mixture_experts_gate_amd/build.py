@@ -26,13 +26,13 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 # routing and quantization decide integers from fp32 values: no contraction
-NO_CONTRACT = {"router.hip", "elementwise.hip"}
+NO_CONTRACT = {"router.hip", "elementwise.hip", "balance.hip"}
 # MFMA results in VGPRs: the FP8 kernels scale every product on the VALU, and
 # with the product in AGPRs the compiler reused one AGPR quad per product,
 # which serialized the MFMAs of the decode tiles behind the copies out
 MFMA_VGPR = {"gemm_fp8.hip"}
 SOURCES = ["dsmoe_api.cpp", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "gemm_fp8.hip", "elementwise.hip", "backward.hip"]
+           "gemm_fp8.hip", "elementwise.hip", "backward.hip", "balance.hip"]
 
 
 def _compile(src: str) -> str:

@@ -416,6 +416,51 @@ BwdLayout bwd_layout(const moe_layer_desc* d) {
   return L;
 }
 
+// ---- sequence-level balance loss ---------------------------------------------
+
+int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
+
+moe_status validate_seq_balance(const moe_layer_desc* d, int32_t seq_len) {
+  moe_status st = validate_desc(d);
+  if (st) return st;
+  if (d->act_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the balance loss supports bf16 activations only");
+  if (seq_len < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "seq_len must be >= 1 (got %d)", seq_len);
+  if (d->T % seq_len != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "seq_len %d does not divide T = %lld", seq_len,
+                static_cast<long long>(d->T));
+  // 32-bit byte offsets of the two products' operands and outputs
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  const int64_t T = d->T, E = d->n_experts;
+  if (T * d->d * 4 > lim) return fail(MOE_ERR_UNSUPPORTED, "T*d*4 must be < 2^31 bytes");
+  if (T * round8(E) * 2 > lim || E * round8(T) * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*E*2 must be < 2^31 bytes");
+  return MOE_OK;
+}
+
+struct SeqBalLayout {
+  int64_t n_seq, chunks, ldE, ldT;
+  size_t part_p, part_c, f, du16, duT16, wr16, bytes;
+};
+
+SeqBalLayout seqbal_layout(const moe_layer_desc* d, int32_t seq_len) {
+  SeqBalLayout L{};
+  const int64_t T = d->T, E = d->n_experts;
+  L.n_seq = T / seq_len;
+  L.chunks = L.n_seq * ((seq_len + 63) / 64);
+  L.ldE = round8(E);
+  L.ldT = round8(T);
+  Carver c;
+  L.part_p = c.take(sizeof(float) * size_t(L.chunks * E));
+  L.part_c = c.take(sizeof(int32_t) * size_t(L.chunks * E));
+  L.f = c.take(sizeof(float) * size_t(L.n_seq * E));
+  L.du16 = c.take(size_t(T) * L.ldE * 2);
+  L.duT16 = c.take(size_t(E) * L.ldT * 2);
+  L.wr16 = c.take(size_t(E) * d->d * 2);
+  L.bytes = c.off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -879,6 +924,81 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   w2.out = g->dw2;
   w2.out_s = g->dws2;
   HIP_TRY(launch_wgrad_bf16(w2, stream), "weight gradient of the down projection");
+  return MOE_OK;
+}
+
+moe_status moe_seq_balance_workspace_size(const moe_layer_desc* desc, int32_t seq_len,
+                                          size_t* bytes) {
+  moe_status st = validate_seq_balance(desc, seq_len);
+  if (st) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = seqbal_layout(desc, seq_len).bytes;
+  return MOE_OK;
+}
+
+moe_status moe_seq_balance_loss(const moe_layer_desc* desc, int32_t seq_len, float alpha,
+                                const void* x, const float* w_router, const float* logits,
+                                const int32_t* topk_idx, float* loss, float* dlogits, float* dx,
+                                float* dw_router, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_seq_balance(desc, seq_len);
+  if (st) return st;
+  if (!std::isfinite(alpha)) return fail(MOE_ERR_INVALID_ARGUMENT, "alpha must be finite");
+  st = check_ptrs({{dw_router, "dw_router"}});
+  if (st) return st;
+  const int64_t T = desc->T;
+  const int E = desc->n_experts, d = desc->d;
+  if (T == 0) {
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(dw_router), int64_t(E) * d, 0, stream),
+            "zero dw_router");
+    return MOE_OK;
+  }
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {logits, "logits"}, {topk_idx, "topk_idx"},
+                   {loss, "loss"}, {dx, "dx"}, {ws, "ws"}});
+  if (st) return st;
+  st = check_opt({{dlogits, "dlogits"}});
+  if (st) return st;
+  const SeqBalLayout L = seqbal_layout(desc, seq_len);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "moe_seq_balance_loss needs %zu workspace bytes, got %zu", L.bytes, ws_bytes);
+  uint16_t* du16 = at<uint16_t>(ws, L.du16);
+  uint16_t* duT16 = at<uint16_t>(ws, L.duT16);
+  uint16_t* wr16 = at<uint16_t>(ws, L.wr16);
+  int32_t* part_c = at<int32_t>(ws, L.part_c);
+  HIP_TRY(launch_seq_balance(logits, topk_idx, T, E, desc->top_k, seq_len, alpha,
+                             at<float>(ws, L.part_p), part_c, at<float>(ws, L.f), loss, dlogits,
+                             du16, static_cast<int>(L.ldE), duT16, L.ldT, stream),
+          "balance loss");
+  HIP_TRY(launch_to_bf16(w_router, int64_t(E) * d, wr16, stream), "router weights to bf16");
+  // dW_r = du^T x: contraction over the T tokens (rows of du and x)
+  WgradArgs a{};
+  a.offsets = part_c;  // no routed groups: only its first entry is read
+  a.E = 0;
+  a.T = T;
+  a.shared = true;
+  a.a_s = du16;
+  a.lda_s = L.ldE;
+  a.b_s = x;
+  a.ldb_s = d;
+  a.Ms = E;
+  a.Ns = d;
+  a.out_s = dw_router;
+  HIP_TRY(launch_wgrad_bf16(a, stream), "balance loss: router weight gradient");
+  // dx = du W_r = (du^T)^T W_r: contraction over the E experts (rows of du^T
+  // and W_r)
+  WgradArgs b{};
+  b.offsets = part_c;
+  b.E = 0;
+  b.T = E;
+  b.shared = true;
+  b.a_s = duT16;
+  b.lda_s = L.ldT;
+  b.b_s = wr16;
+  b.ldb_s = d;
+  b.Ms = static_cast<int>(T);
+  b.Ns = d;
+  b.out_s = dx;
+  HIP_TRY(launch_wgrad_bf16(b, stream), "balance loss: input gradient");
   return MOE_OK;
 }
 

@@ -149,6 +149,16 @@ hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
+// balance.hip: the sequence-level balance loss. part_p / part_c hold
+// [n_seq * ceil(L / 64), E] partial sums, f [n_seq, E]; du16 [T, ldE] and
+// duT16 [E, ldT] are bf16 copies of dloss/du (ldE, ldT multiples of 8).
+hipError_t launch_seq_balance(const float* logits, const int32_t* idx, int64_t T, int E, int K,
+                              int L, float alpha, float* part_p, int32_t* part_c, float* f,
+                              float* loss, float* dlogits, uint16_t* du16, int ldE,
+                              uint16_t* duT16, int64_t ldT, hipStream_t s);
+// dst = bf16(src), n a multiple of 8.
+hipError_t launch_to_bf16(const float* src, int64_t n, uint16_t* dst, hipStream_t s);
+
 // ---- elementwise (elementwise.hip) -----------------------------------------
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,
                           const void* yshared, void* y, int64_t T, int K, int d, int io_dtype,

@@ -134,3 +134,23 @@ class MoELayer:
                        L.make_saved(**saved), dy, dx, L.make_grads(**grads),
                        self.backward_workspace(T), stream)
         return dx, grads
+
+    def seq_balance_loss(self, x: torch.Tensor, saved: dict, seq_len: int, alpha: float,
+                         want_dlogits: bool = False, stream=None) -> dict:
+        """The sequence-level balance loss of the forward that wrote ``saved``
+        (its logits and selection) over sequences of ``seq_len`` tokens, and
+        its gradients (moe_seq_balance_loss): loss [T / seq_len], dx [T, d],
+        dw_router [E, d] (fp32), dlogits [T, E] when asked for."""
+        T, dev, f32 = x.shape[0], self.device, torch.float32
+        need = L.moe_seq_balance_workspace_size(self.desc(T), seq_len)
+        if getattr(self, "_sws", None) is None or self._sws.numel() < need:
+            self._sws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        out = {"loss": torch.empty(T // seq_len, dtype=f32, device=dev),
+               "dx": torch.empty(T, self.wl.d, dtype=f32, device=dev),
+               "dw_router": torch.empty(self.wl.E, self.wl.d, dtype=f32, device=dev),
+               "dlogits": (torch.empty(T, self.wl.E, dtype=f32, device=dev)
+                           if want_dlogits else None)}
+        L.moe_seq_balance_loss(self.desc(T), seq_len, alpha, x, self.w_router, saved["logits"],
+                               saved["topk_idx"], out["loss"], out["dlogits"], out["dx"],
+                               out["dw_router"], self._sws, stream)
+        return out

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(L):
         "moe_expert_ffn", "moe_combine", "moe_bias_update", "deepseek_moe_forward",
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
         "moe_last_error", "moe_abi_version", "moe_profile_events", "moe_forward_train",
-        "moe_backward_workspace_size", "moe_backward"}
+        "moe_backward_workspace_size", "moe_backward", "moe_seq_balance_workspace_size",
+        "moe_seq_balance_loss"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
@@ -167,3 +168,27 @@ def test_training_entry_points_validate_before_launch(L):
     st = lib.moe_backward(ctypes.byref(d), good, good, ctypes.byref(w), ctypes.byref(sv), good,
                           good, ctypes.byref(g), good, 16, None)
     assert st == 4 and b"workspace" in lib.moe_last_error()
+
+
+def test_seq_balance_validates_before_launch(L):
+    lib = L.lib()
+    good = ctypes.c_void_p(4096)
+    n = ctypes.c_size_t(0)
+    d = _desc(L)
+    assert lib.moe_seq_balance_workspace_size(ctypes.byref(d), 16, ctypes.byref(n)) == 0
+    # at least the bf16 copies of du (both layouts) and of the router weights
+    assert n.value >= 2 * 64 * 16 * 2 + 16 * 256 * 2
+    # seq_len must divide T and be positive; fp32 activations are unsupported
+    assert lib.moe_seq_balance_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 1
+    assert lib.moe_seq_balance_workspace_size(ctypes.byref(d), 48, ctypes.byref(n)) == 1
+    assert b"does not divide" in lib.moe_last_error()
+    d32 = _desc(L, act_dtype=0, w_dtype=0)
+    assert lib.moe_seq_balance_workspace_size(ctypes.byref(d32), 16, ctypes.byref(n)) == 2
+    args = lambda **kw: [kw.get(k, good) for k in ("x", "wr", "u", "idx", "loss", "dl", "dx", "dwr")]
+    call = lambda a, alpha=0.01, ws=1 << 30: lib.moe_seq_balance_loss(
+        ctypes.byref(d), 16, alpha, *a, good, ws, None)
+    assert call(args(), alpha=float("nan")) == 1 and b"alpha" in lib.moe_last_error()
+    assert call(args(dwr=None)) == 1 and b"dw_router is NULL" in lib.moe_last_error()
+    assert call(args(u=None)) == 1 and b"logits is NULL" in lib.moe_last_error()
+    assert call(args(dl=ctypes.c_void_p(4100))) == 3
+    assert call(args(), ws=16) == 4 and b"workspace" in lib.moe_last_error()
