@@ -244,12 +244,20 @@ def achievable_peaks() -> dict:
     return res
 
 
+# sequences of the balance loss: the pages fix no length; 4096 tokens, two
+# sequences per 8192-token batch
+BALANCE_SEQ_LEN = 4096
+BALANCE_ALPHA = 1e-4
+
+
 def time_train(layer, x, steps: int, warmup: int) -> dict:
-    """Training forward (moe_forward_train) and backward (moe_backward) back to
-    back per step, each bracketed by HIP events on the current stream. dy is
-    a seeded bf16 N(0, 1) tensor."""
+    """One training step of the layer per iteration: the training forward
+    (moe_forward_train), the sequence-level balance loss with its gradients
+    (moe_seq_balance_loss) and the backward (moe_backward), each bracketed by
+    HIP events on the current stream. dy is a seeded bf16 N(0, 1) tensor."""
     import torch
     T, d = x.shape
+    L = BALANCE_SEQ_LEN if T % BALANCE_SEQ_LEN == 0 else T
     g = torch.Generator(device=x.device)
     g.manual_seed(99)
     dy = torch.randn(T, d, generator=g, device=x.device).to(torch.bfloat16)
@@ -257,20 +265,25 @@ def time_train(layer, x, steps: int, warmup: int) -> dict:
     grads = layer.alloc_grads()
     for _ in range(warmup):
         layer.forward_train(x, sv)
+        layer.seq_balance_loss(x, sv, L, BALANCE_ALPHA)
         layer.backward(x, dy, sv, grads)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record()
         layer.forward_train(x, sv)
         ev[i][1].record()
-        layer.backward(x, dy, sv, grads)
+        layer.seq_balance_loss(x, sv, L, BALANCE_ALPHA)
         ev[i][2].record()
+        layer.backward(x, dy, sv, grads)
+        ev[i][3].record()
     torch.cuda.synchronize()
     fwd = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd = [e[1].elapsed_time(e[2]) for e in ev]
+    bal = [e[1].elapsed_time(e[2]) for e in ev]
+    bwd = [e[2].elapsed_time(e[3]) for e in ev]
     return {"fwd_train_ms": percentiles(fwd)["median"], "bwd_ms": percentiles(bwd)["median"],
-            "bwd_ms_pctl": percentiles(bwd)}
+            "bwd_ms_pctl": percentiles(bwd), "balance_ms": percentiles(bal)["median"],
+            "balance_ms_pctl": percentiles(bal), "balance_seq_len": L}
 
 
 def train_record(wl, T: int, r: dict) -> dict:
@@ -279,11 +292,22 @@ def train_record(wl, T: int, r: dict) -> dict:
     fwd_fl = (6.0 * wl.d * wl.I * wl.K + 6.0 * wl.d * wl.Is) * T
     bwd_fl = 2.0 * fwd_fl
     tf = bwd_fl / (r["bwd_ms"] / 1e3)
+    # balance loss: reads the logits, the selection, x and W_r once and writes
+    # dx and dW_r (fp32); its two products take 2 T E d flops each
+    bal_bytes = (T * wl.E * 4 + T * wl.K * 4 + T * wl.d * 2 + wl.E * wl.d * 4 + T * wl.d * 4
+                 + wl.E * wl.d * 4)
+    bal_s = r["balance_ms"] / 1e3
     return {"T": T, "fwd_train_ms": r["fwd_train_ms"], "bwd_ms": r["bwd_ms"],
             "bwd_ms_pctl": r["bwd_ms_pctl"],
             "bwd_gemm_tflop": bwd_fl / 1e12, "bwd_tflops": tf / 1e12,
             "bwd_mfma_frac": tf / MFMA_PEAK["bf16"],
-            "train_step_tokens_per_s": T / ((r["fwd_train_ms"] + r["bwd_ms"]) / 1e3)}
+            "balance_loss": {"ms": r["balance_ms"], "ms_pctl": r["balance_ms_pctl"],
+                             "seq_len": r["balance_seq_len"], "alpha": BALANCE_ALPHA,
+                             "alg_bytes": bal_bytes, "hbm_GBps": bal_bytes / bal_s / 1e9,
+                             "hbm_frac": bal_bytes / bal_s / HBM_PEAK,
+                             "gflop": 4.0 * T * wl.E * wl.d / 1e9},
+            "train_step_tokens_per_s":
+                T / ((r["fwd_train_ms"] + r["balance_ms"] + r["bwd_ms"]) / 1e3)}
 
 
 def main() -> int:
@@ -326,7 +350,8 @@ def main() -> int:
     if args.train_only:
         log(f"timing the training step of {wl.name}: warmup {args.warmup}, steps {args.steps}")
         rec = train_record(wl, wl.T, time_train(layer, P["x"], args.steps, args.warmup))
-        log(f"train: forward {rec['fwd_train_ms']:.3f} ms, backward {rec['bwd_ms']:.3f} ms "
+        log(f"train: forward {rec['fwd_train_ms']:.3f} ms, balance loss "
+            f"{rec['balance_loss']['ms']:.3f} ms, backward {rec['bwd_ms']:.3f} ms "
             f"({rec['bwd_tflops']:.0f} TFLOP/s)")
         print(json.dumps({"train_bf16": rec, "workload": wl.name}), flush=True)
         return 0
@@ -388,9 +413,11 @@ def main() -> int:
         extra["decode_bf16"] = dec
         tr = train_record(wl, wl.T, time_train(layer, P["x"], 5, 2))
         extra["train_bf16"] = tr
-        log(f"train: forward {tr['fwd_train_ms']:.3f} ms, backward {tr['bwd_ms']:.3f} ms "
+        log(f"train: forward {tr['fwd_train_ms']:.3f} ms, balance loss "
+            f"{tr['balance_loss']['ms']:.3f} ms, backward {tr['bwd_ms']:.3f} ms "
             f"({tr['bwd_tflops']:.0f} TFLOP/s)")
         layer._bws = None
+        layer._sws = None
         torch.cuda.empty_cache()
         try:
             wl8 = CONFIGS["v3_fp8"]

@@ -24,7 +24,8 @@
 namespace dsmoe {
 namespace {
 
-constexpr int kChunk = 64;          // tokens per workgroup
+constexpr int kChunk = kBalanceChunk;
+constexpr int kTokU = 4;            // tokens per wave and step, loads issued together
 constexpr int kMaxJ = 8;            // experts per lane: E <= 512
 constexpr int kThreads = 256;       // 4 waves
 
@@ -55,19 +56,30 @@ __global__ __launch_bounds__(kThreads) void seqbal_partial_kernel(
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j) acc[j] = 0.0f;
   const float inv_e = 1.0f / static_cast<float>(E);
-  for (int i = wave; i < ntok; i += 4) {
-    const float* row = logits + (t0 + i) * E;
-    float s[kMaxJ];
-    float part = 0.0f;
+  // wave w takes tokens 4w .. 4w + 3, then 16 + 4w .., in token order; the
+  // logits of its four tokens are loaded before any is used
+  for (int i0 = wave * kTokU; i0 < ntok; i0 += 4 * kTokU) {
+    float uv[kTokU][kMaxJ];
 #pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) {
-      const int e = lane + 64 * j;
-      s[j] = (j < nj && e < E) ? sigmoid_ieee(row[e]) : 0.0f;
-      part += s[j];
+    for (int k = 0; k < kTokU; ++k)
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        const int e = lane + 64 * j;
+        uv[k][j] = (i0 + k < ntok && j < nj && e < E) ? logits[(t0 + i0 + k) * E + e] : 0.0f;
+      }
+#pragma unroll
+    for (int k = 0; k < kTokU; ++k) {
+      if (i0 + k >= ntok) break;
+      float sv[kMaxJ], part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        sv[j] = (j < nj && lane + 64 * j < E) ? sigmoid_ieee(uv[k][j]) : 0.0f;
+        part += sv[j];
+      }
+      const float S = wave_sum(part);
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) acc[j] += S > 0.0f ? sv[j] / S : inv_e;
     }
-    const float S = wave_sum(part);
-#pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) acc[j] += S > 0.0f ? s[j] / S : inv_e;
   }
 #pragma unroll
   for (int j = 0; j < kMaxJ; ++j)
@@ -93,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void seqbal_reduce_kernel(
   for (int e = tid; e < E; e += kThreads) {
     float p = 0.0f;
     int64_t cnt = 0;
+#pragma unroll 8
     for (int c = 0; c < cps; ++c) {
       p += part_p[(q * cps + c) * E + e];
       cnt += part_c[(q * cps + c) * E + e];
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void seqbal_reduce_kernel(
   if (tid == 0) loss[q] = alpha * (((red[0] + red[1]) + red[2]) + red[3]);
 }
 
-// du for kChunk tokens (one wave per token), written as fp32 [T, E]
+// du for kChunk tokens (each wave four at a time), written as fp32 [T, E]
 // (optional), bf16 [T, ldE] (columns E.. ldE - 1 zero) and bf16 transposed
 // [E, ldT] through an LDS tile. Grid ceil(T / kChunk).
 __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
@@ -121,7 +134,19 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
   const int ntok = static_cast<int>(min(static_cast<int64_t>(kChunk), T - t0));
   const int nj = (E + 63) / 64, njw = (ldE + 63) / 64;
   const float a_l = alpha / static_cast<float>(L);
-  for (int i = wave; i < kChunk; i += 4) {
+  for (int i0 = wave * kTokU; i0 < kChunk; i0 += 4 * kTokU) {
+    // the logits of the wave's four tokens are loaded before any is used
+    float uv[kTokU][kMaxJ];
+#pragma unroll
+    for (int k = 0; k < kTokU; ++k)
+#pragma unroll
+      for (int j = 0; j < kMaxJ; ++j) {
+        const int e = lane + 64 * j;
+        uv[k][j] = (i0 + k < ntok && j < nj && e < E) ? logits[(t0 + i0 + k) * E + e] : 0.0f;
+      }
+#pragma unroll
+    for (int k = 0; k < kTokU; ++k) {
+    const int i = i0 + k;
     const int64_t t = t0 + i;
     if (i >= ntok) {
       // columns of tokens past T: zeros in the transposed tile
@@ -130,7 +155,6 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
         if (j < nj && lane + 64 * j < E) tile[lane + 64 * j][i] = 0;
       continue;
     }
-    const float* row = logits + t * E;
     const float* f = f_all + (t / L) * E;
     float s[kMaxJ], fv[kMaxJ];
     float part = 0.0f;
@@ -138,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
     for (int j = 0; j < kMaxJ; ++j) {
       const int e = lane + 64 * j;
       const bool in = j < nj && e < E;
-      s[j] = in ? sigmoid_ieee(row[e]) : 0.0f;
+      s[j] = in ? sigmoid_ieee(uv[k][j]) : 0.0f;
       fv[j] = in ? f[e] : 0.0f;
       part += s[j];
     }
@@ -162,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
       }
       if (j < njw && e < ldE) du16[t * ldE + e] = e < E ? f32_to_bf16(g) : 0;
     }
+    }
   }
   __syncthreads();
   // rows of the transposed tile: 8 tokens (16 bytes) per store, pieces that
@@ -172,6 +197,38 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
     if (col >= ldT) continue;
     *reinterpret_cast<uint4*>(duT16 + e * ldT + col) = *reinterpret_cast<const uint4*>(&tile[e][8 * g]);
   }
+}
+
+// off[g] = min(g * step, T) for g = 0 .. G: the token groups over which the
+// router weight gradient is split.
+__global__ void token_groups_kernel(int32_t* __restrict__ off, int G, int step, int64_t T) {
+  for (int g = threadIdx.x; g <= G; g += blockDim.x)
+    off[g] = static_cast<int32_t>(min(static_cast<int64_t>(g) * step, T));
+}
+
+// out[i] = ((part[i] + part[n + i]) + ...) + part[(G - 1) n + i], four per
+// thread; n a multiple of 4.
+__global__ __launch_bounds__(kThreads) void sum_groups_kernel(const float* __restrict__ part,
+                                                               int G, int64_t n4,
+                                                               float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const float4* p = reinterpret_cast<const float4*>(part);
+  float4 a = p[i];
+  for (int g0 = 1; g0 < G; g0 += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = g0 + j < G ? p[static_cast<int64_t>(g0 + j) * n4 + i] : a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (g0 + j < G) {
+        a.x = a.x + v[j].x;
+        a.y = a.y + v[j].y;
+        a.z = a.z + v[j].z;
+        a.w = a.w + v[j].w;
+      }
+  }
+  reinterpret_cast<float4*>(out)[i] = a;
 }
 
 // dst[i] = bf16(src[i]), 8 per thread; n a multiple of 8.
@@ -205,6 +262,19 @@ hipError_t launch_seq_balance(const float* logits, const int32_t* idx, int64_t T
   const unsigned nchunks = static_cast<unsigned>((T + kChunk - 1) / kChunk);
   hipLaunchKernelGGL(seqbal_grad_kernel, dim3(nchunks), dim3(kThreads), 0, s, logits, f, T, E, L,
                      alpha, dlogits, du16, ldE, duT16, ldT);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_groups(int32_t* off, int G, int step, int64_t T, hipStream_t s) {
+  hipLaunchKernelGGL(token_groups_kernel, dim3(1), dim3(64), 0, s, off, G, step, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_groups(const float* part, int G, int64_t n, float* out, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_groups_kernel, dim3(static_cast<unsigned>((n4 + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, part, G, n4, out);
   return hipGetLastError();
 }
 

@@ -440,16 +440,26 @@ moe_status validate_seq_balance(const moe_layer_desc* d, int32_t seq_len) {
 
 struct SeqBalLayout {
   int64_t n_seq, chunks, ldE, ldT;
-  size_t part_p, part_c, f, du16, duT16, wr16, bytes;
+  int groups, group_step;  // token groups of the split router weight gradient
+  size_t part_p, part_c, f, du16, duT16, wr16, goff, gpart, bytes;
 };
 
 SeqBalLayout seqbal_layout(const moe_layer_desc* d, int32_t seq_len) {
   SeqBalLayout L{};
   const int64_t T = d->T, E = d->n_experts;
   L.n_seq = T / seq_len;
-  L.chunks = L.n_seq * ((seq_len + 63) / 64);
+  L.chunks = L.n_seq * ((seq_len + kBalanceChunk - 1) / kBalanceChunk);
   L.ldE = round8(E);
   L.ldT = round8(T);
+  // dW_r = du^T x has few output tiles (E x d over 128 x 256): its
+  // contraction over the tokens is split into up to 16 groups of at least 64
+  // tokens, so that about 512 tiles run, and the partial products are added
+  // in group order. A function of the descriptor only.
+  const int64_t tiles = ((E + 127) / 128) * ((d->d + 255) / 256);
+  int64_t g = std::min<int64_t>({16, (512 + tiles - 1) / tiles, (T + 63) / 64});
+  g = std::max<int64_t>(g, 1);
+  L.group_step = static_cast<int>(((T + g - 1) / g + 63) / 64 * 64);
+  L.groups = T > 0 ? static_cast<int>((T + L.group_step - 1) / L.group_step) : 1;
   Carver c;
   L.part_p = c.take(sizeof(float) * size_t(L.chunks * E));
   L.part_c = c.take(sizeof(int32_t) * size_t(L.chunks * E));
@@ -457,6 +467,8 @@ SeqBalLayout seqbal_layout(const moe_layer_desc* d, int32_t seq_len) {
   L.du16 = c.take(size_t(T) * L.ldE * 2);
   L.duT16 = c.take(size_t(E) * L.ldT * 2);
   L.wr16 = c.take(size_t(E) * d->d * 2);
+  L.goff = c.take(sizeof(int32_t) * size_t(L.groups + 1));
+  L.gpart = c.take(L.groups > 1 ? sizeof(float) * size_t(L.groups) * E * d->d : 0);
   L.bytes = c.off;
   return L;
 }
@@ -970,24 +982,30 @@ moe_status moe_seq_balance_loss(const moe_layer_desc* desc, int32_t seq_len, flo
                              du16, static_cast<int>(L.ldE), duT16, L.ldT, stream),
           "balance loss");
   HIP_TRY(launch_to_bf16(w_router, int64_t(E) * d, wr16, stream), "router weights to bf16");
-  // dW_r = du^T x: contraction over the T tokens (rows of du and x)
+  // dW_r = du^T x: contraction over the T tokens (rows of du and x), split
+  // into token groups whose partial products are then added in group order
+  int32_t* goff = at<int32_t>(ws, L.goff);
+  HIP_TRY(launch_token_groups(goff, L.groups, L.group_step, T, stream), "token groups");
   WgradArgs a{};
-  a.offsets = part_c;  // no routed groups: only its first entry is read
-  a.E = 0;
+  a.offsets = goff;
+  a.E = L.groups;
   a.T = T;
-  a.shared = true;
-  a.a_s = du16;
-  a.lda_s = L.ldE;
-  a.b_s = x;
-  a.ldb_s = d;
-  a.Ms = E;
-  a.Ns = d;
-  a.out_s = dw_router;
+  a.shared = false;
+  a.a = du16;
+  a.lda = L.ldE;
+  a.b = x;
+  a.ldb = d;
+  a.M = E;
+  a.N = d;
+  a.out = L.groups > 1 ? at<float>(ws, L.gpart) : dw_router;
   HIP_TRY(launch_wgrad_bf16(a, stream), "balance loss: router weight gradient");
+  if (L.groups > 1)
+    HIP_TRY(launch_sum_groups(at<float>(ws, L.gpart), L.groups, int64_t(E) * d, dw_router, stream),
+            "balance loss: router weight gradient groups");
   // dx = du W_r = (du^T)^T W_r: contraction over the E experts (rows of du^T
   // and W_r)
   WgradArgs b{};
-  b.offsets = part_c;
+  b.offsets = goff;  // no routed groups: only its first entry is read
   b.E = 0;
   b.T = E;
   b.shared = true;

@@ -150,14 +150,19 @@ hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
 // balance.hip: the sequence-level balance loss. part_p / part_c hold
-// [n_seq * ceil(L / 64), E] partial sums, f [n_seq, E]; du16 [T, ldE] and
+// [n_seq * ceil(L / kBalanceChunk), E] partial sums, f [n_seq, E]; du16 [T, ldE] and
 // duT16 [E, ldT] are bf16 copies of dloss/du (ldE, ldT multiples of 8).
+constexpr int kBalanceChunk = 32;  // tokens per workgroup of the balance-loss kernels
 hipError_t launch_seq_balance(const float* logits, const int32_t* idx, int64_t T, int E, int K,
                               int L, float alpha, float* part_p, int32_t* part_c, float* f,
                               float* loss, float* dlogits, uint16_t* du16, int ldE,
                               uint16_t* duT16, int64_t ldT, hipStream_t s);
 // dst = bf16(src), n a multiple of 8.
 hipError_t launch_to_bf16(const float* src, int64_t n, uint16_t* dst, hipStream_t s);
+// off[g] = min(g * step, T), g = 0 .. G.
+hipError_t launch_token_groups(int32_t* off, int G, int step, int64_t T, hipStream_t s);
+// out = sum over g of part[g * n .. (g + 1) n), in g order; n a multiple of 4.
+hipError_t launch_sum_groups(const float* part, int G, int64_t n, float* out, hipStream_t s);
 
 // ---- elementwise (elementwise.hip) -----------------------------------------
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,
