@@ -323,12 +323,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--train-only", action="store_true",
-                    help="only time the training forward + backward of the workload and print "
-                         "that record (for profiling runs)")
+                    help="only time the training step (forward, balance loss, backward) of the "
+                         "workload and print that record (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU are "
-              "not part of this build (see DESIGN.md on sharding).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer and runs on one GPU only; "
+              "--gpus must be 1.", file=sys.stderr)
         return 2
 
     import torch

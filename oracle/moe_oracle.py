@@ -25,7 +25,7 @@ Sources, cited below by tag:
 [WX] "DeepSeek-V3核心技术解析：MoE、MLA、MTP与FP8训练详解" (wenxiaobai), §二(一):
      top-K selection by affinity score; the shared expert takes part globally.
 
-Readings where the pages are silent (each listed with its reason in the design doc):
+Readings where the pages are silent (each taken as the plainest one the rest supports):
 SwiGLU experts without biases; group score = fp32 sum of the top-``topn``
 biased scores of the group; ties go to the lower index; gates divide by the
 plain fp32 sum of the selected unbiased scores (no extra scale); "overloaded"

@@ -7,8 +7,7 @@ with the HIP library.
 What the pages fix: besides the bias-based balancing, DeepSeek-V3 adds a
 sequence-level balance loss so that the tokens of one sequence do not
 concentrate on a few experts [MH §1.2, "序列级负载均衡"]. The pages give it
-in words only; the form below is the plainest one those words support (each
-reading is listed with its reason in the design notes):
+in words only; the form below is the plainest one those words support:
 
 For one sequence of L consecutive tokens, with the layer's own selection
 e_tk (K routed experts per token) and the fp32 router logits u:
