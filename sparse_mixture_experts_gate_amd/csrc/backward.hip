@@ -205,9 +205,10 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
   const int r0 = tid >> 3;
   load_group_tables(gt, a.tiles, a.offsets, a.E);
   const int total = gt.total;
-  const int nb = gridDim.x;
-  const int first = xcd_logical_block(blockIdx.x, nb);
-  if (first >= total) return;
+  // one tile per workgroup (long k loops: d / 64 steps), XCD-contiguous
+  const int first = xcd_single_tile(blockIdx.x, total);
+  if (first < 0) return;
+  const int nb = total;
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
   const i32x4_t rdyp = rsrc4(a.dyp, static_cast<uint32_t>(a.TK) * row_bytes);
   const i32x4_t rdy = rsrc4(a.dy, static_cast<uint32_t>(a.T) * row_bytes);
@@ -505,11 +506,18 @@ hipError_t launch_router_wgrad(const void* x, const int32_t* perm, const int32_t
   return hipGetLastError();
 }
 
+// more than the tiles of the plan: routed rows in 128-row tiles (at most
+// ceil(TK / 128) + E m-tiles over all groups) and the shared rows
+int64_t dgrad_tile_bound(const BwdArgs& a, int n_routed, int n_shared) {
+  const int64_t m = (a.TK + 127) / 128 + a.E;
+  const int64_t b = m * n_routed + (a.Is > 0 ? (a.T + 127) / 128 * n_shared : 0);
+  return (b + 7) / 8 * 8;
+}
+
 hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s) {
   using C = TilePrefill;
-  static int occ = 0;
-  if (!occ) occ = occupancy_of(dgrad2_bf16_kernel<C>, C::NT);
-  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
+  const int g = static_cast<int>(dgrad_tile_bound(a, (a.I + C::BN - 1) / C::BN,
+                                                  (a.Is + C::BN - 1) / C::BN));
   hipLaunchKernelGGL(dgrad2_bf16_kernel<C>, dim3(g), dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }

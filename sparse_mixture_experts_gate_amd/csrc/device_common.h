@@ -51,6 +51,16 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
+// One tile per workgroup: the blocks of XCD x (x, x + 8, x + 16, ...) take
+// tiles [x per, (x + 1) per), per = ceil(total / 8), in order, so the tiles an
+// XCD runs at a time are a contiguous window of the tile order (tiles that
+// share an operand slab stay together however long each takes). -1: no tile.
+__device__ __forceinline__ int xcd_single_tile(int b, int total) {
+  const int per = (total + 7) / 8, slot = b >> 3;
+  const int t = (b & 7) * per + slot;
+  return (slot < per && t < total) ? t : -1;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
