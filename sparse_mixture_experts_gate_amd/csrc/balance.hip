@@ -10,8 +10,10 @@
 //   P_i = (1/L) sum_t s'_ti,  f_i = E / (K L) * (routed slots of expert i);
 //   loss = alpha * sum_i f_i P_i;
 //   du_tj = alpha / (L S_t) * (f_j - F_t) * s_tj (1 - s_tj)
-//         = (alpha / L) * (f_j - F_t) * s'_tj * (1 - s_tj),
-//       F_t = sum_i f_i s'_ti (f is piecewise constant: no gradient);
+//         = (alpha / L) * (g_j - G_t) * s'_tj * (1 - s_tj),
+//       F_t = sum_i f_i s'_ti, g = f - 1, G_t = sum_i g_i s'_ti (the same
+//       difference, since sum_i s'_ti = 1, without the cancellation of two
+//       numbers near 1 at balance; f is piecewise constant: no gradient);
 // then dWr = du^T x and dx = du Wr as two k-major weight-gradient GEMMs
 // (backward.hip), one contracting over the tokens, one over the experts.
 //
@@ -93,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void seqbal_partial_kernel(
   }
 }
 
-// One workgroup per sequence: P_i, f_i and the loss.
+// One workgroup per sequence: P_i, f_i, the loss, and g_i = f_i - 1 for the
+// gradient.
 __global__ __launch_bounds__(kThreads) void seqbal_reduce_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_c, int E, int K, int L,
     int cps, float alpha, float* __restrict__ f_out, float* __restrict__ loss) {
@@ -110,9 +113,11 @@ __global__ __launch_bounds__(kThreads) void seqbal_reduce_kernel(
       p += part_p[(q * cps + c) * E + e];
       cnt += part_c[(q * cps + c) * E + e];
     }
-    const float f = static_cast<float>(static_cast<double>(cnt) * E /
-                                       (static_cast<double>(K) * L));
-    f_out[q * E + e] = f;
+    const double kl = static_cast<double>(K) * L;
+    const float f = static_cast<float>(static_cast<double>(cnt) * E / kl);
+    // the gradient uses g = f - 1, formed from the integer counts: near
+    // balance f_j - F_t cancels, g_j - G_t does not
+    f_out[q * E + e] = static_cast<float>((static_cast<double>(cnt) * E - kl) / kl);
     term += f * (p * inv_l);
   }
   term = wave_sum(term);
@@ -168,7 +173,9 @@ __global__ __launch_bounds__(kThreads) void seqbal_grad_kernel(
     }
     const float S = wave_sum(part);
     // s'_j = s_j / S (zero where S is zero: no gradient); the factor
-    // alpha / (L S) is applied through s', which stays finite for tiny S
+    // alpha / (L S) is applied through s', which stays finite for tiny S.
+    // fv holds g = f - 1: since sum_i s'_i = 1, f_j - F_t = g_j - G_t with
+    // G_t = sum_i g_i s'_i, which keeps its precision near balance
     float sn[kMaxJ], fpart = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxJ; ++j) {

@@ -150,7 +150,7 @@ hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
 // balance.hip: the sequence-level balance loss. part_p / part_c hold
-// [n_seq * ceil(L / kBalanceChunk), E] partial sums, f [n_seq, E]; du16 [T, ldE] and
+// [n_seq * ceil(L / kBalanceChunk), E] partial sums, f - 1 [n_seq, E]; du16 [T, ldE] and
 // duT16 [E, ldT] are bf16 copies of dloss/du (ldE, ldT multiples of 8).
 constexpr int kBalanceChunk = 32;  // tokens per workgroup of the balance-loss kernels
 hipError_t launch_seq_balance(const float* logits, const int32_t* idx, int64_t T, int E, int K,

@@ -6,12 +6,15 @@ logits: 1e-5 (relative for the loss, row metric for dloss/du). dx and dW_r
 come from products of bf16 copies of dloss/du and W_r with fp32
 accumulation: the bf16 bound, 2e-2 (row metric for dx, whose rows are
 tokens; per-matrix metric for dW_r, a sum over tokens)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import sparse_mixture_experts_gate_amd as M
+from sparse_mixture_experts_gate_amd import _lib as L
 from sparse_mixture_experts_gate_amd.workloads import CONFIGS, Workload, make_inputs
 from parity_util import TOL, host, mat_rel_err, row_rel_err
 
@@ -122,3 +125,60 @@ def test_seq_balance_v3_shape():
     torch.cuda.synchronize()
     loss, _ = _check(wl, P, out, 4096, 1e-4, res)
     _log(f"  losses {loss.tolist()}")
+
+
+def _synthetic(T, E, K, d, seed):
+    """Logits N(0, 4), the top-K of each row as the selection, x and W_r as
+    the layer draws them (the entry point takes any logits and selection)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    logits = (2.0 * torch.randn(T, E, generator=g, device=DEV)).contiguous()
+    idx = torch.topk(logits, K, dim=1).indices.to(torch.int32).contiguous()
+    return logits, idx
+
+
+def test_seq_balance_max_experts():
+    # E = 512: eight experts per lane and the largest transposed tile
+    wl = SMALL.with_(name="seqbal_e512", T=256, E=512, K=8, G=1, M=1, topn=1)
+    _log("balance loss parity: E=512 K=8 T=256 seq_len=64")
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    logits, idx = _synthetic(wl.T, wl.E, wl.K, wl.d, 5)
+    out = {"logits": logits, "topk_idx": idx}
+    res = layer.seq_balance_loss(P["x"], out, 64, 0.02, want_dlogits=True)
+    torch.cuda.synchronize()
+    _check(wl, P, out, 64, 0.02, res)
+
+
+def test_seq_balance_at_size_limit():
+    # the largest T the library accepts for d = 1024: dx [T, d] fp32 just
+    # below 2^31 bytes. 2^19 - 1 is prime, so it runs as one sequence (16384
+    # chunk sums per expert in the reduction). Loss and dloss/du are checked
+    # on every token, dW_r in full, dx on the last rows.
+    wl = SMALL.with_(name="seqbal_limit", d=1024, E=16, K=2, G=1, M=1, topn=1,
+                     x_kind="normal")
+    n = ctypes.c_size_t(0)
+    ok = lambda T: L.lib().moe_seq_balance_workspace_size(
+        ctypes.byref(M.make_desc(wl, T)), 1, ctypes.byref(n)) == 0
+    T = (1 << 19) - 1
+    assert ok(T) and not ok(T + 1)
+    _log(f"balance loss at the size limit: T={T} d={wl.d} one sequence")
+    wl = wl.with_(T=T)
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    logits, idx = _synthetic(T, wl.E, wl.K, wl.d, 6)
+    out = {"logits": logits, "topk_idx": idx}
+    res = layer.seq_balance_loss(P["x"], out, T, 0.05, want_dlogits=True)
+    torch.cuda.synchronize()
+    loss, du = O.seq_balance_loss(host(logits), host(idx), wl.E, T, 0.05)
+    el = float(abs(host(res["loss"])[0] - loss[0]) / abs(loss[0]))
+    eu = row_rel_err(host(res["dlogits"]), du)
+    x = host(P["x"])
+    dwr = du.T @ x.astype(np.float64)
+    ew = mat_rel_err(host(res["dw_router"]), dwr)
+    rows = np.arange(T - 64, T)
+    dx = du[rows] @ host(P["w_router"]).astype(np.float64)
+    ex = row_rel_err(host(res["dx"][torch.as_tensor(rows, device=DEV)]), dx)
+    _log(f"  loss {el:.2e} dlogits {eu:.2e} dw_router {ew:.2e} dx(last rows) {ex:.2e}")
+    assert el <= TOL["f32"] and eu <= TOL["f32"]
+    assert ew <= TOL["bf16"] and ex <= TOL["bf16"]
