@@ -170,17 +170,18 @@ __global__ __launch_bounds__(kRowT) void router_wgrad_kernel(
   const uint16_t* xc = x + ch * 8;
   const int r1 = offsets[e + 1];
   int r = offsets[e];
-  // four rows in flight per iteration; they are added in row order
-  for (; r + 4 <= r1; r += 4) {
-    uint4 v[4];
-    float u[4];
+  // sixteen rows in flight per iteration (the hottest expert's segment bounds
+  // the kernel); they are added in row order
+  for (; r + 16 <= r1; r += 16) {
+    uint4 v[16];
+    float u[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
       v[i] = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(perm[r + i]) * d);
       u[i] = du_perm[r + i];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) add_row(u[i], v[i]);
+    for (int i = 0; i < 16; ++i) add_row(u[i], v[i]);
   }
   for (; r < r1; ++r)
     add_row(du_perm[r], *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(perm[r]) * d));
