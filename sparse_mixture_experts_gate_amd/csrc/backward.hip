@@ -103,6 +103,8 @@ __global__ __launch_bounds__(kRowT) void bwd_gate_kernel(
 
 // dx_t = dA_s[t] + sum_k dA[inv[t,k]] + sum_k du_tk Wr[idx[t,k]], fp32 in that
 // order, bf16 out. One workgroup per token.
+constexpr int kRowsInFlight = 8;
+
 __global__ __launch_bounds__(kRowT) void bwd_combine_kernel(
     const uint16_t* __restrict__ dap, const uint16_t* __restrict__ das,
     const int32_t* __restrict__ inv, const int32_t* __restrict__ idx,
@@ -124,14 +126,23 @@ __global__ __launch_bounds__(kRowT) void bwd_combine_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     }
-    for (int k = 0; k < K; ++k) {
-      const int64_t r = inv[t * K + k];
-      const uint4 v = *reinterpret_cast<const uint4*>(dap + r * d + ch * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // the rows' loads go out eight at a time, then add in k order
+    for (int k0 = 0; k0 < K; k0 += kRowsInFlight) {
+      uint4 rv[kRowsInFlight];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += __uint_as_float(w[j] << 16);
-        acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+      for (int k = 0; k < kRowsInFlight; ++k)
+        if (k0 + k < K)
+          rv[k] = *reinterpret_cast<const uint4*>(
+              dap + static_cast<int64_t>(inv[t * K + k0 + k]) * d + ch * 8);
+#pragma unroll
+      for (int k = 0; k < kRowsInFlight; ++k) {
+        if (k0 + k >= K) break;
+        const uint32_t w[4] = {rv[k].x, rv[k].y, rv[k].z, rv[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += __uint_as_float(w[j] << 16);
+          acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+        }
       }
     }
     for (int k = 0; k < K; ++k) {

@@ -250,3 +250,12 @@ def test_backward_zero_score_sum():
     assert not ref.dw_router.any()
     assert not host(gr["dw_router"]).any()
     _check_grads(wl, sv, dx, gr, ref)
+
+
+def test_backward_more_than_eight_experts_per_token():
+    # K = 10: the input-gradient combine takes its rows eight at a time
+    wl = TRAIN_SMALL.with_(name="train_k10", E=16, K=10, G=1, M=1, topn=1, T=130)
+    _log("backward parity: K = 10")
+    P, layer, y, sv, dy, dx, gr = _run(wl)
+    ref = _oracle(wl, P, sv, dy)
+    _check_grads(wl, sv, dx, gr, ref)
