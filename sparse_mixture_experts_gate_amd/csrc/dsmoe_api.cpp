@@ -379,6 +379,11 @@ moe_status validate_train(const moe_layer_desc* d) {
     return fail(MOE_ERR_UNSUPPORTED, "T*K*d*2 must be < 2^31 bytes for training");
   if ((TK + d->T) * 2 * ldh * 2 > lim)
     return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*2*max(I,Is)*2 must be < 2^31 bytes for training");
+  // one expert's fp32 weight gradient (the largest, [2 max(I,Is), d]) is
+  // written through a buffer resource whose byte size must stay below 2^31,
+  // so that the out-of-range offset of masked epilogue entries lies past it
+  if (2 * ldh * d->d * 4 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "2*max(I,Is)*d*4 must be < 2^31 bytes for training");
   return MOE_OK;
 }
 

@@ -137,6 +137,14 @@ def test_training_entry_points_validate_before_launch(L):
     assert lib.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
     # holds at least the gated output gradients [T*K, d] and [da | db] [T*(K+1), 2 max(I, Is)]
     assert n.value >= 64 * 2 * 256 * 2 + 64 * 3 * 256 * 2
+    # one expert's fp32 weight gradient must stay below 2^31 bytes: this
+    # layer is a valid forward but too large for the backward's epilogue
+    big = _desc(L, inter=1 << 20, shared_inter=128)
+    assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 2
+    assert b"2*max(I,Is)*d*4" in lib.moe_last_error()
+    big = _desc(L, inter=128, shared_inter=(1 << 20) - 128)
+    assert lib.moe_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
     # fp32 and fp8 layers have no training path
     for kw in (dict(act_dtype=0, w_dtype=0), dict(w_dtype=2)):
         assert lib.moe_backward_workspace_size(ctypes.byref(_desc(L, **kw)), ctypes.byref(n)) == 2

@@ -423,3 +423,108 @@ def test_e4m3_arithmetic_encoder_equals_table_search():
     mids = ((vals[:-1] + vals[1:]) / 2).astype(F32)
     v = np.concatenate([v, mids, -mids, np.float32([0.0, -0.0, 448.0, 464.0, 1e9, -1e9, 2.0 ** -10])])
     assert np.array_equal(O.e4m3_encode(v), O.e4m3_encode_table(v))
+
+
+def test_block_dequant_round_trip_with_non_unit_scales():
+    """128x128 weight blocks of very different magnitudes [GK Q8; MH §4.1]:
+    every block gets its own scale (none of them 1), and dequantizing the
+    codes multiplies each decoded code by its block's scale, so every value
+    comes back within half an e4m3 step of the original (relative 2^-4 for
+    normal codes, 2^-10 of the scale for subnormal ones). Dividing by the
+    scale instead, or taking another block's scale, fails this."""
+    rng = np.random.default_rng(18)
+    W = rng.normal(0, 1.0, (384, 256)).astype(F32)
+    mags = np.array([[3e-3, 0.7], [41.0, 5e-5], [2.0, 900.0]])
+    W = (W.reshape(3, 128, 2, 128) * mags[:, None, :, None]).reshape(384, 256).astype(F32)
+    q, s = O.quantize_blocks_128(W)
+    assert s.shape == (3, 2) and np.all(s != 1.0)
+    dq = O.dequant_blocks_128(q, s)
+    sc = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)
+    bound = sc * (np.abs(O.e4m3_decode(q)).astype(np.float64) * 2.0 ** -4 + 2.0 ** -10)
+    err = np.abs(dq - W.astype(np.float64))
+    assert np.all(err <= bound * (1 + 1e-6))
+    # the per-block error is a small fraction of that block's magnitude
+    rel = (err.reshape(3, 128, 2, 128).max((1, 3)) /
+           np.abs(W).reshape(3, 128, 2, 128).max((1, 3)))
+    assert np.all(rel <= 2.0 ** -4)
+
+
+def _pow2_grid_matrix(rng, rows, cols, exps, grid):
+    """Values on the e4m3 grid times 2^k, with k fixed per 128x128 block
+    (exps [ceil(rows/128), cols/128]; one row gives 1x128 activation tiles)
+    and a 448 * 2^k in every block, so the block's max-abs scale is exactly
+    2^k and quantization is lossless."""
+    a = rng.choice(grid, size=(rows, cols)) * rng.choice([-1.0, 1.0], size=(rows, cols))
+    a[::128, ::128] = 448.0
+    k = np.repeat(np.repeat(np.asarray(exps, np.float64), 128, 0), 128, 1)[:rows]
+    return (a * np.exp2(k)).astype(F32)
+
+
+def test_fp8_layer_with_power_of_two_scales_and_shared_expert():
+    """FP8 layer on values that sit on the e4m3 grid times per-block powers
+    of two (every activation tile and weight block has a scale 2^k != 1), so
+    quantizing x and the weights is exact and the dequantized values equal
+    the originals. The reference is a dense fp64 SwiGLU of those exact values
+    (torch), shared expert included with weight 1 [MH §1.1], routed experts
+    weighted by their gates. The down projections are selectors (output j
+    reads one H column, times 448 * 2^k), so each output is one value of H,
+    and H's own 1x128 re-quantization is the only lossy step: the error is
+    within half an e4m3 step of the H values it reads. A dequantization that
+    divides by the scale, a dropped shared expert or a transposed down
+    projection fails this."""
+    rng = np.random.default_rng(19)
+    grid = O.e4m3_decode(np.arange(40, 100, dtype=np.uint8)).astype(np.float64)
+    T, d, I, E = 6, 256, 128, 3
+    xk = rng.integers(-7, -3, size=(T, d // 128))
+    x = np.concatenate([_pow2_grid_matrix(rng, 1, d, xk[t:t + 1], grid) for t in range(T)])
+    xq, xs = O.quantize_rows_1x128(x)
+    assert np.all(xs != 1.0) and np.array_equal(O.dequant_rows_1x128(xq, xs), x.astype(np.float64))
+
+    def expert(seed_shift):
+        w13 = _pow2_grid_matrix(rng, 2 * I, d, rng.integers(-9, -5, size=(2, 2)), grid)
+        cols = rng.permutation(I)
+        sel = np.zeros((d, I), np.float64)
+        sel[np.arange(d), np.concatenate([cols, cols[::-1]])] = 1.0
+        kk = rng.integers(-8, -4, size=(2, 1))
+        w2 = (sel * 448.0 * np.exp2(np.repeat(kk, 128, 0))).astype(F32)
+        return w13, w2
+
+    ws = [expert(e) for e in range(E + 1)]
+    q13, s13, q2, s2 = [], [], [], []
+    for w13, w2 in ws:
+        a, b = O.quantize_blocks_128(w13)
+        c, e = O.quantize_blocks_128(w2)
+        assert np.all(b != 1.0) and np.all(e != 1.0)
+        assert np.array_equal(O.dequant_blocks_128(a, b), w13.astype(np.float64))
+        assert np.array_equal(O.dequant_blocks_128(c, e), w2.astype(np.float64))
+        q13.append(a); s13.append(b); q2.append(c); s2.append(e)
+    idx = np.array([[0, 1], [1, 2], [2, 0], [0, 2], [1, 0], [2, 1]], np.int32)
+    g = rng.uniform(0.1, 0.9, size=(T, 2)).astype(F32)
+    g = (g / g.sum(1, keepdims=True)).astype(F32)
+    y8 = O.layer_output_fp8(x, idx, g, q13[:E], s13[:E], q2[:E], s2[:E],
+                            q13[E], s13[E], q2[E], s2[E])
+
+    xt = torch.from_numpy(x.astype(np.float64))
+
+    def dense(e):
+        w13 = torch.from_numpy(ws[e][0].astype(np.float64))
+        w2 = torch.from_numpy(ws[e][1].astype(np.float64))
+        h = torch.nn.functional.silu(xt @ w13[:I].T) * (xt @ w13[I:].T)
+        return (h @ w2.T).numpy(), h.numpy(), w2.numpy()
+
+    ref = np.zeros((T, d))
+    bound = np.zeros((T, d))
+    for e in range(E + 1):
+        ye, h, w2 = dense(e)
+        # half an e4m3 step of each H value, plus the subnormal step of its tile
+        amax = np.abs(h).reshape(T, I // 128, 128).max(2)
+        hb = np.abs(h) * 2.0 ** -4 + np.repeat(amax / 448.0, 128, 1) * 2.0 ** -10
+        wgt = np.ones(T) if e == E else np.where(idx == e, g, 0.0).sum(1)
+        ref += wgt[:, None] * ye
+        bound += wgt[:, None] * (hb @ np.abs(w2).T)
+    err = np.abs(y8 - ref)
+    assert np.all(err <= bound * (1 + 1e-5) + 1e-12 * np.abs(ref).max())
+    # the shared expert's share is well above the bound: without it most
+    # outputs would fail
+    ys = dense(E)[0]
+    assert np.mean(np.abs(y8 - (ref - ys)) > bound) > 0.5
