@@ -87,7 +87,7 @@ class LayerGrads:
 
 
 def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
-                   experts=None) -> LayerGrads:
+                   experts=None, workers=1) -> LayerGrads:
     """Gradients of L = sum <dy, y> for the layer with the selection fixed to
     ``topk_idx`` [T, K]; the gates are recomputed in fp64 from the fp32
     ``logits`` [T, E] (g = s / S over the selected s), except for tokens whose
@@ -96,7 +96,8 @@ def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
     may be lazy containers. ``experts`` (optional) restricts the routed weight
     gradients to those expert ids (the others stay zero); dx, dg and du need
     every routed expert of every token, so it is only for weight-gradient
-    spot checks."""
+    spot checks. With workers > 1 the experts' backward passes run on that
+    many threads; their results are added in the same order either way."""
     x = np.asarray(x, F64)
     wr = np.asarray(w_router, F64)
     u = np.asarray(logits, F64)
@@ -122,14 +123,26 @@ def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
     dw13 = np.zeros((E, 2 * inter, d), F64)
     dw2 = np.zeros((E, d, inter), F64)
     wanted = None if experts is None else set(int(e) for e in experts)
-    for e in np.unique(idx):
-        e = int(e)
+
+    def one(e):
         rows, slots = np.nonzero(idx == e)
         dYe = g[rows, slots][:, None] * dy[rows]
         dXe, dW13e, dW2e, Ye = swiglu_expert_backward(x[rows], w13[e], w2[e], dYe)
+        if wanted is not None and e not in wanted:
+            dW13e = dW2e = None
+        return e, rows, slots, dXe, dW13e, dW2e, Ye
+
+    ids = [int(e) for e in np.unique(idx)]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            outs = list(ex.map(one, ids))
+    else:
+        outs = map(one, ids)
+    for e, rows, slots, dXe, dW13e, dW2e, Ye in outs:
         dg[rows, slots] = np.sum(dy[rows] * Ye, axis=1)
         np.add.at(dx, rows, dXe)
-        if wanted is None or e in wanted:
+        if dW13e is not None:
             dw13[e] = dW13e
             dw2[e] = dW2e
     dws13 = dws2 = None

@@ -304,10 +304,10 @@ def round_bf16(v) -> np.ndarray:
     return np.ldexp(q, e).astype(F32)
 
 
-def e4m3_decode(code) -> np.ndarray:
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
     """OCP E4M3FN (the forward-pass FP8 format): 1 sign, 4 exponent (bias 7),
     3 mantissa bits; no infinities; S.1111.111 is NaN; max 448."""
-    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    c = np.asarray(c, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     ex = (c >> 3) & 0xF
     mant = c & 0x7
@@ -315,6 +315,16 @@ def e4m3_decode(code) -> np.ndarray:
                    (1.0 + mant / 8.0) * np.exp2(ex - 7.0))
     val = np.where((ex == 15) & (mant == 7), np.nan, val)
     return (sign * val).astype(F32)
+
+
+# the value of every one of the 256 codes, from the format definition above
+_E4M3_VALUES = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """E4M3FN code -> fp32 value (a look-up of the 256 values the format
+    defines)."""
+    return _E4M3_VALUES[np.asarray(code, dtype=np.uint8)]
 
 
 _E4M3_POS = e4m3_decode(np.arange(0, 127, dtype=np.uint8)).astype(F64)  # codes 0..126, ascending
@@ -427,8 +437,11 @@ def _fp8_expert(Xd, w13q, w13s, w2q, w2s):
 
 
 def layer_output_fp8(x, topk_idx, topk_gate, w13q, w13s, w2q, w2s,
-                     ws13q=None, ws13s=None, ws2q=None, ws2s=None) -> np.ndarray:
-    """FP8 forward of the layer outputs, fp64 result (round to bf16 after)."""
+                     ws13q=None, ws13s=None, ws2q=None, ws2s=None, workers=1) -> np.ndarray:
+    """FP8 forward of the layer outputs, fp64 result (round to bf16 after).
+    With workers > 1 the experts' outputs are computed by that many threads
+    (each expert on its own rows); they are added in the same order either
+    way."""
     xq, xs = quantize_rows_1x128(np.asarray(x, F32))
     Xd = dequant_rows_1x128(xq, xs)
     idx = np.asarray(topk_idx)
@@ -436,10 +449,19 @@ def layer_output_fp8(x, topk_idx, topk_gate, w13q, w13s, w2q, w2s,
     y = np.zeros(Xd.shape, F64)
     if ws13q is not None:
         y += _fp8_expert(Xd, ws13q, ws13s, ws2q, ws2s)
-    for e in np.unique(idx):
+    experts = [int(e) for e in np.unique(idx)]
+
+    def one(e):
         rows, slots = np.nonzero(idx == e)
-        e = int(e)
-        ye = _fp8_expert(Xd[rows], w13q[e], w13s[e], w2q[e], w2s[e])
+        return rows, slots, _fp8_expert(Xd[rows], w13q[e], w13s[e], w2q[e], w2s[e])
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            outs = list(ex.map(one, experts))
+    else:
+        outs = [one(e) for e in experts]
+    for rows, slots, ye in outs:
         for i in range(rows.shape[0]):
             y[rows[i]] += g[rows[i], slots[i]] * ye[i]
     return y

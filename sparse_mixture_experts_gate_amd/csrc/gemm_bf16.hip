@@ -248,7 +248,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn1_bf16_kernel(FfnArgs a) {
         }
     }
   };
-  gemm_stream<C, true>(lds, first, nb, total, next_ops, nk_of, epilogue);
+  auto rows_of = [&](int tile) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    return c.rows - c.m * C::BM;
+  };
+  gemm_stream<C, true, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, true, -1,
+              false, false, decltype(rows_of)>(lds, first, nb, total, next_ops, nk_of, epilogue,
+                                               rows_of);
 }
 
 // y = H W2^T per group: routed rows to y_perm, shared rows to y_shared.
@@ -321,7 +327,13 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
         }
     }
   };
-  gemm_stream<C, false>(lds, first, nb, total, next_ops, nk_of, epilogue);
+  auto rows_of = [&](int tile) {
+    const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
+    return c.rows - c.m * C::BM;
+  };
+  gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, true, -1,
+              false, false, decltype(rows_of)>(lds, first, nb, total, next_ops, nk_of, epilogue,
+                                               rows_of);
 }
 
 // Router: partial[s][t][e] = sum over k-split s of x[t, k mod d] * wsplit[e, k],

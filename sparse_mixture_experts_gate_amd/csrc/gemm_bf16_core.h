@@ -205,11 +205,25 @@ __device__ __forceinline__ bf16x8_t frag_kmajor(uint32_t base, int n0, int k0, i
 // multiplies; the step's barrier sits before its last sub-step, whose
 // fragments are already in registers, so that the next stage's first
 // fragments are read while those MFMAs run.
+// rows_of(tile) (optional): rows of the tile that hold data (the rest are
+// padding past a group's last row). A wave whose 64-row band holds fewer
+// rows skips the MFMAs of its 32-row sub-tiles that lie wholly past them:
+// the count is fixed per tile, so each count runs its own copy of the k-loop
+// and no branch splits a step (the fragment reads stay as they are, so the
+// registers that carry the next tile's first sub-step are always filled).
+struct AllRows {
+  __device__ int operator()(int) const { return 1 << 30; }
+};
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, bool SWAP = true,
-          int POST = -1, bool BKM = false, bool AKM = false>
+          int POST = -1, bool BKM = false, bool AKM = false, class RowsOf = AllRows>
 __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, int total,
                                             NextOps&& next_ops, NkOf&& nk_of,
-                                            Epilogue&& epilogue) {
+                                            Epilogue&& epilogue, RowsOf rows_of = RowsOf{}) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -268,9 +282,9 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
     }
   };
   f32x16_t acc[C::MI][C::NJ];
-  auto mma = [&](int buf) {
+  auto mma = [&](int buf, auto nmi) {
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
+    for (int mi = 0; mi < decltype(nmi)::value; ++mi)
 #pragma unroll
       for (int nj = 0; nj < C::NJ; ++nj) {
         if constexpr (SWAP)
@@ -296,20 +310,21 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
   for (int tc = first; tc < total; tc += nb) {
     zero_acc<C>(acc);
     const int nkc = nk_of(tc);
+    auto kloop = [&](auto nmi) {
     for (int kc = 0; kc < nkc; ++kc) {
       issue(st_issue);  // into the stage read in the previous step
       fetch(st, 1, 1);
       // fragment reads go out before the MFMAs that do not need them (the
       // scheduler would otherwise reuse their registers and serialize)
       __builtin_amdgcn_sched_barrier(0);
-      mma(0);
+      mma(0, nmi);
       advance();
       fetch(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mma(1);
+      mma(1, nmi);
       fetch(st, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
-      mma(0);
+      mma(0, nmi);
       // this wave's part of the next stage has landed; the barrier makes
       // every wave's part visible and frees the stage whose last fragments
       // are now in registers
@@ -327,7 +342,21 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
       st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
       fetch(st, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mma(1);
+      mma(1, nmi);
+    }
+    };
+    // 32-row sub-tiles of this wave's band that hold data
+    const int band = rows_of(tc) - wm * C::WM;
+    const int nmi = band <= 0 ? 0 : band >= C::WM ? C::MI : (band + 31) / 32;
+    if (nmi >= C::MI) {
+      kloop(IntC<C::MI>{});
+    } else if constexpr (C::MI > 1) {
+      if (nmi == 1)
+        kloop(IntC<1>{});
+      else
+        kloop(IntC<0>{});
+    } else {
+      kloop(IntC<0>{});
     }
     epilogue(tc, acc);
   }

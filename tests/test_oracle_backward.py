@@ -157,3 +157,16 @@ def test_zero_score_sum_gives_constant_gates():
     gr2 = oracle.layer_backward(p["x"], p["wr"], u, p["idx"], p["w13"], p["w2"], p["ws13"],
                                 p["ws2"], p["dy"])
     assert np.max(np.abs(gr2.du)) > 0
+
+
+def test_threaded_experts_give_identical_results():
+    """Running the experts' backward passes on threads changes nothing: the
+    results are added in the same order."""
+    p = _tiny(seed=9, T=12, E=6, K=3)
+    u = p["x"] @ p["wr"].T
+    a = oracle.layer_backward(p["x"], p["wr"], u, p["idx"], p["w13"], p["w2"], p["ws13"],
+                              p["ws2"], p["dy"])
+    b = oracle.layer_backward(p["x"], p["wr"], u, p["idx"], p["w13"], p["w2"], p["ws13"],
+                              p["ws2"], p["dy"], workers=4)
+    for name in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2", "dg", "du"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name

@@ -528,3 +528,17 @@ def test_fp8_layer_with_power_of_two_scales_and_shared_expert():
     # outputs would fail
     ys = dense(E)[0]
     assert np.mean(np.abs(y8 - (ref - ys)) > bound) > 0.5
+
+
+def test_fp8_layer_threaded_experts_identical():
+    """layer_output_fp8 with its experts on threads equals the sequential run."""
+    rng = np.random.default_rng(20)
+    T, d, I, E, K = 16, 256, 128, 5, 2
+    x = rng.normal(size=(T, d)).astype(F32)
+    qs = [O.quantize_blocks_128(rng.normal(0, 0.05, (2 * I, d)).astype(F32)) for _ in range(E)]
+    q2 = [O.quantize_blocks_128(rng.normal(0, 0.05, (d, I)).astype(F32)) for _ in range(E)]
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    g = rng.uniform(0.2, 0.8, (T, K)).astype(F32)
+    args = (x, idx, g, [q[0] for q in qs], [q[1] for q in qs], [q[0] for q in q2],
+            [q[1] for q in q2])
+    assert np.array_equal(O.layer_output_fp8(*args), O.layer_output_fp8(*args, workers=3))
