@@ -16,8 +16,10 @@ fields it carries:
   extra         per-step median / p10 / p90, decode-sized batches
                 (T = 16/64/256: per-call median with L2 and the Infinity Cache
                 flushed by a 512 MB write before every call, HBM GB/s, and the
-                warm back-to-back time beside it), the fp8 layer and the stage
-                breakdown.
+                warm back-to-back time beside it), the fp8 layer, its 100-step
+                load-balancing loop beside the oracle's own loop, the small
+                bf16 and tiny fp32 layers, the training step, the oracle's
+                throughput per workload and the stage breakdown.
 """
 from __future__ import annotations
 
@@ -165,14 +167,20 @@ def traffic_record(kernel: str, workload: str):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(wl, P, n_tokens: int) -> dict:
-    """The CPU oracle, unchanged, on the first n_tokens tokens of the batch:
-    router product, routing and the fp64 experts. Weights of the experts those
-    tokens use are copied to the host before the clock starts."""
+def blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return int(max(blas) if blas else 1)
+
+
+def cpu_baseline(wl, P, n_tokens: int, x=None) -> dict:
+    """The CPU oracle, unchanged, on the first n_tokens tokens of the batch
+    (of ``x`` when given): router product, routing and the fp64 experts.
+    Weights of the experts those tokens use are copied to the host before the
+    clock starts."""
     import numpy as np
     import oracle as O
-    from threadpoolctl import threadpool_info
-    x = P["x"][:n_tokens].float().cpu().numpy()
+    x = (P["x"] if x is None else x)[:n_tokens].float().cpu().numpy()
     wr = P["w_router"].cpu().numpy()
     b = P["bias"].cpu().numpy()
     u = O.router_logits(x, wr)
@@ -185,8 +193,7 @@ def cpu_baseline(wl, P, n_tokens: int) -> dict:
     t0 = time.perf_counter()
     O.forward(x, wr, b, w13, w2, ws13, ws2, wl.K, wl.G, wl.M, wl.topn)
     secs = time.perf_counter() - t0
-    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    return {"value": n_tokens / secs, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
+    return {"value": n_tokens / secs, "unit": "tokens/s", "cores": blas_threads(),
             "kind": "oracle",
             "sample": f"{n_tokens} tokens of {wl.name} (T={wl.T}), full oracle forward "
                       f"(fp64 router product, routing, fp64 SwiGLU experts over the "
@@ -242,6 +249,130 @@ def achievable_peaks() -> dict:
         t = best(lambda: mb.dsmoe_mb_mfma(fp8, iters, blocks, sink.data_ptr(), stream))
         res[name] = blocks * 4 * iters * 8 * flops / t / 1e12
     return res
+
+
+def cpu_baseline_fp8(wl, layer_bf16_P, x, n_tokens: int, workers: int) -> dict:
+    """The oracle's FP8 forward on n_tokens tokens: routing from its own fp64
+    logits, x quantized in 1x128 tiles, the E4M3 experts (the oracle's own
+    128x128 block quantization of the bf16 weights, done before the clock,
+    like the library's once-per-weight-set preparation) with fp32 H
+    re-quantized. The experts run on ``workers`` threads."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle as O
+    P = layer_bf16_P
+    xh = x[:n_tokens].float().cpu().numpy()
+    u = O.router_logits(xh, P["w_router"].cpu().numpy())
+    rr = O.route(u, P["bias"].cpu().numpy(), wl.K, wl.G, wl.M, wl.topn)
+    need = [int(e) for e in np.unique(rr.idx)]
+
+    def quant(e):
+        return e, O.quantize_blocks_128(P["w13"][e].float().cpu().numpy()), \
+            O.quantize_blocks_128(P["w2"][e].float().cpu().numpy())
+
+    with ThreadPoolExecutor(workers) as ex:
+        qs = {e: (a, b) for e, a, b in ex.map(quant, need)}
+    sh13 = O.quantize_blocks_128(P["ws13"].float().cpu().numpy())
+    sh2 = O.quantize_blocks_128(P["ws2"].float().cpu().numpy())
+
+    class _Pick:
+        def __init__(self, which, part):
+            self.which, self.part = which, part
+
+        def __getitem__(self, e):
+            return qs[int(e)][self.which][self.part]
+
+    t0 = time.perf_counter()
+    u = O.router_logits(xh, P["w_router"].cpu().numpy())
+    rr = O.route(u, P["bias"].cpu().numpy(), wl.K, wl.G, wl.M, wl.topn)
+    O.layer_output_fp8(xh, rr.idx, rr.gate, _Pick(0, 0), _Pick(0, 1), _Pick(1, 0), _Pick(1, 1),
+                       sh13[0], sh13[1], sh2[0], sh2[1], workers=workers)
+    secs = time.perf_counter() - t0
+    return {"value": n_tokens / secs, "unit": "tokens/s", "cores": max(workers, blas_threads()),
+            "kind": "oracle",
+            "sample": f"{n_tokens} tokens of {wl.name}: fp64 router product, routing, FP8 "
+                      f"experts ({len(need)} routed + shared, E4M3 weights prepared before the "
+                      f"clock) on {workers} threads, {secs:.1f} s"}
+
+
+def small_record(dev, cpu: bool) -> dict:
+    """The small bf16 layer (T = 4096, d = 2048, 64 experts of 1408, top-6,
+    shared expert of 2816, clustered tokens): tokens/s, the layer's and the
+    gate/up GEMM's fraction of the bf16 MFMA peak, and the oracle on all its
+    tokens."""
+    import sparse_mixture_experts_gate_amd as M
+    from sparse_mixture_experts_gate_amd.workloads import CONFIGS, make_inputs
+    wl = CONFIGS["small_bf16"]
+    P = make_inputs(wl, dev)
+    layer = M.MoELayer(wl, P)
+    r = time_layer(layer, P["x"], 50, 5)
+    nt = int((r["out"]["counts"] > 0).sum())
+    a = algorithmic(wl, wl.T, nt)
+    ms = r["wall_ms_per_step"]
+    g1 = r["stage_ms"]["gemm_gate_up"]
+    rec = {"T": wl.T, "ms": ms, "ms_pctl": r["step_ms_pctl"], "tokens_per_s": wl.T / (ms / 1e3),
+           "layer_mfma_frac": a["layer_flops"] / (ms / 1e3) / MFMA_PEAK["bf16"],
+           "layer_hbm_frac": a["layer_bytes"] / (ms / 1e3) / HBM_PEAK,
+           "gemm_gate_up_ms": g1,
+           "gemm_gate_up_mfma_frac": a["g1_flops"] / (g1 / 1e3) / MFMA_PEAK["bf16"],
+           "stage_ms": r["stage_ms"], "n_touched": nt}
+    if cpu:
+        rec["cpu_oracle"] = cpu_baseline(wl, P, wl.T)
+    return rec
+
+
+def fp8_loop_record(layer8, wl8, P, dev, steps: int = 100) -> dict:
+    """The FP8 layer's load-balancing loop: `steps` forwards + bias updates
+    (gamma = 0.001) on fresh Zipf-skewed batches (seed 1000 + s), from the
+    layer's initial bias. Beside it the oracle runs the same loop on its own:
+    its own fp64 router logits, routing, counts and bias update on every
+    token of every batch (routing only, timed on the host cores). Reports
+    the max/mean expert load of both per step and their difference."""
+    import numpy as np
+    import torch
+    import oracle as O
+    from sparse_mixture_experts_gate_amd.workloads import make_tokens
+    T, E, K = wl8.T, wl8.E, wl8.K
+    mean = T * K / E
+    layer8.bias.copy_(P["bias"])
+    out = layer8.alloc_outputs(T)
+    layer8.workspace(T)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    gpu = []
+    for s in range(steps):
+        x = make_tokens(wl8, T, 1000 + s, dev)
+        ev[s][0].record()
+        layer8.forward(x, out, with_logits=False)
+        layer8.bias_update(out["counts"], T)
+        ev[s][1].record()
+        gpu.append(float(out["counts"].max().item()) / mean)
+    torch.cuda.synchronize()
+    step_ms = percentiles([a.elapsed_time(b) for a, b in ev])
+    wr = P["w_router"].cpu().numpy()
+    b = P["bias"].cpu().numpy()
+    ora, secs = [], 0.0
+    for s in range(steps):
+        xh = make_tokens(wl8, T, 1000 + s, dev).float().cpu().numpy()
+        t0 = time.perf_counter()
+        rr = O.route(O.router_logits(xh, wr), b, K, wl8.G, wl8.M, wl8.topn)
+        counts = np.bincount(rr.idx.ravel(), minlength=E)
+        b = O.bias_update(b, counts, wl8.gamma, T, K)
+        secs += time.perf_counter() - t0
+        ora.append(float(counts.max()) / mean)
+    diff = np.abs(np.asarray(gpu) - np.asarray(ora))
+    return {"steps": steps, "gamma": wl8.gamma, "T": T,
+            "gpu_step_ms": step_ms,
+            "max_over_mean_gpu": [round(v, 4) for v in gpu],
+            "max_over_mean_oracle": [round(v, 4) for v in ora],
+            "abs_diff_max": float(diff.max()), "abs_diff_mean": float(diff.mean()),
+            "first": {"gpu": gpu[0], "oracle": ora[0]},
+            "final": {"gpu": gpu[-1], "oracle": ora[-1]},
+            "mean_last10": {"gpu": float(np.mean(gpu[-10:])), "oracle": float(np.mean(ora[-10:]))},
+            "oracle_loop": {"value": steps * T / secs, "unit": "tokens/s", "seconds": secs,
+                            "cores": blas_threads(), "kind": "oracle",
+                            "sample": f"{steps} steps x {T} tokens, routing only (fp64 router "
+                                      f"product, routing, counts, bias update)"}}
 
 
 # sequences of the balance loss: the pages fix no length; 4096 tokens, two
@@ -322,6 +453,8 @@ def main() -> int:
                          "counters can be scaled against a kernel of known traffic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the FP8 layer's 100-step load-balancing loop and its oracle loop")
     ap.add_argument("--train-only", action="store_true",
                     help="only time the training step (forward, balance loss, backward) of the "
                          "workload and print that record (for profiling runs)")
@@ -441,10 +574,37 @@ def main() -> int:
                     f"{dec8[str(T)]['hbm_GBps']:.0f} GB/s, {nt} experts; warm back-to-back "
                     f"{rd['wall_ms_per_step']:.3f} ms")
             extra["decode_fp8"] = dec8
+            if not args.no_loop:
+                log("fp8 load-balancing loop: 100 steps, then the oracle's own loop")
+                lp = fp8_loop_record(layer8, wl8, P, dev)
+                extra["fp8_bias_loop"] = lp
+                log(f"fp8 loop: max/mean load gpu {lp['first']['gpu']:.3f} -> "
+                    f"{lp['final']['gpu']:.3f}, oracle {lp['first']['oracle']:.3f} -> "
+                    f"{lp['final']['oracle']:.3f}, max |diff| {lp['abs_diff_max']:.3f}; oracle "
+                    f"loop {lp['oracle_loop']['value']:.0f} tokens/s")
             del layer8
         except M.MoeError as e:
             extra["fp8"] = {"error": str(e)}
             log(f"fp8: {e}")
+        log("small bf16 layer")
+        sm = small_record(dev, not args.no_cpu_baseline)
+        extra["small_bf16"] = sm
+        log(f"small_bf16: {sm['ms']:.3f} ms, {sm['tokens_per_s'] / 1e6:.2f} M tok/s, layer MFMA "
+            f"{sm['layer_mfma_frac']:.1%}, gate/up GEMM MFMA {sm['gemm_gate_up_mfma_frac']:.1%}")
+        tw = CONFIGS["tiny_f32"]
+        Pt = make_inputs(tw, dev)
+        rt = time_layer(M.MoELayer(tw, Pt), Pt["x"], 50, 5)
+        extra["tiny_f32"] = {"T": tw.T, "ms": rt["wall_ms_per_step"],
+                             "tokens_per_s": tw.T / (rt["wall_ms_per_step"] / 1e3)}
+        if not args.no_cpu_baseline:
+            cpus = {"tiny_f32": cpu_baseline(tw, Pt, tw.T)}
+            xd = make_tokens(CONFIGS["v3_decode_bf16"], 64, 3, dev)
+            cpus["v3_decode_bf16_T64"] = cpu_baseline(wl, P, 64, x=xd)
+            workers = max(1, min(16, len(os.sched_getaffinity(0))))
+            cpus["v3_fp8"] = cpu_baseline_fp8(CONFIGS["v3_fp8"], P, P["x"], 8, workers)
+            extra["cpu_oracle_per_config"] = cpus
+            log("cpu oracle per config: " + json.dumps(
+                {k: round(v["value"], 1) for k, v in cpus.items()}))
 
     cpu = None
     if not args.no_cpu_baseline:

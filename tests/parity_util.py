@@ -1,5 +1,7 @@
 """Helpers shared by the GPU parity tests: host copies, the row-max relative
 error metric, lazy per-expert host views for the oracle."""
+import threading
+
 import numpy as np
 import torch
 
@@ -33,12 +35,21 @@ def mat_rel_err(y, ref) -> float:
 
 class LazyHost:
     """Indexable host view of a device tensor [E, ...]: expert e is copied to
-    the host (as fp32) when the oracle asks for it, and not kept."""
+    the host (as fp32) when the oracle asks for it, and not kept. With a
+    label, every 32nd copy prints a progress line."""
 
-    def __init__(self, t: torch.Tensor):
+    def __init__(self, t: torch.Tensor, label: str | None = None):
         self.t = t
+        self.label = label
+        self.n = 0
+        self.lock = threading.Lock()
 
     def __getitem__(self, e):
+        if self.label:
+            with self.lock:
+                self.n += 1
+                if self.n % 32 == 0:
+                    print(f"    oracle: {self.n} {self.label} copies", flush=True)
         return host(self.t[int(e)])
 
 

@@ -171,7 +171,7 @@ def test_backward_v3_sampled():
     logits = host(sv["logits"])
     idx = host(sv["topk_idx"])
     dyh = host(dy)
-    w13, w2 = LazyHost(P["w13"]), LazyHost(P["w2"])
+    w13, w2 = LazyHost(P["w13"], "expert"), LazyHost(P["w2"])
     ws13, ws2 = host(P["ws13"]), host(P["ws2"])
     tol = TOL["bf16"]
     # input gradient of 256 seeded tokens: one oracle call over those tokens

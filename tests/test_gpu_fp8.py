@@ -39,6 +39,8 @@ class LazyQuant:
             hit = O.quantize_blocks_128(host(self.t[e]))
             with self.lock:
                 self.cache[e] = hit
+                if len(self.cache) % 32 == 0:
+                    print(f"    oracle: {len(self.cache)} experts quantized", flush=True)
         return hit
 
 
