@@ -201,6 +201,30 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
                                 int32_t* near_tie, float* logits, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. deepseek_moe_forward with the same arguments and results, except
+ * that its workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of a caller buffer; the call allocates and frees nothing.
+ *   - Each GPU the library runs on holds its own copy of that array from the
+ *     first call on it until the process ends; the first call on a device
+ *     looks its address up (hipGetSymbolAddress), with that device current.
+ *   - A call whose workspace (moe_workspace_size) exceeds the array returns
+ *     MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (at the V3 shape,
+ *     d = 7168 and 256 experts of 2048 plus a shared one, calls of up to 532
+ *     tokens fit with bf16 weights and up to 557 with FP8 weights).
+ *   - Every call on one GPU uses the same array: calls on one GPU that
+ *     overlap in time (e.g. on different streams without ordering between
+ *     them) race and must be serialized by the caller. Nothing in the array
+ *     needs to start zeroed: every buffer the forward keeps there is written
+ *     before it is read, on every call. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status deepseek_moe_forward_noalloc(const moe_layer_desc* desc, const void* x,
+                                        const float* w_router, const float* bias,
+                                        const moe_weights* w, void* y, int32_t* topk_idx,
+                                        float* topk_gate, int32_t* counts, int32_t* near_tie,
+                                        float* logits, hipStream_t stream);
+
 /* FP8 weight preparation, once per weight set: n_mats matrices [rows, cols]
  * of `src_dtype` (MOE_DT_F32 or MOE_DT_BF16) -> E4M3 codes q (same shape) and
  * fp32 scales [n_mats, rows/128, cols/128]. Per 128x128 block: amax = max|w|;

@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": [D, P, P, P, P, P, P],
             "moe_bias_update": [D, P, F, P, P],
             "deepseek_moe_forward": [D, P, P, P, W, P, P, P, P, P, P, P, ctypes.c_size_t, P],
+            "deepseek_moe_forward_noalloc": [D, P, P, P, W, P, P, P, P, P, P, P],
             "moe_quantize_fp8_blocks": [P, I32, I64, I32, I32, P, P, P],
             "moe_quantize_fp8_rows": [P, I32, I64, I32, P, P, P],
             "moe_profile_events": [ctypes.POINTER(ctypes.c_void_p), I32],
@@ -187,6 +188,15 @@ def deepseek_moe_forward(desc, x, w_router, bias, weights: MoeWeights, y, topk_i
                                       _p(counts), _p(near_tie), _p(logits), _p(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)),
            "deepseek_moe_forward")
+
+
+def deepseek_moe_forward_noalloc(desc, x, w_router, bias, weights: MoeWeights, y, topk_idx,
+                                 topk_gate, counts, near_tie, logits, stream=None):
+    _check(lib().deepseek_moe_forward_noalloc(ctypes.byref(desc), _p(x), _p(w_router), _p(bias),
+                                              ctypes.byref(weights), _p(y), _p(topk_idx),
+                                              _p(topk_gate), _p(counts), _p(near_tie), _p(logits),
+                                              _stream(stream)),
+           "deepseek_moe_forward_noalloc")
 
 
 def _dt(t) -> int:

@@ -6,7 +6,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
+
+#include <hip/hip_runtime.h>
 
 #include "dsmoe.h"
 #include "internal.h"
@@ -478,6 +481,51 @@ SeqBalLayout seqbal_layout(const moe_layer_desc* d, int32_t seq_len) {
   return L;
 }
 
+moe_status check_forward_ptrs(const void* x, const float* w_router, const float* bias, void* y,
+                              int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                              int32_t* near_tie, float* logits) {
+  moe_status st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {bias, "bias"}, {y, "y"},
+                              {topk_idx, "topk_idx"}, {topk_gate, "topk_gate"},
+                              {counts, "counts"}});
+  if (st) return st;
+  return check_opt({{near_tie, "near_tie"}, {logits, "logits"}});
+}
+
+moe_status run_forward(const moe_layer_desc* desc, const void* x, const float* w_router,
+                       const float* bias, const moe_weights* w, void* y, int32_t* topk_idx,
+                       float* topk_gate, int32_t* counts, int32_t* near_tie, float* logits,
+                       void* ws, const FwdLayout& L, hipStream_t stream);
+
+// ---- fixed scratch of the allocation-free forward ------------------------------
+//
+// Workspace of deepseek_moe_forward_noalloc: a file-scope device array, so the
+// call allocates nothing. Each GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` only names the array: its
+// device address, per GPU, comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is passed on.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_ptr(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -666,16 +714,53 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
   st = check_weights(desc, w);
   if (st) return st;
   if (desc->T == 0) return zero_counts(desc, counts, near_tie, stream);
-  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {bias, "bias"}, {y, "y"},
-                   {topk_idx, "topk_idx"}, {topk_gate, "topk_gate"}, {counts, "counts"},
-                   {ws, "ws"}});
+  st = check_forward_ptrs(x, w_router, bias, y, topk_idx, topk_gate, counts, near_tie, logits);
   if (st) return st;
-  st = check_opt({{near_tie, "near_tie"}, {logits, "logits"}});
+  st = check_ptrs({{ws, "ws"}});
   if (st) return st;
   const FwdLayout L = fwd_layout(desc);
   if (ws_bytes < L.bytes)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
                 "deepseek_moe_forward needs %zu workspace bytes, got %zu", L.bytes, ws_bytes);
+  return run_forward(desc, x, w_router, bias, w, y, topk_idx, topk_gate, counts, near_tie, logits,
+                     ws, L, stream);
+}
+
+moe_status deepseek_moe_forward_noalloc(const moe_layer_desc* desc, const void* x,
+                                        const float* w_router, const float* bias,
+                                        const moe_weights* w, void* y, int32_t* topk_idx,
+                                        float* topk_gate, int32_t* counts, int32_t* near_tie,
+                                        float* logits, hipStream_t stream) {
+  moe_status st = validate_desc(desc);
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (desc->T == 0) return zero_counts(desc, counts, near_tie, stream);
+  st = check_forward_ptrs(x, w_router, bias, y, topk_idx, topk_gate, counts, near_tie, logits);
+  if (st) return st;
+  const FwdLayout L = fwd_layout(desc);
+  if (L.bytes > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "deepseek_moe_forward_noalloc: this call needs %zu workspace bytes, the fixed "
+                "scratch holds %zu (use deepseek_moe_forward with a caller workspace)",
+                L.bytes, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st) return st;
+  return run_forward(desc, x, w_router, bias, w, y, topk_idx, topk_gate, counts, near_tie, logits,
+                     ws, L, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The forward on a validated call (T > 0) with workspace ws of L.bytes.
+moe_status run_forward(const moe_layer_desc* desc, const void* x, const float* w_router,
+                       const float* bias, const moe_weights* w, void* y, int32_t* topk_idx,
+                       float* topk_gate, int32_t* counts, int32_t* near_tie, float* logits,
+                       void* ws, const FwdLayout& L, hipStream_t stream) {
+  moe_status st;
   void* gws = at<void>(ws, L.gate_base);
   void* fws = at<void>(ws, L.ffn_base);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
@@ -703,6 +788,10 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
   HIP_TRY(prof_record(5, stream), "profile event");
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 moe_status moe_profile_events(const hipEvent_t* events, int32_t n_events) {
   if (!events || n_events == 0) {

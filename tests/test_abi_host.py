@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
         "moe_last_error", "moe_abi_version", "moe_profile_events", "moe_forward_train",
         "moe_backward_workspace_size", "moe_backward", "moe_seq_balance_workspace_size",
-        "moe_seq_balance_loss"}
+        "moe_seq_balance_loss", "deepseek_moe_forward_noalloc"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
@@ -200,3 +200,28 @@ def test_seq_balance_validates_before_launch(L):
     assert call(args(u=None)) == 1 and b"logits is NULL" in lib.moe_last_error()
     assert call(args(dl=ctypes.c_void_p(4100))) == 3
     assert call(args(), ws=16) == 4 and b"workspace" in lib.moe_last_error()
+
+
+def test_noalloc_forward_validates_before_touching_the_device(L):
+    """The allocation-free forward checks its arguments and that the call's
+    workspace fits the fixed scratch before it looks the scratch up or
+    launches anything (no GPU is needed to see these errors)."""
+    lib = L.lib()
+    good = ctypes.c_void_p(4096)
+    w = L.MoeWeights(4096, 4096, 4096, 4096, None, None, None, None)
+    args = lambda d, x=good: (ctypes.byref(d), x, good, good, ctypes.byref(w), good, good, good,
+                              good, None, None, None)
+    d = _desc(L)
+    assert lib.deepseek_moe_forward_noalloc(*args(d, None)) == 1
+    assert b"x is NULL" in lib.moe_last_error()
+    assert lib.deepseek_moe_forward_noalloc(*args(d, ctypes.c_void_p(4100))) == 3
+    # V3-shaped layer: T = 532 fits the 128 MiB scratch in bf16, T = 533 does not
+    v3 = dict(d=7168, n_experts=256, top_k=8, n_groups=8, topk_groups=4, inter=2048,
+              shared_inter=2048)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(_desc(L, T=532, **v3)), ctypes.byref(n)) == 0
+    assert n.value <= 128 << 20
+    big = _desc(L, T=533, **v3)
+    assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 128 << 20
+    assert lib.deepseek_moe_forward_noalloc(*args(big)) == 4
+    assert b"fixed scratch" in lib.moe_last_error()
