@@ -486,7 +486,10 @@ def main() -> int:
         log(f"train: forward {rec['fwd_train_ms']:.3f} ms, balance loss "
             f"{rec['balance_loss']['ms']:.3f} ms, backward {rec['bwd_ms']:.3f} ms "
             f"({rec['bwd_tflops']:.0f} TFLOP/s)")
-        print(json.dumps({"train_bf16": rec, "workload": wl.name}), flush=True)
+        if wl.w == "fp8":
+            rec["bwd_mfma_frac_fp8"] = rec["bwd_tflops"] * 1e12 / MFMA_PEAK["fp8"]
+        key = "train_fp8" if wl.w == "fp8" else "train_bf16"
+        print(json.dumps({key: rec, "workload": wl.name}), flush=True)
         return 0
     log(f"timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
     r = time_layer(layer, P["x"], args.steps, args.warmup)
@@ -574,6 +577,16 @@ def main() -> int:
                     f"{dec8[str(T)]['hbm_GBps']:.0f} GB/s, {nt} experts; warm back-to-back "
                     f"{rd['wall_ms_per_step']:.3f} ms")
             extra["decode_fp8"] = dec8
+            tr8 = train_record(wl8, wl8.T, time_train(layer8, P["x"], 5, 2))
+            tr8["bwd_mfma_frac_fp8"] = tr8["bwd_tflops"] * 1e12 / MFMA_PEAK["fp8"]
+            extra["train_fp8"] = tr8
+            log(f"train fp8: forward {tr8['fwd_train_ms']:.3f} ms, balance loss "
+                f"{tr8['balance_loss']['ms']:.3f} ms, backward {tr8['bwd_ms']:.3f} ms "
+                f"({tr8['bwd_tflops']:.0f} TFLOP/s)")
+            layer8._bws = None
+            layer8._sws = None
+            layer8._wt = layer8._wt_tensors = None
+            torch.cuda.empty_cache()
             if not args.no_loop:
                 log("fp8 load-balancing loop: 100 steps, then the oracle's own loop")
                 lp = fp8_loop_record(layer8, wl8, P, dev)

@@ -242,7 +242,8 @@ moe_status moe_quantize_fp8_rows(const void* src, int32_t src_dtype, int64_t n, 
 
 /* ---- Training: forward that keeps tensors for the backward, and the backward
  *
- * bf16 activations and bf16 weights only (other dtypes: MOE_ERR_UNSUPPORTED).
+ * bf16 activations with bf16 weights (moe_backward) or FP8 weights
+ * (moe_backward_fp8); other dtypes: MOE_ERR_UNSUPPORTED.
  * The backward differentiates the layer for the selection its forward made
  * (top-K is piecewise constant in every parameter): with the gates
  * g = s / S over the selected sigmoid scores (kaiyunto.com walkthrough,
@@ -279,7 +280,9 @@ typedef struct moe_saved {
 
 /* deepseek_moe_forward that also fills `saved` (every field required; h and
  * gu have TK + T rows when Is > 0, TK rows otherwise). Same workspace as
- * deepseek_moe_forward. */
+ * deepseek_moe_forward. With FP8 weights the forward is the FP8 one (its
+ * down projection reads H in E4M3); saved.h then holds H in bf16 and
+ * saved.gu the fp32-accumulated pre-activations in bf16. */
 moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const float* w_router,
                              const float* bias, const moe_weights* w, void* y,
                              const moe_saved* saved, int32_t* near_tie, void* ws,
@@ -297,7 +300,8 @@ typedef struct moe_grads {
   float* dw_router;
 } moe_grads;
 
-/* Bytes of workspace moe_backward needs for `desc`. Host only. */
+/* Bytes of workspace moe_backward (bf16 weights) or moe_backward_fp8 (FP8
+ * weights) needs for `desc`. Host only. */
 moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes);
 
 /* Backward of the layer from the output gradient dy [T, d] bf16:
@@ -308,6 +312,40 @@ moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes
 moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* w_router,
                         const moe_weights* w, const moe_saved* saved, const void* dy, void* dx,
                         const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Transposed copies of block-quantized FP8 weights, for the FP8 backward:
+ * q [n_mats, rows, cols] E4M3 codes with scales [n_mats, rows/128,
+ * cols/128] (as moe_quantize_fp8_blocks writes them) -> qt [n_mats, cols,
+ * rows] and scale_t [n_mats, cols/128, rows/128]. A 128x128 block of W is a
+ * block of W^T with the same scale, so this is exactly the block
+ * quantization of the transposed matrices (mhpq.cn "DeepSeek-V3 高效训练
+ * 关键技术全景解析" §4.1: 128x128 weight blocks). rows, cols multiples of
+ * 128. Weight preparation: once per weight set. */
+moe_status moe_transpose_fp8_blocks(const uint8_t* q, const float* scale, int64_t n_mats,
+                                    int32_t rows, int32_t cols, uint8_t* qt, float* scale_t,
+                                    hipStream_t stream);
+
+/* Backward of the FP8 layer (bf16 activations, E4M3 weights): the forward
+ * computes in E4M3, the backward in E5M2 (10100.com DeepSeek-V3 technical
+ * report article, FP8 paragraph), with 1x128 tiles for activations and
+ * gradients and the 128x128 weight blocks (mhpq.cn §4.1), fp32 accumulation.
+ * Every GEMM of the backward contracts FP8 operands quantized along its own
+ * contraction axis:
+ *   - input gradients: the gradient rows (gated output gradients, then
+ *     [da | db]) in E5M2 1x128 tiles, times the forward's E4M3 weights read
+ *     through the transposed copies `wt` (w13 [E, d, 2I] = [W1; W3]^T, w2
+ *     [E, I, d] = W2^T, ws13 [d, 2Is], ws2 [Is, d] and their scales, from
+ *     moe_transpose_fp8_blocks);
+ *   - weight gradients: contraction over each expert's tokens, both
+ *     operands in 128x1 tiles (128 consecutive tokens of the segment per
+ *     channel): dY and [da | db] in E5M2, H and x in E4M3.
+ * The gates, the router and the combine stay in high precision, as in
+ * moe_backward. x, w_router, w, saved, dy, dx, g as in moe_backward (saved
+ * from moe_forward_train with the same FP8 weights). */
+moe_status moe_backward_fp8(const moe_layer_desc* desc, const void* x, const float* w_router,
+                            const moe_weights* w, const moe_weights* wt, const moe_saved* saved,
+                            const void* dy, void* dx, const moe_grads* g, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* ---- Sequence-level balance loss of the router
  *

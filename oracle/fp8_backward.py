@@ -25,13 +25,22 @@ exponent holds infinities and NaNs, so the largest finite value is 57344.
 Scaling as for E4M3: scale = amax / 57344, codes of fl32(v * fl32(57344 /
 amax)), round to nearest even, saturating at 57344; an all-zero group gets
 scale 1 and zero codes.
+
+Precision of what gets quantized: a code is an integer decided by floating
+point, so each quantizer reads the values the layer keeps, in the precision
+it keeps them (as in the bf16 backward, intermediates are bf16): the gated
+output gradient bf16(fl32(g) * dy) with the forward's fp32 gates, the
+pre-activations a, b and H in bf16 as the training forward saves them (the
+forward itself uses their fp32 values), [da | db] in fp32 for the input
+gradient (formed in the down GEMM's epilogue) and in bf16 for the weight
+gradient, x in bf16. Everything after the quantizers is fp64.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .moe_oracle import (e4m3_decode, e4m3_encode, _silu64, router_logits,  # noqa: F401
-                         sigmoid_f32)
+                         round_bf16, sigmoid_f32)
 from .moe_backward import LayerGrads, _sigmoid64
 
 F32 = np.float32
@@ -69,12 +78,12 @@ def e5m2_encode(v) -> np.ndarray:
     |v| = 1.f * 2^E, a normal code (E >= -14) counts steps of 2^(E-2), a
     subnormal one steps of 2^-16: code = (E + 15) * 4 + (steps - 4), or steps."""
     v = np.asarray(v, dtype=F32)
-    a = np.minimum(np.abs(v).astype(F64), E5M2_MAX)
+    a = np.minimum(np.abs(v), F32(E5M2_MAX))  # fp32: the scalings and rint are exact
     _, e = np.frexp(a)
     E = e - 1
     sub = E < -14
     step_exp = np.where(sub, -16, E - 2)
-    steps = np.rint(np.ldexp(a, -step_exp)).astype(np.int64)
+    steps = np.rint(np.ldexp(a, -step_exp)).astype(np.int32)
     code = np.where(sub, steps, (E + 15) * 4 + (steps - 4))
     code = np.where(a == 0.0, 0, code).astype(np.uint8)
     return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
@@ -156,18 +165,20 @@ def _dq_blocks(q, s) -> np.ndarray:
     return e4m3_decode(q).astype(F64) * sc
 
 
-def fp8_expert_backward(X, w13q, w13s, w2q, w2s, dY):
+def fp8_expert_backward(X, w13q, w13s, w2q, w2s, dY, weight_grads: bool = True):
     """Backward of one expert of the FP8 layer on rows X (bf16 values) with
-    output gradient dY (fp64), for the FP8 forward the layer computed:
-    X in E4M3 1x128 tiles, E4M3 128x128 weight blocks, fp32 pre-activations
-    a, b and H = silu(a) * b. Returns (dX, dW13, dW2, Y) in fp64, where
+    output gradient dY (the stored bf16 values), for the FP8 forward the
+    layer computed: X in E4M3 1x128 tiles, E4M3 128x128 weight blocks, fp32
+    pre-activations a, b and H = silu(a) * b. With a16, b16, H16 their bf16
+    copies, returns (dX, dW13, dW2, Y) in fp64, where
       dH  = deq(E5M2 1x128 of dY) W2,        (contraction over d)
-      da  = dH * b * silu'(a),  db = dH * silu(a),
+      da  = fl32(dH * b16 * silu'(a16)),  db = fl32(dH * silu(a16)),
       dX  = deq(E5M2 1x128 of [da | db]) [W1; W3],   (contraction over 2I)
-      dW2 = deq(E5M2 128x1 of dY)^T deq(E4M3 128x1 of H),
-      dW13 = deq(E5M2 128x1 of [da | db])^T deq(E4M3 128x1 of X)
+      dW2 = deq(E5M2 128x1 of dY)^T deq(E4M3 128x1 of H16),
+      dW13 = deq(E5M2 128x1 of bf16([da | db]))^T deq(E4M3 128x1 of X)
     (weight gradients contract over the rows, in 128-row tiles), and Y is
-    the forward output (H re-quantized in E4M3 1x128 tiles)."""
+    the forward output (fp32 H re-quantized in E4M3 1x128 tiles). With
+    weight_grads=False the weight gradients are not formed (None)."""
     from .moe_oracle import dequant_rows_1x128, quantize_rows_1x128
     X = np.asarray(X, F32)
     W13 = _dq_blocks(w13q, w13s)
@@ -177,21 +188,26 @@ def fp8_expert_backward(X, w13q, w13s, w2q, w2s, dY):
     Xd = dequant_rows_1x128(xq, xs)
     a = (Xd @ W13[:inter].T).astype(F32).astype(F64)
     b = (Xd @ W13[inter:].T).astype(F32).astype(F64)
-    sa = _sigmoid64(a)
-    H = (a * sa * b).astype(F32)
+    H = (a * _sigmoid64(a) * b).astype(F32)
     hq, hs = quantize_rows_1x128(H)
     Y = dequant_rows_1x128(hq, hs) @ W2.T
+    a16 = round_bf16(a).astype(F64)
+    b16 = round_bf16(b).astype(F64)
+    H16 = round_bf16(H)
     dY32 = np.asarray(dY, F64).astype(F32)
     dYd = dequant_1x128(*quantize_1x128(dY32, "e5m2"), "e5m2")
     dH = dYd @ W2
-    da = dH * b * (sa * (1.0 + a * (1.0 - sa)))
-    db = dH * a * sa
+    sa = _sigmoid64(a16)
+    da = dH * b16 * (sa * (1.0 + a16 * (1.0 - sa)))
+    db = dH * a16 * sa
     dG32 = np.concatenate([da, db], axis=1).astype(F32)
     dGd = dequant_1x128(*quantize_1x128(dG32, "e5m2"), "e5m2")
     dX = dGd @ W13
+    if not weight_grads:
+        return dX, None, None, Y
     dW2 = dequant_128x1(*quantize_128x1(dY32, "e5m2"), "e5m2").T @ \
-        dequant_128x1(*quantize_128x1(H, "e4m3"), "e4m3")
-    dW13 = dequant_128x1(*quantize_128x1(dG32, "e5m2"), "e5m2").T @ \
+        dequant_128x1(*quantize_128x1(H16, "e4m3"), "e4m3")
+    dW13 = dequant_128x1(*quantize_128x1(round_bf16(dG32), "e5m2"), "e5m2").T @ \
         dequant_128x1(*quantize_128x1(X, "e4m3"), "e4m3")
     return dX, dW13, dW2, Y
 
@@ -201,7 +217,8 @@ def layer_backward_fp8(x, w_router, logits, topk_idx, w13q, w13s, w2q, w2s,
     """Gradients of L = sum <dy, y> for the FP8 layer with the selection
     fixed to ``topk_idx``: as ``layer_backward``, with every expert's backward
     taken by ``fp8_expert_backward`` (routed experts on their rows with the
-    gated output gradient g * dy, the shared expert on every row with dy).
+    gated output gradient bf16(fl32(g) * dy), g the forward's fp32 gates, the
+    shared expert on every row with dy).
     The gates, the router and the combine stay in high precision (the gating
     module is kept in high precision [MH §4.1]): dg = <dy, y_e> with the
     expert's FP8 forward output. ``experts`` restricts the stored routed
@@ -223,6 +240,9 @@ def layer_backward_fp8(x, w_router, logits, topk_idx, w13q, w13s, w2q, w2s,
         S32 = (S32 + s32[:, k]).astype(F32)
     safe = S32 > 0
     g = np.where(safe[:, None], s / np.where(safe, S, 1.0)[:, None], 1.0 / K)
+    # the forward's fp32 gates: selected fp32 scores over their fp32 sum
+    g32 = np.where(safe[:, None], (s32 / np.where(safe, S32, F32(1.0))[:, None]).astype(F32),
+                   F32(1.0) / F32(K)).astype(F32)
     dx = np.zeros((T, d), F64)
     dg = np.zeros((T, K), F64)
     inter = np.asarray(w13q[int(idx.flat[0])]).shape[0] // 2 if T > 0 else 0
@@ -232,11 +252,10 @@ def layer_backward_fp8(x, w_router, logits, topk_idx, w13q, w13s, w2q, w2s,
 
     def one(e):
         rows, slots = np.nonzero(idx == e)
-        dYe = g[rows, slots][:, None] * dy[rows]
+        dYe = round_bf16((g32[rows, slots][:, None] * dy[rows].astype(F32)).astype(F32))
+        keep = wanted is None or e in wanted
         dXe, dW13e, dW2e, Ye = fp8_expert_backward(x[rows], w13q[e], w13s[e], w2q[e], w2s[e],
-                                                   dYe)
-        if wanted is not None and e not in wanted:
-            dW13e = dW2e = None
+                                                   dYe, keep)
         return e, rows, slots, dXe, dW13e, dW2e, Ye
 
     ids = [int(e) for e in np.unique(idx)]

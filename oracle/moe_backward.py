@@ -49,10 +49,11 @@ def _sigmoid64(z):
         return 1.0 / (1.0 + np.exp(-z))
 
 
-def swiglu_expert_backward(X, w13, w2, dY):
+def swiglu_expert_backward(X, w13, w2, dY, weight_grads: bool = True):
     """Gradients of Y = (silu(X W1^T) * (X W3^T)) W2^T, with w13 = [W1; W3]
     stacked as [2I, d] and w2 = [d, I], for the output gradient dY.
-    Returns (dX [n, d], dW13 [2I, d], dW2 [d, I], Y [n, d]), all fp64."""
+    Returns (dX [n, d], dW13 [2I, d], dW2 [d, I], Y [n, d]), all fp64; with
+    weight_grads=False the two weight gradients are not formed (None)."""
     X = np.asarray(X, F64)
     w13 = np.asarray(w13, F64)
     w2 = np.asarray(w2, F64)
@@ -65,12 +66,14 @@ def swiglu_expert_backward(X, w13, w2, dY):
     silu = a * sa
     h = silu * b
     Y = h @ w2.T
-    dW2 = dY.T @ h
     dh = dY @ w2
     da = dh * b * (sa * (1.0 + a * (1.0 - sa)))
     db = dh * silu
-    dW13 = np.concatenate([da.T @ X, db.T @ X], axis=0)
     dX = da @ W1 + db @ W3
+    if not weight_grads:
+        return dX, None, None, Y
+    dW2 = dY.T @ h
+    dW13 = np.concatenate([da.T @ X, db.T @ X], axis=0)
     return dX, dW13, dW2, Y
 
 
@@ -127,9 +130,8 @@ def layer_backward(x, w_router, logits, topk_idx, w13, w2, ws13, ws2, dy,
     def one(e):
         rows, slots = np.nonzero(idx == e)
         dYe = g[rows, slots][:, None] * dy[rows]
-        dXe, dW13e, dW2e, Ye = swiglu_expert_backward(x[rows], w13[e], w2[e], dYe)
-        if wanted is not None and e not in wanted:
-            dW13e = dW2e = None
+        keep = wanted is None or e in wanted
+        dXe, dW13e, dW2e, Ye = swiglu_expert_backward(x[rows], w13[e], w2[e], dYe, keep)
         return e, rows, slots, dXe, dW13e, dW2e, Ye
 
     ids = [int(e) for e in np.unique(idx)]

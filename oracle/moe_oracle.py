@@ -337,15 +337,16 @@ def e4m3_encode(v) -> np.ndarray:
     From the format: with |v| = 1.f * 2^E, a normal code (E >= -6) counts steps
     of 2^(E-3) (3 mantissa bits), a subnormal one steps of 2^-9. The magnitude
     divided by its step is rounded to the nearest integer, ties to even (exact
-    in fp64); code = (E + 7) * 8 + (steps - 8) for normals (steps == 16 rolls
-    into the next binade by itself), code = steps for subnormals."""
+    in fp32: scaling by a power of two and rint lose nothing); code =
+    (E + 7) * 8 + (steps - 8) for normals (steps == 16 rolls into the next
+    binade by itself), code = steps for subnormals."""
     v = np.asarray(v, dtype=F32)
-    a = np.minimum(np.abs(v).astype(F64), 448.0)
+    a = np.minimum(np.abs(v), F32(448.0))
     _, e = np.frexp(a)
     E = e - 1
     sub = E < -6
     step_exp = np.where(sub, -9, E - 3)
-    steps = np.rint(np.ldexp(a, -step_exp)).astype(np.int64)
+    steps = np.rint(np.ldexp(a, -step_exp)).astype(np.int32)
     code = np.where(sub, steps, (E + 7) * 8 + (steps - 8))
     code = np.where(a == 0.0, 0, code).astype(np.uint8)
     return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)

@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
             "moe_backward_workspace_size": [D, ctypes.POINTER(ctypes.c_size_t)],
             "moe_backward": [D, P, P, W, ctypes.POINTER(MoeSaved), P, P, ctypes.POINTER(MoeGrads),
                              P, ctypes.c_size_t, P],
+            "moe_transpose_fp8_blocks": [P, P, I64, I32, I32, P, P, P],
+            "moe_backward_fp8": [D, P, P, W, W, ctypes.POINTER(MoeSaved), P, P,
+                                 ctypes.POINTER(MoeGrads), P, ctypes.c_size_t, P],
             "moe_seq_balance_workspace_size": [D, I32, ctypes.POINTER(ctypes.c_size_t)],
             "moe_seq_balance_loss": [D, I32, F, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         }
@@ -274,3 +277,21 @@ def moe_seq_balance_loss(desc, seq_len: int, alpha: float, x, w_router, logits, 
                                       _p(logits), _p(topk_idx), _p(loss), _p(dlogits), _p(dx),
                                       _p(dw_router), _p(ws), ws.numel() * ws.element_size(),
                                       _stream(stream)), "moe_seq_balance_loss")
+
+
+def moe_transpose_fp8_blocks(q, scale, qt, scale_t, stream=None):
+    """q [n_mats, rows, cols] uint8 (or [rows, cols]), scale fp32
+    [n_mats, rows/128, cols/128] -> qt [.., cols, rows], scale_t
+    [.., cols/128, rows/128]."""
+    shp = q.shape if q.dim() == 3 else (1, *q.shape)
+    _check(lib().moe_transpose_fp8_blocks(_p(q), _p(scale), shp[0], shp[1], shp[2], _p(qt),
+                                          _p(scale_t), _stream(stream)),
+           "moe_transpose_fp8_blocks")
+
+
+def moe_backward_fp8(desc, x, w_router, weights: MoeWeights, weights_t: MoeWeights,
+                     saved: MoeSaved, dy, dx, grads: MoeGrads, ws, stream=None):
+    _check(lib().moe_backward_fp8(ctypes.byref(desc), _p(x), _p(w_router), ctypes.byref(weights),
+                                  ctypes.byref(weights_t), ctypes.byref(saved), _p(dy), _p(dx),
+                                  ctypes.byref(grads), _p(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "moe_backward_fp8")

@@ -29,6 +29,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Four bf16 values as one 8-byte word.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
 // silu(z) = z * sigmoid(z) for the expert activations (tolerance-checked).
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -43,6 +48,38 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return static_cast<uint32_t>(w);
 }
+
+// Four E5M2 codes (the backward's gradient format) from fp32 values already
+// scaled into [-57344, 57344]: clamp (saturation), then the hardware
+// conversion, which rounds to nearest even.
+__device__ __forceinline__ uint32_t e5m2_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -57344.0f), 57344.0f);
+  b = fminf(fmaxf(b, -57344.0f), 57344.0f);
+  c = fminf(fmaxf(c, -57344.0f), 57344.0f);
+  d = fminf(fmaxf(d, -57344.0f), 57344.0f);
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// FP8 formats of the layer: E4M3 (forward operands, weights, activations)
+// and E5M2 (backward gradients); the largest finite value of each.
+template <int FMT>
+struct Fp8Fmt;
+template <>
+struct Fp8Fmt<0> {
+  static constexpr float kMax = 448.0f;
+  __device__ static uint32_t pack4(float a, float b, float c, float d) {
+    return e4m3_pack4(a, b, c, d);
+  }
+};
+template <>
+struct Fp8Fmt<1> {
+  static constexpr float kMax = 57344.0f;
+  __device__ static uint32_t pack4(float a, float b, float c, float d) {
+    return e5m2_pack4(a, b, c, d);
+  }
+};
 
 // Maps a physical workgroup id to a logical one so that logically adjacent
 // workgroups run on the same XCD (workgroups are dealt round-robin over the

@@ -335,7 +335,11 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   a.ws2 = w->ws2;
   a.w2_scale = w->w2_scale;
   a.ws2_scale = w->ws2_scale;
-  a.H = h_out ? h_out : at<void>(ws, L.H);
+  // training: bf16 weights keep H itself, FP8 weights its E4M3 codes in the
+  // workspace and a bf16 copy in h_out
+  const bool fp8w = d->w_dtype == MOE_DT_FP8_E4M3;
+  a.H = (h_out && !fp8w) ? h_out : at<void>(ws, L.H);
+  a.h16 = fp8w ? h_out : nullptr;
   a.H_scale = at<float>(ws, L.Hs);
   a.gu = gu_out;
   a.yperm = y_perm;
@@ -372,8 +376,10 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
 moe_status validate_train(const moe_layer_desc* d) {
   moe_status st = validate_desc(d);
   if (st) return st;
-  if (d->act_dtype != MOE_DT_BF16 || d->w_dtype != MOE_DT_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "training supports bf16 activations and weights only");
+  if (d->act_dtype != MOE_DT_BF16 ||
+      (d->w_dtype != MOE_DT_BF16 && d->w_dtype != MOE_DT_FP8_E4M3))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "training supports bf16 activations with bf16 or FP8 weights only");
   // 32-bit byte offsets of the backward's buffers
   const int64_t lim = (int64_t(1) << 31) - 1;
   const int64_t TK = d->T * d->top_k;
@@ -422,6 +428,71 @@ BwdLayout bwd_layout(const moe_layer_desc* d) {
   L.xperm = c.take(size_t(TK) * d->d * 2);
   L.bytes = c.off;
   return L;
+}
+
+// Workspace of the FP8 backward. The transposed 128x1-tile operands of the
+// weight-gradient GEMMs hold, per routed expert, its tokens padded to a
+// multiple of 128 (at most TK + 128 E in all), then the shared rows.
+struct Bwd8Layout {
+  int ldh;
+  int64_t rblocks, sblocks;  // upper bounds of the 128-row blocks: routed, shared
+  size_t tiles_h, tiles_d, qtiles, dyp, du, du_perm, dyq, dys, dysq, dyss, dg, dgq, dgs, dap,
+      das, qt_dy, qs_dy, qt_h, qs_h, qt_dg, qs_dg, qt_x, qs_x, bytes;
+};
+
+Bwd8Layout bwd8_layout(const moe_layer_desc* d) {
+  Bwd8Layout L{};
+  const int64_t T = d->T, TK = d->T * d->top_k;
+  const int E = d->n_experts, D = d->d, I = d->inter, Is = d->shared_inter;
+  L.ldh = std::max(I, Is);
+  const int64_t hrows = TK + (Is > 0 ? T : 0);
+  L.rblocks = (TK + 127) / 128 + E;
+  L.sblocks = Is > 0 ? (T + 127) / 128 : 0;
+  auto qt = [&](int64_t cr, int64_t cs) { return size_t(cr * 128 * L.rblocks + cs * 128 * L.sblocks); };
+  auto qs = [&](int64_t cr, int64_t cs) { return sizeof(float) * size_t(cr * L.rblocks + cs * L.sblocks); };
+  Carver c;
+  L.tiles_h = c.take(sizeof(int32_t) * (E + 2));
+  L.tiles_d = c.take(sizeof(int32_t) * (E + 2));
+  L.qtiles = c.take(sizeof(int32_t) * (E + 2));
+  L.dyp = c.take(size_t(TK) * D * 2);
+  L.du = c.take(sizeof(float) * size_t(TK));
+  L.du_perm = c.take(sizeof(float) * size_t(TK));
+  L.dyq = c.take(size_t(TK) * D);
+  L.dys = c.take(sizeof(float) * size_t(TK) * (D / 128));
+  L.dysq = c.take(Is > 0 ? size_t(T) * D : 0);
+  L.dyss = c.take(Is > 0 ? sizeof(float) * size_t(T) * (D / 128) : 0);
+  L.dg = c.take(size_t(hrows) * 2 * L.ldh * 2);
+  L.dgq = c.take(size_t(hrows) * 2 * L.ldh);
+  L.dgs = c.take(sizeof(float) * size_t(hrows) * (2 * L.ldh / 128));
+  L.dap = c.take(size_t(TK) * D * 2);
+  L.das = c.take(Is > 0 ? size_t(T) * D * 2 : 0);
+  L.qt_dy = c.take(qt(D, D));
+  L.qs_dy = c.take(qs(D, D));
+  L.qt_h = c.take(qt(I, Is));
+  L.qs_h = c.take(qs(I, Is));
+  L.qt_dg = c.take(qt(2 * int64_t(I), 2 * int64_t(Is)));
+  L.qs_dg = c.take(qs(2 * int64_t(I), 2 * int64_t(Is)));
+  L.qt_x = c.take(qt(D, D));
+  L.qs_x = c.take(qs(D, D));
+  L.bytes = c.off;
+  return L;
+}
+
+moe_status zero_grads(const moe_layer_desc* desc, const moe_grads* g, hipStream_t stream) {
+  const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
+  HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw13), int64_t(E) * 2 * I * d, 0, stream),
+          "zero dw13");
+  HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw2), int64_t(E) * d * I, 0, stream),
+          "zero dw2");
+  HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dw_router), int64_t(E) * d, 0, stream),
+          "zero dw_router");
+  if (Is > 0) {
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dws13), int64_t(2) * Is * d, 0, stream),
+            "zero dws13");
+    HIP_TRY(launch_fill_i32(reinterpret_cast<int32_t*>(g->dws2), int64_t(d) * Is, 0, stream),
+            "zero dws2");
+  }
+  return MOE_OK;
 }
 
 // ---- sequence-level balance loss ---------------------------------------------
@@ -889,7 +960,7 @@ moe_status moe_backward_workspace_size(const moe_layer_desc* desc, size_t* bytes
   moe_status st = validate_train(desc);
   if (st) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  *bytes = bwd_layout(desc).bytes;
+  *bytes = desc->w_dtype == MOE_DT_FP8_E4M3 ? bwd8_layout(desc).bytes : bwd_layout(desc).bytes;
   return MOE_OK;
 }
 
@@ -898,6 +969,9 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
                         const moe_grads* g, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = validate_train(desc);
   if (st) return st;
+  if (desc->w_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_backward takes bf16 weights; FP8 weights go through moe_backward_fp8");
   const int64_t T = desc->T, TK = T * desc->top_k;
   const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
   const int K = desc->top_k;
@@ -1030,6 +1104,192 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
   w2.out = g->dw2;
   w2.out_s = g->dws2;
   HIP_TRY(launch_wgrad_bf16(w2, stream), "weight gradient of the down projection");
+  return MOE_OK;
+}
+
+moe_status moe_transpose_fp8_blocks(const uint8_t* q, const float* scale, int64_t n_mats,
+                                    int32_t rows, int32_t cols, uint8_t* qt, float* scale_t,
+                                    hipStream_t stream) {
+  if (n_mats < 0 || rows < 0 || cols < 0 || rows % 128 || cols % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "rows and cols must be non-negative multiples of 128");
+  if (n_mats * (rows / 64) * int64_t(cols / 64) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  moe_status st = check_ptrs({{q, "q"}, {scale, "scale"}, {qt, "qt"}, {scale_t, "scale_t"}});
+  if (st) return st;
+  HIP_TRY(launch_transpose_fp8(q, scale, n_mats, rows, cols, qt, scale_t, stream),
+          "transpose FP8 blocks");
+  return MOE_OK;
+}
+
+moe_status moe_backward_fp8(const moe_layer_desc* desc, const void* x, const float* w_router,
+                            const moe_weights* w, const moe_weights* wt, const moe_saved* sv,
+                            const void* dy, void* dx, const moe_grads* g, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  moe_status st = validate_train(desc);
+  if (st) return st;
+  if (desc->w_dtype != MOE_DT_FP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward_fp8 takes FP8 weights (w_dtype E4M3)");
+  const int64_t T = desc->T, TK = T * desc->top_k;
+  const int E = desc->n_experts, d = desc->d, I = desc->inter, Is = desc->shared_inter;
+  const int K = desc->top_k;
+  const bool shared = Is > 0;
+  if (!g) return fail(MOE_ERR_INVALID_ARGUMENT, "grads is NULL");
+  st = check_ptrs({{g->dw13, "dw13"}, {g->dw2, "dw2"}, {g->dw_router, "dw_router"}});
+  if (st) return st;
+  if (shared) {
+    st = check_ptrs({{g->dws13, "dws13"}, {g->dws2, "dws2"}});
+    if (st) return st;
+  }
+  if (T == 0) return zero_grads(desc, g, stream);
+  st = check_ptrs({{x, "x"}, {w_router, "w_router"}, {dy, "dy"}, {dx, "dx"}, {ws, "ws"}});
+  if (st) return st;
+  st = check_weights(desc, w);
+  if (st) return st;
+  if (!wt) return fail(MOE_ERR_INVALID_ARGUMENT, "transposed weights are NULL");
+  st = check_ptrs({{wt->w13, "wt.w13"}, {wt->w2, "wt.w2"}, {wt->w13_scale, "wt.w13_scale"},
+                   {wt->w2_scale, "wt.w2_scale"}});
+  if (st) return st;
+  if (shared) {
+    st = check_ptrs({{wt->ws13, "wt.ws13"}, {wt->ws2, "wt.ws2"}, {wt->ws13_scale, "wt.ws13_scale"},
+                     {wt->ws2_scale, "wt.ws2_scale"}});
+    if (st) return st;
+  }
+  st = check_saved(desc, sv);
+  if (st) return st;
+  const Bwd8Layout L = bwd8_layout(desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_backward_fp8 needs %zu workspace bytes, got %zu",
+                L.bytes, ws_bytes);
+  const int ldh = L.ldh;
+  int32_t* tiles_h = at<int32_t>(ws, L.tiles_h);
+  int32_t* tiles_d = at<int32_t>(ws, L.tiles_d);
+  int32_t* qtiles = at<int32_t>(ws, L.qtiles);
+  void* dyp = at<void>(ws, L.dyp);
+  float* du = at<float>(ws, L.du);
+  float* du_perm = at<float>(ws, L.du_perm);
+
+  // tile tables: 128 x 256 tiles over (rows, Ig) and (rows, d); 128-row
+  // blocks per group for the weight-gradient operands
+  PlanParams pp{};
+  pp.T = T;
+  pp.E = E;
+  pp.K = K;
+  pp.d = d;
+  pp.I = I;
+  pp.Is = Is;
+  pp.bm1 = 128;
+  pp.bnh1 = 256;
+  pp.bm2 = 128;
+  pp.bn2 = 256;
+  HIP_TRY(launch_plan(nullptr, sv->offsets, nullptr, tiles_h, tiles_d, pp, stream), "plan");
+  pp.bnh1 = 1 << 30;
+  HIP_TRY(launch_plan(nullptr, sv->offsets, nullptr, qtiles, nullptr, pp, stream), "plan blocks");
+  HIP_TRY(launch_bwd_gate(dy, sv->y_perm, sv->topk_idx, sv->inv, sv->topk_gate, sv->logits, T, K,
+                          E, d, dyp, du, du_perm, stream),
+          "gate gradients");
+  // E5M2 gradients in 1x128 tiles along d for the down projection's input gradient
+  BwdFp8Args b{};
+  b.offsets = sv->offsets;
+  b.tiles_h = tiles_h;
+  b.tiles_d = tiles_d;
+  b.T = T;
+  b.TK = TK;
+  b.E = E;
+  b.d = d;
+  b.I = I;
+  b.Is = Is;
+  b.ldh = ldh;
+  b.dyq = at<uint8_t>(ws, L.dyq);
+  b.dys = at<float>(ws, L.dys);
+  b.dysq = shared ? at<uint8_t>(ws, L.dysq) : nullptr;
+  b.dyss = shared ? at<float>(ws, L.dyss) : nullptr;
+  HIP_TRY(launch_quant_rows(dyp, MOE_DT_BF16, nullptr, TK, d, at<uint8_t>(ws, L.dyq),
+                            at<float>(ws, L.dys), stream, 1),
+          "quantize gated output gradients");
+  if (shared)
+    HIP_TRY(launch_quant_rows(dy, MOE_DT_BF16, nullptr, T, d, at<uint8_t>(ws, L.dysq),
+                              at<float>(ws, L.dyss), stream, 1),
+            "quantize output gradient");
+  b.w2t = static_cast<const uint8_t*>(wt->w2);
+  b.w2t_scale = wt->w2_scale;
+  b.ws2t = static_cast<const uint8_t*>(wt->ws2);
+  b.ws2t_scale = wt->ws2_scale;
+  b.w13t = static_cast<const uint8_t*>(wt->w13);
+  b.w13t_scale = wt->w13_scale;
+  b.ws13t = static_cast<const uint8_t*>(wt->ws13);
+  b.ws13t_scale = wt->ws13_scale;
+  b.gu = static_cast<const uint16_t*>(sv->gu);
+  b.dg = at<uint16_t>(ws, L.dg);
+  b.dgq = at<uint8_t>(ws, L.dgq);
+  b.dgs = at<float>(ws, L.dgs);
+  b.dap = at<uint16_t>(ws, L.dap);
+  b.das = shared ? at<uint16_t>(ws, L.das) : nullptr;
+  HIP_TRY(launch_dgrad2_fp8(b, stream), "FP8 input gradient of the down projection");
+  HIP_TRY(launch_dgrad1_fp8(b, stream), "FP8 input gradient of the gate/up projection");
+  HIP_TRY(launch_bwd_combine(b.dap, b.das, sv->inv, sv->topk_idx, du, w_router, T, K, d, dx, stream),
+          "input gradient");
+  HIP_TRY(launch_router_wgrad(x, sv->perm, sv->offsets, du_perm, E, d, g->dw_router, stream),
+          "router weight gradient");
+  // weight-gradient operands: 128x1 tiles down each expert's token segment,
+  // written transposed (channels x tokens)
+  const int64_t max_blocks = L.rblocks + L.sblocks;
+  auto qcols = [&](const void* src, const int32_t* perm, int64_t ld, const void* src_s,
+                   int64_t ld_s, int C, int Cs, size_t qoff, size_t soff, int fmt) {
+    QuantColsArgs q{};
+    q.qtiles = qtiles;
+    q.offsets = sv->offsets;
+    q.E = E;
+    q.shared = shared;
+    q.T = T;
+    q.src = static_cast<const uint16_t*>(src);
+    q.perm = perm;
+    q.ld = ld;
+    q.src_s = static_cast<const uint16_t*>(src_s);
+    q.ld_s = ld_s;
+    q.C = C;
+    q.Cs = Cs;
+    q.q = at<uint8_t>(ws, qoff);
+    q.scale = at<float>(ws, soff);
+    return launch_quant_cols(q, max_blocks, fmt, stream);
+  };
+  const uint16_t* h16 = static_cast<const uint16_t*>(sv->h);
+  HIP_TRY(qcols(dyp, nullptr, d, dy, d, d, d, L.qt_dy, L.qs_dy, 1), "quantize dY (128x1)");
+  HIP_TRY(qcols(h16, nullptr, ldh, h16 + TK * ldh, ldh, I, Is, L.qt_h, L.qs_h, 0),
+          "quantize H (128x1)");
+  HIP_TRY(qcols(b.dg, nullptr, 2 * ldh, b.dg + TK * 2 * ldh, 2 * ldh, 2 * I, 2 * Is, L.qt_dg,
+                L.qs_dg, 1),
+          "quantize [da | db] (128x1)");
+  HIP_TRY(qcols(x, sv->perm, d, x, d, d, d, L.qt_x, L.qs_x, 0), "quantize x (128x1)");
+  WgradFp8Args w2{};
+  w2.qtiles = qtiles;
+  w2.E = E;
+  w2.shared = shared;
+  w2.a = at<uint8_t>(ws, L.qt_dy);
+  w2.as = at<float>(ws, L.qs_dy);
+  w2.b = at<uint8_t>(ws, L.qt_h);
+  w2.bs = at<float>(ws, L.qs_h);
+  w2.M = d;
+  w2.N = I;
+  w2.Ms = d;
+  w2.Ns = Is;
+  w2.out = g->dw2;
+  w2.out_s = g->dws2;
+  HIP_TRY(launch_wgrad_fp8(w2, 1, 0, stream), "FP8 weight gradient of the down projection");
+  WgradFp8Args w1{};
+  w1.qtiles = qtiles;
+  w1.E = E;
+  w1.shared = shared;
+  w1.a = at<uint8_t>(ws, L.qt_dg);
+  w1.as = at<float>(ws, L.qs_dg);
+  w1.b = at<uint8_t>(ws, L.qt_x);
+  w1.bs = at<float>(ws, L.qs_x);
+  w1.M = 2 * I;
+  w1.N = d;
+  w1.Ms = 2 * Is;
+  w1.Ns = d;
+  w1.out = g->dw13;
+  w1.out_s = g->dws13;
+  HIP_TRY(launch_wgrad_fp8(w1, 1, 0, stream), "FP8 weight gradient of the gate/up projection");
   return MOE_OK;
 }
 

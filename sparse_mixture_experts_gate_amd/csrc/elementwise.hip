@@ -111,15 +111,17 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float gam
 }
 
 // Max-abs scaling of one group (mhpq.cn §4.1, online max-abs; gkm0120.cn
-// notes Q8, 1x128 tiles / 128x128 blocks): scale = amax/448 and codes of
-// v * (448/amax); an all-zero group gets scale 1 and zero codes.
+// notes Q8, 1x128 tiles / 128x128 blocks): scale = amax/max and codes of
+// v * (max/amax), max the format's largest value (448 for E4M3, 57344 for
+// E5M2); an all-zero group gets scale 1 and zero codes.
+template <int FMT = 0>
 __device__ __forceinline__ void quant_params(float amax, float& inv, float& scale) {
   if (amax == 0.0f) {
     inv = 0.0f;
     scale = 1.0f;
   } else {
-    inv = 448.0f / amax;
-    scale = amax / 448.0f;
+    inv = Fp8Fmt<FMT>::kMax / amax;
+    scale = amax / Fp8Fmt<FMT>::kMax;
   }
 }
 
@@ -143,10 +145,11 @@ __device__ __forceinline__ void load8(const void* src, int dtype, int64_t i, flo
 }
 
 // Codes of v * inv for eight values (all zero when the group is all zero).
+template <int FMT = 0>
 __device__ __forceinline__ uint2 encode8(const float (&v)[8], float amax, float inv) {
   if (amax == 0.0f) return make_uint2(0u, 0u);
-  return make_uint2(e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
-                    e4m3_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
+  return make_uint2(Fp8Fmt<FMT>::pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                    Fp8Fmt<FMT>::pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
 }
 
 // One workgroup (256 threads) per 128x128 block: 16 lanes cover one block row
@@ -186,7 +189,8 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const void* __restric
 }
 
 // 16 lanes per 1x128 tile (8 elements each, 16-byte loads), 16 tiles per
-// workgroup; rows gathered through perm when given.
+// workgroup; rows gathered through perm when given. FMT: 0 E4M3, 1 E5M2.
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int dtype,
                                                          const int32_t* __restrict__ perm,
                                                          int64_t n, int cols,
@@ -212,8 +216,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   if (!valid) return;
   float inv, sc;
-  quant_params(amax, inv, sc);
-  *reinterpret_cast<uint2*>(q + base) = encode8(v, amax, inv);
+  quant_params<FMT>(amax, inv, sc);
+  *reinterpret_cast<uint2*>(q + base) = encode8<FMT>(v, amax, inv);
   if (l16 == 0) scale[tile] = sc;
 }
 
@@ -260,11 +264,16 @@ hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, i
 }
 
 hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm, int64_t n,
-                             int cols, uint8_t* q, float* scale, hipStream_t s) {
+                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt) {
   const int64_t tiles = n * (cols / 128);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(static_cast<unsigned>((tiles + 15) / 16)), dim3(256),
-                     0, s, src, src_dtype, perm, n, cols, q, scale);
+  const dim3 grid(static_cast<unsigned>((tiles + 15) / 16)), block(256);
+  if (fmt == 1)
+    hipLaunchKernelGGL(quant_rows_kernel<1>, grid, block, 0, s, src, src_dtype, perm, n, cols, q,
+                       scale);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<0>, grid, block, 0, s, src, src_dtype, perm, n, cols, q,
+                       scale);
   return hipGetLastError();
 }
 

@@ -348,15 +348,22 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
     // 32-row sub-tiles of this wave's band that hold data
     const int band = rows_of(tc) - wm * C::WM;
     const int nmi = band <= 0 ? 0 : band >= C::WM ? C::MI : (band + 31) / 32;
+    static_assert(C::MI <= 4, "row-skip counts 0..4");
     if (nmi >= C::MI) {
       kloop(IntC<C::MI>{});
-    } else if constexpr (C::MI > 1) {
+    } else if constexpr (C::MI == 1) {
+      kloop(IntC<0>{});
+    } else {
+      if constexpr (C::MI >= 4) {
+        if (nmi == 3) { kloop(IntC<3 % C::MI>{}); epilogue(tc, acc); continue; }
+      }
+      if constexpr (C::MI >= 3) {
+        if (nmi == 2) { kloop(IntC<2 % C::MI>{}); epilogue(tc, acc); continue; }
+      }
       if (nmi == 1)
         kloop(IntC<1>{});
       else
         kloop(IntC<0>{});
-    } else {
-      kloop(IntC<0>{});
     }
     epilogue(tc, acc);
   }
@@ -370,10 +377,6 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// Four bf16 values as one 8-byte word.
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-}
 
 }  // namespace
 }  // namespace dsmoe

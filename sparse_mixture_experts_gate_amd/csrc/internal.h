@@ -77,7 +77,8 @@ struct FfnArgs {
   const float* ws13_scale;
   void* H;                 // [TK + T, ldh]
   float* H_scale;          // fp8: [TK + T, ldh/128]
-  void* gu;                // bf16 training forward: pre-activations [TK + T, 2 ldh], or NULL
+  void* gu;                // training forward: pre-activations [TK + T, 2 ldh] bf16, or NULL
+  void* h16;               // FP8 training forward: H [TK + T, ldh] in bf16, or NULL
   // GEMM2
   const void* w2;
   const void* ws2;
@@ -149,6 +150,79 @@ hipError_t launch_dgrad2_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s);
 
+// ---- FP8 backward (backward_fp8.hip) ----------------------------------------
+// Input-gradient GEMMs on E5M2 gradients and the forward's E4M3 weights, read
+// from transposed copies (rows along the contraction).
+struct BwdFp8Args {
+  const int32_t* offsets;     // [E+1]
+  const int32_t* tiles_h;     // [E+2] 128 x 256 tiles over (rows, Ig)
+  const int32_t* tiles_d;     // [E+2] 128 x 256 tiles over (rows, d)
+  int64_t T, TK;
+  int E, d, I, Is, ldh;
+  const uint8_t* dyq;         // [TK, d] E5M2 gated output gradients, 1x128 scales dys
+  const float* dys;
+  const uint8_t* dysq;        // [T, d] E5M2 output gradient (shared rows), scales dyss
+  const float* dyss;
+  const uint8_t* w2t;         // [E, I, d] E4M3 W2^T, scales [E, I/128, d/128]
+  const float* w2t_scale;
+  const uint8_t* ws2t;        // [Is, d], scales [Is/128, d/128]
+  const float* ws2t_scale;
+  const uint8_t* w13t;        // [E, d, 2I] E4M3 [W1; W3]^T, scales [E, d/128, 2I/128]
+  const float* w13t_scale;
+  const uint8_t* ws13t;       // [d, 2Is], scales [d/128, 2Is/128]
+  const float* ws13t_scale;
+  const uint16_t* gu;         // [TK + T, 2 ldh] saved pre-activations (bf16)
+  uint16_t* dg;               // [TK + T, 2 ldh] OUT [da | db] bf16
+  uint8_t* dgq;               // [TK + T, 2 ldh] OUT [da | db] E5M2
+  float* dgs;                 // [TK + T, 2 ldh / 128] OUT its 1x128 scales
+  uint16_t* dap;              // [TK, d] OUT input gradients of the routed rows
+  uint16_t* das;              // [T, d] OUT the shared expert's
+};
+// Weight gradients out_g = A_g B_g^T from transposed 128x1-tile codes; qtiles
+// [E+2] is the 128-row block prefix of the groups (routed, then shared).
+struct WgradFp8Args {
+  const int32_t* qtiles;
+  int E;
+  bool shared;
+  const uint8_t* a;
+  const float* as;
+  const uint8_t* b;
+  const float* bs;
+  int M, N, Ms, Ns;
+  float* out;                 // [E, M, N]
+  float* out_s;               // [Ms, Ns]
+};
+// 128x1 quantization along each group's rows into the transposed layout:
+// group g's C channels x npad_g tokens at byte C * 128 * qtiles[g] (the
+// shared group after the routed ones, with Cs channels), scales
+// [C, npad_g / 128] at float C * qtiles[g]. Routed rows: rows offsets[g] ..
+// of src (row stride ld), or of src through perm; shared rows: rows of src_s.
+struct QuantColsArgs {
+  const int32_t* qtiles;
+  const int32_t* offsets;
+  int E;
+  bool shared;
+  int64_t T;
+  const uint16_t* src;
+  const int32_t* perm;
+  int64_t ld;
+  const uint16_t* src_s;
+  int64_t ld_s;
+  int C, Cs;
+  uint8_t* q;
+  float* scale;
+};
+hipError_t launch_dgrad2_fp8(const BwdFp8Args& a, hipStream_t s);
+hipError_t launch_dgrad1_fp8(const BwdFp8Args& a, hipStream_t s);
+// fa / fb: formats of A and B (0 = E4M3, 1 = E5M2); E5M2 x E4M3 only
+hipError_t launch_wgrad_fp8(const WgradFp8Args& w, int fa, int fb, hipStream_t s);
+// max_blocks: an upper bound of the groups' 128-row blocks (grid size)
+hipError_t launch_quant_cols(const QuantColsArgs& q, int64_t max_blocks, int fmt, hipStream_t s);
+// codes [n, rows, cols] -> [n, cols, rows]; block scales [n, rows/128, cols/128]
+// -> [n, cols/128, rows/128]
+hipError_t launch_transpose_fp8(const uint8_t* q, const float* scale, int64_t n_mats, int rows,
+                                int cols, uint8_t* qt, float* scale_t, hipStream_t s);
+
 // balance.hip: the sequence-level balance loss. part_p / part_c hold
 // [n_seq * ceil(L / kBalanceChunk), E] partial sums, f - 1 [n_seq, E]; du16 [T, ldE] and
 // duT16 [E, ldT] are bf16 copies of dloss/du (ldE, ldT multiples of 8).
@@ -172,9 +246,10 @@ hipError_t launch_bias_update(const int32_t* counts, float gamma, float* bias, i
                               int64_t T, int K, hipStream_t s);
 hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, int rows,
                                int cols, uint8_t* q, float* scale, hipStream_t s);
-// Row i of the output quantizes source row perm[i] (perm == NULL: row i).
+// Row i of the output quantizes source row perm[i] (perm == NULL: row i);
+// fmt 0 = E4M3, 1 = E5M2.
 hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm, int64_t n,
-                             int cols, uint8_t* q, float* scale, hipStream_t s);
+                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt = 0);
 
 // number of compute units of the current device (cached per device)
 int device_cu_count();

@@ -12,6 +12,7 @@
 
 namespace {
 
+using dsmoe::dma16;
 using dsmoe::dma16_nt;
 using dsmoe::i32x4_t;
 using dsmoe::lds_addr;
@@ -19,10 +20,12 @@ using dsmoe::rsrc4;
 using dsmoe::vm_wait;
 
 // The layer's load path: 16-byte buffer loads straight into LDS (one 1 KB
-// piece per wave and instruction, non-temporal like the decode GEMMs' weight
-// loads), each wave cycling over 8 slots of its own 8 KB LDS ring, at most 24
-// loads in flight; workgroup b reads pieces b, b + nb, ... of the buffer
-// (bytes < 2^31). Five workgroups per CU fill its LDS and read fastest.
+// piece per wave and instruction; NT: non-temporal like the decode GEMMs'
+// weight loads, else the default policy of the prefill GEMMs), each wave
+// cycling over 8 slots of its own 8 KB LDS ring, at most 24 loads in flight;
+// workgroup b reads pieces b, b + nb, ... of the buffer (bytes < 2^31). Five
+// workgroups per CU fill its LDS and read fastest.
+template <bool NT>
 __global__ __launch_bounds__(256) void hbm_dma_kernel(const void* src, uint32_t bytes) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][8][1024];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -34,8 +37,11 @@ __global__ __launch_bounds__(256) void hbm_dma_kernel(const void* src, uint32_t 
   for (; p + 7 * nw < pieces; p += 8 * nw) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      dma16_nt(r, (p + u * nw) * 1024u + lane * 16u,
-            __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][slot][0])));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][slot][0]));
+      if constexpr (NT)
+        dma16_nt(r, (p + u * nw) * 1024u + lane * 16u, dst);
+      else
+        dma16(r, (p + u * nw) * 1024u + lane * 16u, dst);
       slot = (slot + 1) & 7;
     }
     vm_wait<16>();
@@ -51,6 +57,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // non-temporal) and folds them into one word, written out so that no load is
 // dead.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4_t* __restrict__ src,
                                                        int64_t n16, uint32_t* __restrict__ sink) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -59,7 +66,8 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4_t* __restrict
   for (; i + 7 * stride < n16; i += 8 * stride) {
     u32x4_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+    for (int u = 0; u < 8; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(&src[i + u * stride]) : src[i + u * stride];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
@@ -116,8 +124,14 @@ __global__ __launch_bounds__(256) void mfma_fp8_kernel(int iters, float* __restr
 extern "C" {
 
 // The same over the LDS-DMA load path; bytes a multiple of 1 KB, < 2^31.
+// Non-temporal loads; dsmoe_mb_hbm_dma_default: the default cache policy.
 int dsmoe_mb_hbm_dma(const void* src, int64_t bytes, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL(hbm_dma_kernel, dim3(blocks), dim3(256), 0, s, src,
+  hipLaunchKernelGGL(hbm_dma_kernel<true>, dim3(blocks), dim3(256), 0, s, src,
+                     static_cast<uint32_t>(bytes));
+  return hipGetLastError();
+}
+int dsmoe_mb_hbm_dma_default(const void* src, int64_t bytes, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(hbm_dma_kernel<false>, dim3(blocks), dim3(256), 0, s, src,
                      static_cast<uint32_t>(bytes));
   return hipGetLastError();
 }
@@ -125,7 +139,14 @@ int dsmoe_mb_hbm_dma(const void* src, int64_t bytes, int blocks, hipStream_t s) 
 // Reads `bytes` (a multiple of 16) from src with `blocks` workgroups of 256
 // threads; sink holds blocks * 256 words. Returns a hipError_t.
 int dsmoe_mb_hbm_read(const void* src, int64_t bytes, int blocks, void* sink, hipStream_t s) {
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const u32x4_t*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  return hipGetLastError();
+}
+// The same with the default cache policy.
+int dsmoe_mb_hbm_read_default(const void* src, int64_t bytes, int blocks, void* sink,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(blocks), dim3(256), 0, s,
                      static_cast<const u32x4_t*>(src), bytes / 16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
 }

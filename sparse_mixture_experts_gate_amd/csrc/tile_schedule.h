@@ -84,12 +84,14 @@ constexpr uint32_t kInvalidRow = 0x80000000u;
 // Raw buffer descriptor as four scalar words: base address, no stride,
 // `bytes` records (range-checked: offsets at or beyond it read as zeros).
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// The words are read through readfirstlane: every caller builds a
+// wave-uniform descriptor, and the loads take it in scalar registers.
 __device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   i32x4_t r;
-  r[0] = static_cast<int>(static_cast<uint32_t>(b));
-  r[1] = static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu);
-  r[2] = static_cast<int>(bytes);
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
   r[3] = 0x00020000;
   return r;
 }

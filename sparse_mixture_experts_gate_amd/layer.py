@@ -124,15 +124,44 @@ class MoELayer:
             self._bws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._bws
 
+    def weights_transposed(self) -> L.MoeWeights:
+        """Transposed copies of the FP8 weights (codes and block scales) that
+        the FP8 backward reads, made once by the library."""
+        if getattr(self, "_wt", None) is None:
+            wl, dev, u8, f32 = self.wl, self.device, torch.uint8, torch.float32
+
+            def tr(q, sc):
+                lead = q.shape[:-2]
+                qt = torch.empty(*lead, q.shape[-1], q.shape[-2], dtype=u8, device=dev)
+                st = torch.empty(*lead, sc.shape[-1], sc.shape[-2], dtype=f32, device=dev)
+                L.moe_transpose_fp8_blocks(q, sc, qt, st)
+                return qt, st
+
+            w13t, s13t = tr(self.w13, self.w13_scale)
+            w2t, s2t = tr(self.w2, self.w2_scale)
+            ws13t = ws2t = ss13t = ss2t = None
+            if wl.Is:
+                ws13t, ss13t = tr(self.ws13, self.ws13_scale)
+                ws2t, ss2t = tr(self.ws2, self.ws2_scale)
+            self._wt_tensors = (w13t, w2t, ws13t, ws2t, s13t, s2t, ss13t, ss2t)
+            self._wt = L.make_weights(*self._wt_tensors)
+        return self._wt
+
     def backward(self, x: torch.Tensor, dy: torch.Tensor, saved: dict, grads: dict | None = None,
                  stream=None) -> tuple:
-        """dx [T, d] bf16 and the fp32 weight gradients (moe_backward)."""
+        """dx [T, d] bf16 and the fp32 weight gradients (moe_backward, or
+        moe_backward_fp8 for FP8 weights)."""
         T = x.shape[0]
         grads = self.alloc_grads() if grads is None else grads
         dx = torch.empty(T, self.wl.d, dtype=torch.bfloat16, device=self.device)
-        L.moe_backward(self.desc(T), x, self.w_router, self.weights,
-                       L.make_saved(**saved), dy, dx, L.make_grads(**grads),
-                       self.backward_workspace(T), stream)
+        if self.wl.w == "fp8":
+            L.moe_backward_fp8(self.desc(T), x, self.w_router, self.weights,
+                               self.weights_transposed(), L.make_saved(**saved), dy, dx,
+                               L.make_grads(**grads), self.backward_workspace(T), stream)
+        else:
+            L.moe_backward(self.desc(T), x, self.w_router, self.weights,
+                           L.make_saved(**saved), dy, dx, L.make_grads(**grads),
+                           self.backward_workspace(T), stream)
         return dx, grads
 
     def seq_balance_loss(self, x: torch.Tensor, saved: dict, seq_len: int, alpha: float,

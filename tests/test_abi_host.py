@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(L):
         "moe_quantize_fp8_blocks", "moe_quantize_fp8_rows", "moe_status_string",
         "moe_last_error", "moe_abi_version", "moe_profile_events", "moe_forward_train",
         "moe_backward_workspace_size", "moe_backward", "moe_seq_balance_workspace_size",
-        "moe_seq_balance_loss", "deepseek_moe_forward_noalloc"}
+        "moe_seq_balance_loss", "deepseek_moe_forward_noalloc", "moe_transpose_fp8_blocks",
+        "moe_backward_fp8"}
     so = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(so, n), n
@@ -145,9 +146,10 @@ def test_training_entry_points_validate_before_launch(L):
     assert b"2*max(I,Is)*d*4" in lib.moe_last_error()
     big = _desc(L, inter=128, shared_inter=(1 << 20) - 128)
     assert lib.moe_backward_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
-    # fp32 and fp8 layers have no training path
-    for kw in (dict(act_dtype=0, w_dtype=0), dict(w_dtype=2)):
-        assert lib.moe_backward_workspace_size(ctypes.byref(_desc(L, **kw)), ctypes.byref(n)) == 2
+    # fp32 layers have no training path; FP8 layers train through moe_backward_fp8
+    assert lib.moe_backward_workspace_size(ctypes.byref(_desc(L, act_dtype=0, w_dtype=0)),
+                                           ctypes.byref(n)) == 2
+    assert lib.moe_backward_workspace_size(ctypes.byref(_desc(L, w_dtype=2)), ctypes.byref(n)) == 0
     w = L.MoeWeights(4096, 4096, 4096, 4096, None, None, None, None)
     sv = L.MoeSaved(*([4096] * 10))
     # forward_train: NULL saved, then a misaligned saved tensor

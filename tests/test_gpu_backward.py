@@ -158,11 +158,15 @@ def test_backward_single_token_and_zero_tokens():
 def test_backward_v3_sampled():
     """The V3 prefill layer (T = 8192, d = 7168, 256 experts in 8 groups,
     K = 8, I = Is = 2048) in the launch configuration the benchmark times;
-    the oracle computes sampled outputs one by one: the input gradient of 256
-    seeded tokens (each needs only its own experts), the weight gradients of
-    eight experts from the hottest to the coldest (all their tokens), the
-    router-weight gradients of a cold and a median expert, and full rows of
-    the shared expert's gradients."""
+    the oracle computes sampled outputs one by one:
+      - the input gradient of 256 seeded tokens whose experts all lie among
+        the 32 most loaded ones, plus one token of each of the 8 least loaded
+        experts (a token's input gradient needs only its own experts);
+      - the weight gradients of eight experts from the hottest to the
+        coldest (all their tokens);
+      - the router-weight gradients of the two least loaded experts (every
+        token routed to them, with all of those tokens' experts);
+      - full rows of the shared expert's gradients."""
     wl = CONFIGS["v3_prefill_bf16"]
     _log("backward V3 sampled: running the layer")
     P, layer, y, sv, dy, dx, gr = _run(wl)
@@ -174,22 +178,24 @@ def test_backward_v3_sampled():
     w13, w2 = LazyHost(P["w13"], "expert"), LazyHost(P["w2"])
     ws13, ws2 = host(P["ws13"]), host(P["ws2"])
     tol = TOL["bf16"]
-    # input gradient of 256 seeded tokens: one oracle call over those tokens
-    # (a token's input gradient needs only its own experts and its own dy)
+    counts = host(sv["counts"])
+    by_load = np.argsort(-counts, kind="stable")
+    used = by_load[counts[by_load] > 0]
     rng = np.random.default_rng(5)
-    toks = np.sort(rng.choice(wl.T, size=256, replace=False))
-    _log(f"  oracle: input gradients of {len(toks)} tokens on {WORKERS} threads")
+    inside = np.nonzero(np.isin(idx, by_load[:32]).all(axis=1))[0]
+    hot = rng.choice(inside, size=min(256, len(inside)), replace=False)
+    cold = [int(np.nonzero((idx == e).any(axis=1))[0][0]) for e in used[::-1][:8]]
+    toks = np.unique(np.concatenate([hot, cold]))
+    assert len(toks) >= 256
+    _log(f"  oracle: input gradients of {len(toks)} tokens ({len(np.unique(idx[toks]))} experts)")
     ref = O.layer_backward(x[toks], wr, logits[toks], idx[toks], w13, w2, ws13, ws2, dyh[toks],
                            experts=(), workers=WORKERS)
     e = row_rel_err(host(dx)[toks], ref.dx)
-    _log(f"  dx of {len(toks)} tokens ({len(np.unique(idx[toks]))} experts): {e:.2e}")
+    _log(f"  dx of {len(toks)} tokens: {e:.2e}")
     assert e <= tol
     # weight gradients of eight experts spread over the loads, hottest and
     # coldest included (every token routed to each)
-    counts = host(sv["counts"])
-    order = np.argsort(counts, kind="stable")
-    order = order[counts[order] > 0]
-    pick = sorted(set(int(order[int(round(q * (len(order) - 1)))])
+    pick = sorted(set(int(used[::-1][int(round(q * (len(used) - 1)))])
                       for q in (0.0, 0.02, 0.1, 0.3, 0.5, 0.7, 0.9, 1.0)))
     assert len(pick) >= 8
     s_sel = 1.0 / (1.0 + np.exp(-np.take_along_axis(logits.astype(np.float64), idx, 1)))
@@ -207,9 +213,11 @@ def test_backward_v3_sampled():
     for e, n, e13, e2 in res:
         _log(f"  expert {e} ({n} tokens): dw13 {e13:.2e} dw2 {e2:.2e}")
         assert e13 <= tol and e2 <= tol
-    # router-weight gradients of a cold and a median expert: every token routed
-    # to it, with all of that token's experts (the gates' normalisation couples them)
-    for e in (pick[0], pick[len(pick) // 2]):
+    # router-weight gradients of the two least loaded experts: every token
+    # routed to it, with all of that token's experts (the gates' normalisation
+    # couples them)
+    for e in used[::-1][:2]:
+        e = int(e)
         rows = np.nonzero((idx == e).any(axis=1))[0]
         ref = O.layer_backward(x[rows], wr, logits[rows], idx[rows], w13, w2, None, None,
                                dyh[rows], experts=(), workers=WORKERS)

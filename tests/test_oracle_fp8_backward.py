@@ -75,9 +75,11 @@ def test_tile_quantizers_shapes_scales_and_bounds():
 
 def _exact_codecs(monkeypatch):
     """Every quantizer of the FP8 path made exact: codes are the values
-    themselves, scales 1 (an FP8 format with unlimited precision)."""
+    themselves, scales 1 (an FP8 format with unlimited precision), and the
+    bf16 storage of the intermediates exact too."""
     ident = lambda X, fmt=None: (np.asarray(X, np.float64), np.ones(1))
     deq = lambda q, s, fmt=None: np.asarray(q, np.float64)
+    monkeypatch.setattr(FB, "round_bf16", lambda v: np.asarray(v, np.float64))
     monkeypatch.setattr(FB, "quantize_1x128", ident)
     monkeypatch.setattr(FB, "dequant_1x128", deq)
     monkeypatch.setattr(FB, "quantize_128x1", ident)
@@ -153,7 +155,8 @@ def test_formats_and_axes_per_operand(monkeypatch):
     along its GEMM's contraction axis: dY (n x d) and [da | db] (n x 2I) in
     1x128 tiles along their rows for the input-gradient GEMMs and in 128x1
     tiles down their columns for the weight-gradient GEMMs, H (n x I) and X
-    (n x d) in 128x1 tiles for the weight-gradient GEMMs."""
+    (n x d) in 128x1 tiles for the weight-gradient GEMMs; the quantizers read
+    the bf16 copies the layer keeps of a, b, H and [da | db]."""
     calls = []
     q1, q128 = FB.quantize_1x128, FB.quantize_128x1
     monkeypatch.setattr(FB, "quantize_1x128",
@@ -165,7 +168,14 @@ def test_formats_and_axes_per_operand(monkeypatch):
     X = rng.normal(size=(n, d)).astype(F32)
     w13q, w13s = O.quantize_blocks_128(rng.normal(0, 0.05, (2 * inter, d)).astype(F32))
     w2q, w2s = O.quantize_blocks_128(rng.normal(0, 0.05, (d, inter)).astype(F32))
+    rounded = []
+    rb = FB.round_bf16
+    monkeypatch.setattr(FB, "round_bf16",
+                        lambda v: (rounded.append(np.shape(v)), rb(v))[1])
     FB.fp8_expert_backward(X, w13q, w13s, w2q, w2s, rng.normal(size=(n, d)))
+    # bf16 copies the layer keeps: a, b, H (saved by the training forward)
+    # and [da | db] (the weight-gradient operand)
+    assert sorted(rounded) == sorted([(n, inter), (n, inter), (n, inter), (n, 2 * inter)])
     assert sorted(calls) == sorted([
         ("1x128", "e5m2", (n, d)), ("1x128", "e5m2", (n, 2 * inter)),
         ("128x1", "e5m2", (n, d)), ("128x1", "e4m3", (n, inter)),
