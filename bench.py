@@ -201,6 +201,47 @@ def cpu_baseline(wl, P, n_tokens: int, x=None) -> dict:
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+# Known-byte reads for counter calibration (bench.py --calibrate-loads), one
+# per load path of the library's kernels: buffer loads straight into LDS with
+# the default and the non-temporal policy (dsmoe_mb_hbm_dma[_default], 1280
+# workgroups x 4 waves x 1 KB pieces, a whole number of 8-piece rounds per
+# wave, so every byte is read exactly once), and 16-byte register loads with
+# both policies (dsmoe_mb_hbm_read[_default], grid-stride, every byte once).
+# Kernel-name substring -> bytes read per launch.
+DMA_BLOCKS = 1280
+DMA_BYTES = ((2 ** 31 - 1) // (8 * DMA_BLOCKS * 4 * 1024)) * 8 * DMA_BLOCKS * 4 * 1024
+READ_BYTES = 1 << 30
+LOAD_CALIBRATION = {"hbm_dma_kernel<false>": DMA_BYTES, "hbm_dma_kernel<true>": DMA_BYTES,
+                    "hbm_read_kernel<false>": READ_BYTES, "hbm_read_kernel<true>": READ_BYTES}
+
+
+def calibrate_loads() -> None:
+    """Three launches of each calibration read (LOAD_CALIBRATION), for the
+    counters of a profiled run; nothing is timed."""
+    import ctypes
+    import torch
+    mb = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_gate_amd",
+                                  "libdsmoe_microbench.so"))
+    for f in (mb.dsmoe_mb_hbm_dma, mb.dsmoe_mb_hbm_dma_default):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    for f in (mb.dsmoe_mb_hbm_read, mb.dsmoe_mb_hbm_read_default):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                      ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.ones(max(DMA_BYTES, READ_BYTES), dtype=torch.uint8, device="cuda")
+    blocks = 8192
+    sink = torch.empty(blocks * 256 * 4, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        for f in (mb.dsmoe_mb_hbm_dma_default, mb.dsmoe_mb_hbm_dma):
+            if f(buf.data_ptr(), DMA_BYTES, DMA_BLOCKS, stream) != 0:
+                raise RuntimeError("calibration launch failed")
+        for f in (mb.dsmoe_mb_hbm_read_default, mb.dsmoe_mb_hbm_read):
+            if f(buf.data_ptr(), READ_BYTES, blocks, sink.data_ptr(), stream) != 0:
+                raise RuntimeError("calibration launch failed")
+    torch.cuda.synchronize()
+    del buf, sink
+
+
 def achievable_peaks() -> dict:
     """Microbenchmarked peaks of this GPU (libdsmoe_microbench.so, hand-written
     HIP kernels): streaming reads far beyond the 256 MB Infinity Cache, once
@@ -451,6 +492,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times, so that HBM byte "
                          "counters can be scaled against a kernel of known traffic")
+    ap.add_argument("--calibrate-loads", action="store_true",
+                    help="also read known byte counts through each load path of the kernels "
+                         "(LDS-DMA and register loads, default and non-temporal policy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-loop", action="store_true",
@@ -477,6 +521,8 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.calibrate_loads:
+        calibrate_loads()
     log(f"generating {wl.name} inputs")
     P = make_inputs(wl, dev)
     layer = M.MoELayer(wl, P)
