@@ -246,7 +246,8 @@ def achievable_peaks() -> dict:
     """Microbenchmarked peaks of this GPU (libdsmoe_microbench.so, hand-written
     HIP kernels): streaming reads far beyond the 256 MB Infinity Cache, once
     into registers (4 GiB) and once over the layer's own LDS-DMA load path
-    (2 GiB), and back-to-back independent MFMAs with operands in registers,
+    (2 GiB), streaming writes of 4 GiB (4- and 16-byte stores, default and
+    non-temporal), and back-to-back independent MFMAs with operands in registers,
     bf16 32x32x16 and FP8 32x32x64. Each is the best of 3 timed launches
     after a warm-up launch."""
     import ctypes
@@ -283,8 +284,15 @@ def achievable_peaks() -> dict:
                                                stream))
     dma_bytes = (2 << 30) - 1024
     t_dma = best(lambda: mb.dsmoe_mb_hbm_dma(buf.data_ptr(), dma_bytes, cus * 5, stream))
-    del buf
     res = {"hbm_read_GBps": nbytes / t_read / 1e9, "hbm_dma_GBps": dma_bytes / t_dma / 1e9}
+    # writes: 4-byte and 16-byte stores, default and non-temporal policy
+    mb.dsmoe_mb_hbm_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    for mode, key in ((0, "hbm_write_b32_GBps"), (1, "hbm_write_b32_nt_GBps"),
+                      (2, "hbm_write_b128_GBps"), (3, "hbm_write_b128_nt_GBps")):
+        t = best(lambda: mb.dsmoe_mb_hbm_write(buf.data_ptr(), nbytes, blocks, mode, stream))
+        res[key] = nbytes / t / 1e9
+    del buf
     for name, fp8, iters, flops in (("mfma_bf16_TFLOPs", 0, 20000, 32768.0),
                                     ("mfma_fp8_TFLOPs", 1, 10000, 131072.0)):
         t = best(lambda: mb.dsmoe_mb_mfma(fp8, iters, blocks, sink.data_ptr(), stream))

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
 // 128 with zeros), scales [rows, npad_g / 128]. Groups: the E routed
 // experts, then the shared expert (its own M, N). A group with no token
 // reads one block of zeros and stores exact zeros. Tiles: 128 x 256 of the
-// output, m fastest inside a group; out fp32, row-major [M, N].
+// output, n fastest inside a group; out fp32, row-major [M, N].
 template <class C, int FA, int FB>
 __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
@@ -325,22 +325,24 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
   };
   auto coord = [&](int tile) {
     Coord c;
-    int ntm, rem;
+    int ntn, rem;
     if (tile < w.E * tpg) {
       c.g = tile / tpg;
       rem = tile - c.g * tpg;
       c.M = w.M;
       c.N = w.N;
-      ntm = tm;
+      ntn = tn;
     } else {
       c.g = w.E;
       rem = tile - w.E * tpg;
       c.M = w.Ms;
       c.N = w.Ns;
-      ntm = tms;
+      ntn = tns;
     }
-    c.nt = rem / ntm;
-    c.mt = rem - c.nt * ntm;
+    // n fastest: the tiles one XCD runs together write adjacent pieces of the
+    // same output rows
+    c.mt = rem / ntn;
+    c.nt = rem - c.mt * ntn;
     c.q0 = __builtin_amdgcn_readfirstlane(sq[c.g]);
     c.mtg = __builtin_amdgcn_readfirstlane(sq[c.g + 1]) - c.q0;
     return c;
@@ -387,28 +389,41 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
     const Coord c = coord(tile);
     return c.mtg > 0 ? c.mtg : 1;
   };
+  // acc in the A-first layout: lane l owns output column l % 32 of each 32 x 32
+  // product and rows 8 g + 4 (l / 32) + q, so one register across the wave
+  // stores two 128-byte row pieces. Buffer stores with out-of-range offsets
+  // for the masked entries: every call issues exactly MI * NJ * 16 stores (no
+  // branch skips one), which lets them drain during the next tile's first k
+  // block.
   auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const Coord c = coord(tile);
     float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        out, 0, static_cast<int>(static_cast<uint32_t>(c.M) * c.N * 4u), 0x00020000);
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-      const int m = c.mt * C::BM + wm * C::WM + mi * 32 + (lane & 31);
-      if (m >= c.M) continue;
-      float* op = out + static_cast<int64_t>(m) * c.N;
+    for (int nj = 0; nj < C::NJ; ++nj) {
+      const int n = c.nt * C::BN + wn * C::WN + nj * 32 + (lane & 31);
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj)
+      for (int mi = 0; mi < C::MI; ++mi) {
+        const int m0 = c.mt * C::BM + wm * C::WM + mi * 32 + 4 * (lane >> 5);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = c.nt * C::BN + wn * C::WN + nj * 32 + 8 * g + 4 * (lane >> 5);
-          if (n >= c.N) continue;
-          const f32x16_t& v = acc[mi][nj];
-          *reinterpret_cast<float4*>(op + n) =
-              make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 8 * (r >> 2) + (r & 3);
+          const uint32_t off = (m < c.M && n < c.N)
+                                   ? (static_cast<uint32_t>(m) * c.N + n) * 4u
+                                   : kInvalidRow;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0, 0);
         }
+      }
     }
   };
+  constexpr int kStores = C::MI * C::NJ * 16;
+  constexpr int kIn = C::template NL<true> * (C::NST - 2);
+  constexpr int kPost = kIn + kStores < 63 ? kIn + kStores : 63;
+  static_assert(kPost <= kStores + kIn, "the waits after an epilogue stay exact");
   gemm8_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, FB, FA,
-               true>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
+               true, false, kPost>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of,
+                                   epilogue);
 }
 
 // ---- 128x1 quantization along the tokens, written transposed ----------------

@@ -154,10 +154,15 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
 // FW / FA: formats of the B (weight-side, first MFMA operand) and A codes,
 // 0 = E4M3, 1 = E5M2. SBROW: B carries one scale per row and k block instead
 // of a block scale, so each of a lane's 16 values gets its own scale product.
-template <class C, bool SWIGLU, int FW, int FA, bool SBROW, class Mid>
+// SWAP = false (SBROW only) puts the A fragment first instead: lane l then
+// owns B row (output column) l % 32 and the 16 A rows 8 g + 4 (l / 32) + q of
+// each 32-row group, so that one accumulator register across the wave is two
+// 128-byte output row pieces (full cache lines for fp32 outputs).
+template <class C, bool SWIGLU, int FW, int FA, bool SBROW, bool SWAP, class Mid>
 __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_sa,
                                            const float* lds_sb, int st, int wave, int wm, int wn,
                                            int lane, f32x16_t (&acc)[C::MI][C::NJ], Mid&& mid) {
+  static_assert(SWAP || SBROW, "the A-first order is built for row scales on both sides");
   const uint8_t* As = lds + st * C::STAGE;
   const uint8_t* Bs = As + C::BM * BK8;
   const float s_lo = SBROW ? 1.0f : lds_sb[(st * C::NWAVES + wave) * 2];
@@ -165,28 +170,39 @@ __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_
   const int rl = lane & 31;
   const int ch = 2 * (lane >> 5);  // first chunk of the lane's 32-byte k group
   float sl[C::MI], sh[C::MI];
+  if constexpr (SWAP) {
 #pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) {
-    const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 32 + rl];
-    sl[mi] = sa * s_lo;
-    sh[mi] = sa * s_hi;
+    for (int mi = 0; mi < C::MI; ++mi) {
+      const float sa = lds_sa[st * C::NT + wm * C::WM + mi * 32 + rl];
+      sl[mi] = sa * s_lo;
+      sh[mi] = sa * s_hi;
+    }
   }
-  // SBROW: the scales of the lane's 16 B rows (columns 8 g + 4 (lane / 32) + q
-  // of each 32-row B group), read now: after mid()'s barrier the stage's
-  // scale slots may already be refilled for a later k block
-  float sbv[SBROW ? C::NJ : 1][16];
+  // SBROW: the scales of the lane's 16 rows on the register side (B rows
+  // with SWAP, A rows without) and of its one row on the lane side, read
+  // now: after mid()'s barrier the stage's scale slots may already be
+  // refilled for a later k block
+  constexpr int NR = SWAP ? C::NJ : C::MI;
+  float sbv[SBROW ? NR : 1][16];
+  float slane[SWAP ? 1 : C::NJ];
   if constexpr (SBROW) {
 #pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj) {
-      const float* sb = lds_sb + st * C::NT + b_row8<C, SWIGLU>(wn, nj) + 4 * (lane >> 5);
+    for (int i = 0; i < NR; ++i) {
+      const float* sr = SWAP ? lds_sb + st * C::NT + b_row8<C, SWIGLU>(wn, i) + 4 * (lane >> 5)
+                             : lds_sa + st * C::NT + wm * C::WM + i * 32 + 4 * (lane >> 5);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 s4 = *reinterpret_cast<const float4*>(sb + 8 * g);
-        sbv[nj][4 * g] = s4.x;
-        sbv[nj][4 * g + 1] = s4.y;
-        sbv[nj][4 * g + 2] = s4.z;
-        sbv[nj][4 * g + 3] = s4.w;
+        const float4 s4 = *reinterpret_cast<const float4*>(sr + 8 * g);
+        sbv[i][4 * g] = s4.x;
+        sbv[i][4 * g + 1] = s4.y;
+        sbv[i][4 * g + 2] = s4.z;
+        sbv[i][4 * g + 3] = s4.w;
       }
+    }
+    if constexpr (!SWAP) {
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+        slane[nj] = lds_sb[st * C::NT + b_row8<C, SWIGLU>(wn, nj) + rl];
     }
   }
   i32x8_t bfr[C::NJ][2];
@@ -204,10 +220,14 @@ __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_
   af[0][1] = a_frag(0, 1);
   auto fold = [&](int u) {
     const int pm = u / C::NJ, pn = u % C::NJ;
-    if constexpr (SBROW) {
+    if constexpr (SBROW && SWAP) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         acc[pm][pn][r] = __builtin_fmaf(p[u & 1][r], sl[pm] * sbv[pn][r], acc[pm][pn][r]);
+    } else if constexpr (SBROW) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[pm][pn][r] = __builtin_fmaf(p[u & 1][r], sbv[pm][r] * slane[pn], acc[pm][pn][r]);
     } else {
       const float s = (!SWIGLU || pn < C::NJ / 2) ? sl[pm] : sh[pm];
 #pragma unroll
@@ -223,10 +243,17 @@ __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_
       __builtin_amdgcn_sched_barrier(0);
     }
     const f32x16_t zero = {};
-    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][0], af[mi & 1][0], zero, FW,
-                                                               FA, 0, 127, 0, 127);
-    p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][1], af[mi & 1][1],
-                                                               p[t & 1], FW, FA, 0, 127, 0, 127);
+    if constexpr (SWAP) {
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][0], af[mi & 1][0], zero,
+                                                                 FW, FA, 0, 127, 0, 127);
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[nj][1], af[mi & 1][1],
+                                                                 p[t & 1], FW, FA, 0, 127, 0, 127);
+    } else {
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi & 1][0], bfr[nj][0], zero,
+                                                                 FA, FW, 0, 127, 0, 127);
+      p[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi & 1][1], bfr[nj][1],
+                                                                 p[t & 1], FA, FW, 0, 127, 0, 127);
+    }
     if (nj == 0 && mi + 1 < C::MI) {
       af[(mi + 1) & 1][0] = a_frag(mi + 1, 0);
       af[(mi + 1) & 1][1] = a_frag(mi + 1, 1);
@@ -252,8 +279,16 @@ __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_
 // stages nobody reads), so with loads NST - 1 blocks ahead at most the newest
 // NL * (NST - 2) may be in flight when a stage is read; extra loads or stores
 // in between only make such a wait stronger.
+// POST >= 0 lets the epilogue's stores drain during the next tile's first
+// two k blocks: the next tile's first loads are issued before the epilogue
+// (into the stage the last block has just freed), so the stages both of
+// those blocks wait for were loaded before the stores, and their waits
+// allow POST operations in flight instead. With NST = 3, one k block's loads
+// and the epilogue's stores follow each of those stages, so that is exact
+// only if every epilogue call issues at least POST - NL vector-memory
+// instructions. SWAP: operand order of the MFMAs (stage8_mma).
 template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, int FW = 0, int FA = 0,
-          bool SBROW = false>
+          bool SBROW = false, bool SWAP = true, int POST = -1>
 __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float* lds_sb, int first,
                                              int nb, int total, NextOps&& next_ops, NkOf&& nk_of,
                                              Epilogue&& epilogue) {
@@ -263,6 +298,7 @@ __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float*
   constexpr int NST = C::NST;
   constexpr int INFLIGHT = C::template NL<SBROW> * (NST - 2);
   const uint32_t lds0 = lds_addr(lds), sa0 = lds_addr(lds_sa), sb0 = lds_addr(lds_sb);
+  static_assert(POST < 0 || NST == 3, "the early issue before an epilogue assumes three stages");
 
   // issue side
   StreamOps8<C> op;
@@ -296,8 +332,17 @@ __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float*
   int st = 0, st_issue = NST - 1;
   // this wave's part of the next stage has landed; the barrier makes every
   // wave's part visible and frees the stage being read
+  bool after_epilogue = false;
   auto mid = [&]() {
-    vm_wait<INFLIGHT>();
+    if constexpr (POST >= 0) {
+      static_assert(POST >= INFLIGHT && POST <= 63, "vmcnt range");
+      if (after_epilogue)
+        vm_wait<POST>();
+      else
+        vm_wait<INFLIGHT>();
+    } else {
+      vm_wait<INFLIGHT>();
+    }
     lds_barrier();
   };
   for (int tc = first; tc < total; tc += nb) {
@@ -308,11 +353,23 @@ __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float*
       for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = f32x16_t{};
     const int nkc = nk_of(tc);
     for (int kc = 0; kc < nkc; ++kc) {
-      issue(st_issue);  // into the stage read in the previous k block
-      advance();
-      stage8_mma<C, SWIGLU, FW, FA, SBROW>(lds, lds_sa, lds_sb, st, wave, wm, wn, lane, acc, mid);
+      // into the stage read in the previous k block (with POST, the first
+      // block's loads went out before the previous tile's epilogue)
+      if (POST < 0 || kc > 0 || tc == first) {
+        issue(st_issue);
+        advance();
+      }
+      after_epilogue = POST >= 0 && kc < 2 && tc != first;
+      stage8_mma<C, SWIGLU, FW, FA, SBROW, SWAP>(lds, lds_sa, lds_sb, st, wave, wm, wn, lane, acc,
+                                                 mid);
       st = st == NST - 1 ? 0 : st + 1;
       st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
+    }
+    if constexpr (POST >= 0) {
+      if (tc + nb < total) {
+        issue(st_issue);
+        advance();
+      }
     }
     epilogue(tc, acc);
   }

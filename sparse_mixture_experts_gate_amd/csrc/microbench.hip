@@ -78,6 +78,34 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4_t* __restrict
   sink[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
 }
 
+// Every thread writes 16-byte chunks (VEC) or 4-byte words in a grid-stride
+// loop; NT: non-temporal stores. The written values depend on the index so
+// nothing is constant-folded.
+template <bool NT, bool VEC>
+__global__ __launch_bounds__(256) void hbm_write_kernel(uint32_t* __restrict__ dst, int64_t n32) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if constexpr (VEC) {
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+    const int64_t n = n32 / 4;
+    for (int64_t i = i0; i < n; i += stride) {
+      const uint32_t v = static_cast<uint32_t>(i);
+      const u32x4_t w = {v, v + 1u, v + 2u, v + 3u};
+      if constexpr (NT)
+        __builtin_nontemporal_store(w, &d[i]);
+      else
+        d[i] = w;
+    }
+  } else {
+    for (int64_t i = i0; i < n32; i += stride) {
+      if constexpr (NT)
+        __builtin_nontemporal_store(static_cast<uint32_t>(i), &dst[i]);
+      else
+        dst[i] = static_cast<uint32_t>(i);
+    }
+  }
+}
+
 // Eight independent accumulators per wave, so the matrix core never waits
 // on a result; the operands change every iteration so nothing is hoisted.
 __global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* __restrict__ sink) {
@@ -148,6 +176,21 @@ int dsmoe_mb_hbm_read_default(const void* src, int64_t bytes, int blocks, void* 
                               hipStream_t s) {
   hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(blocks), dim3(256), 0, s,
                      static_cast<const u32x4_t*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  return hipGetLastError();
+}
+
+// Writes `bytes` (a multiple of 16) to dst with `blocks` workgroups of 256
+// threads: mode bit 0 = non-temporal stores, bit 1 = 16-byte stores (else
+// 4-byte words). Returns a hipError_t.
+int dsmoe_mb_hbm_write(void* dst, int64_t bytes, int blocks, int mode, hipStream_t s) {
+  uint32_t* d = static_cast<uint32_t*>(dst);
+  const int64_t n32 = bytes / 4;
+  switch (mode & 3) {
+    case 0: hipLaunchKernelGGL((hbm_write_kernel<false, false>), dim3(blocks), dim3(256), 0, s, d, n32); break;
+    case 1: hipLaunchKernelGGL((hbm_write_kernel<true, false>), dim3(blocks), dim3(256), 0, s, d, n32); break;
+    case 2: hipLaunchKernelGGL((hbm_write_kernel<false, true>), dim3(blocks), dim3(256), 0, s, d, n32); break;
+    default: hipLaunchKernelGGL((hbm_write_kernel<true, true>), dim3(blocks), dim3(256), 0, s, d, n32); break;
+  }
   return hipGetLastError();
 }
 
