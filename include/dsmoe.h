@@ -82,11 +82,16 @@ typedef enum moe_dtype {
  *                biased scores of eligible experts differ by <= eps, or the
  *                M-th and (M+1)-th group scores do (fp32 difference).
  * Divisibility: d, I, Is multiples of 64 for BF16/F32 weights and of 128 for
- * FP8 weights. The router weights and bias are always fp32. Size limits (the
- * kernels use 32-bit byte offsets): T*d*sizeof(x), T*(K+1)*max(I,Is)*sizeof(H)
- * (H is bf16 / fp32 / one byte with FP8), one expert's weights, 6*E*d and
- * T*K*4 (the int32 selections) must each stay below 2^31 bytes; larger calls
- * return MOE_ERR_UNSUPPORTED. */
+ * FP8 weights (the GEMMs step through the contraction 64 elements at a time,
+ * and an FP8 scale covers 128 of them). The router weights and bias are
+ * always fp32. Size limits (the kernels address gathered rows and one expert's
+ * weights with 32-bit byte offsets; H and the routed rows are addressed per
+ * tile from a 64-bit base): T*d*sizeof(x), one expert's weights, 6*E*d, T*K*4
+ * (the int32 selections) and, with FP8 weights, T*(K+1)*max(I,Is)/128*4 (H's
+ * scales) must each stay below 2^31 bytes; larger calls return
+ * MOE_ERR_UNSUPPORTED. Training (moe_forward_train, moe_backward,
+ * moe_backward_fp8) also needs T*max(d, 2*max(I,Is))*2 and
+ * 2*max(I,Is)*d*4 below 2^31 bytes. */
 typedef struct moe_layer_desc {
   int64_t T;
   int32_t d;

@@ -222,8 +222,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
   if (first < 0) return;
   const int nb = total;
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
-  const i32x4_t rdyp = rsrc4(a.dyp, static_cast<uint32_t>(a.TK) * row_bytes);
-  const i32x4_t rdy = rsrc4(a.dy, static_cast<uint32_t>(a.T) * row_bytes);
   const int nk = a.d / BK;
   const int64_t ldg = 2 * static_cast<int64_t>(a.ldh);
 
@@ -231,13 +229,16 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad2_bf16_kernel(BwdArgs a) 
     const TileCoord c = tile_coord_lds(gt, a.E, a.T, tile, C::BM);
     const int Ig = c.shared ? a.Is : a.I;
     const int rows_left = c.rows - c.m * C::BM;
-    const int rbase = (c.shared ? 0 : c.rbase) + c.m * C::BM;
+    const int64_t rbase = (c.shared ? 0 : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    // the tile's gradient rows through a resource based at its first row
+    // (64-bit base, 32-bit offsets inside the tile)
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(rbase + lr) * row_bytes : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * row_bytes : kInvalidRow;
     }
-    op.ra = c.shared ? rdy : rdyp;
+    op.ra = rsrc4(static_cast<const uint16_t*>(c.shared ? a.dy : a.dyp) + rbase * a.d,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * row_bytes);
     swizzle_rows<C>(op.ao);
     const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2)
                                  : static_cast<const uint16_t*>(a.w2) +
@@ -310,8 +311,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad1_bf16_kernel(BwdArgs a) 
   const int first = xcd_logical_block(blockIdx.x, nb);
   if (first >= total) return;
   const uint32_t grow_bytes = static_cast<uint32_t>(a.ldh) * 4u;  // rows of [da | db]
-  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const i32x4_t rg = rsrc4(a.dg, static_cast<uint32_t>(hrows) * grow_bytes);
   const uint32_t ld_bytes = static_cast<uint32_t>(a.d) * 2u;
   const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
 
@@ -320,12 +319,14 @@ __global__ __launch_bounds__(C::NT, C::MINW) void dgrad1_bf16_kernel(BwdArgs a) 
     const int Ig = c.shared ? a.Is : a.I;
     const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
     const int rows_left = c.rows - c.m * C::BM;
+    // the tile's [da | db] rows through a resource based at its first row
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * grow_bytes : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * grow_bytes : kInvalidRow;
     }
-    op.ra = rg;
+    op.ra = rsrc4(static_cast<const uint16_t*>(a.dg) + hrow0 * 2 * a.ldh,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * grow_bytes);
     swizzle_rows<C>(op.ao);
     const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws13)
                                  : static_cast<const uint16_t*>(a.w13) +

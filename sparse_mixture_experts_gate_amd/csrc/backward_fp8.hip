@@ -76,8 +76,6 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
   const int dkb = a.d / 128;
   const int gkb = 2 * a.ldh / 128;
   const uint32_t d = static_cast<uint32_t>(a.d);
-  const i32x4_t ryr = rsrc4(a.dyq, static_cast<uint32_t>(a.TK) * d);
-  const i32x4_t rys = rsrc4(a.dysq, static_cast<uint32_t>(a.T) * d);
   const i32x4_t rsyr = rsrc4(a.dys, static_cast<uint32_t>(a.TK) * dkb * 4u);
   const i32x4_t rsys = rsrc4(a.dyss, static_cast<uint32_t>(a.T) * dkb * 4u);
   const int nk = a.d / BK8;
@@ -87,15 +85,18 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
     const int Ig = c.shared ? a.Is : a.I;
     const int rows_left = c.rows - c.m * C::BM;
     const int64_t row0 = (c.shared ? 0 : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    // the tile's gradient codes through a resource based at its first row
+    // (64-bit base, 32-bit offsets inside the tile)
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(row0 + lr) * d : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * d : kInvalidRow;
     }
     op.sa_off = (tid < C::BM && tid < rows_left)
                     ? static_cast<uint32_t>((row0 + tid) * dkb) * 4u
                     : kInvalidRow;
-    op.ra = c.shared ? rys : ryr;
+    op.ra = rsrc4((c.shared ? a.dysq : a.dyq) + row0 * a.d,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * d);
     op.rsa = c.shared ? rsys : rsyr;
     const uint8_t* W = c.shared ? a.ws2t : a.w2t + static_cast<int64_t>(c.g) * a.I * a.d;
     const float* WS = c.shared ? a.ws2t_scale
@@ -226,7 +227,6 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
   const int gkb = 2 * a.ldh / 128;
   const uint32_t lrow = 2u * static_cast<uint32_t>(a.ldh);
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const i32x4_t rg = rsrc4(a.dgq, static_cast<uint32_t>(hrows) * lrow);
   const i32x4_t rsg = rsrc4(a.dgs, static_cast<uint32_t>(hrows) * gkb * 4u);
   const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
 
@@ -235,15 +235,17 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
     const int Ig = c.shared ? a.Is : a.I;
     const int rows_left = c.rows - c.m * C::BM;
     const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
+    // the tile's [da | db] codes through a resource based at its first row
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * lrow : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * lrow : kInvalidRow;
     }
     op.sa_off = (tid < C::BM && tid < rows_left)
                     ? static_cast<uint32_t>((hrow0 + tid) * gkb) * 4u
                     : kInvalidRow;
-    op.ra = rg;
+    op.ra = rsrc4(a.dgq + hrow0 * lrow,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * lrow);
     op.rsa = rsg;
     const int kb = 2 * Ig / 128;
     const uint8_t* W = c.shared ? a.ws13t : a.w13t + static_cast<int64_t>(c.g) * a.d * 2 * a.I;

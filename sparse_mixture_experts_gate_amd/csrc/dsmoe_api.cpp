@@ -91,15 +91,17 @@ moe_status validate_desc(const moe_layer_desc* d) {
   // the permutation reads topk_idx through a 32-bit byte range
   if (d->T * static_cast<int64_t>(d->top_k) * 4 >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*K*4 must be < 2^31 bytes");
-  // the GEMMs address x, H and each expert's weights with 32-bit byte offsets
+  // the GEMMs address the gathered rows of x and each expert's weights with
+  // 32-bit byte offsets (H is addressed per tile, from a 64-bit base)
   const int64_t lim = (int64_t(1) << 31) - 1;
   const int64_t s_act = d->act_dtype == MOE_DT_F32 ? 4 : 2;
   const int64_t s_w = d->w_dtype == MOE_DT_F32 ? 4 : d->w_dtype == MOE_DT_BF16 ? 2 : 1;
   const int64_t ldh = std::max(d->inter, d->shared_inter);
   if (d->T * d->d * s_act > lim)
     return fail(MOE_ERR_UNSUPPORTED, "T*d*sizeof(act) must be < 2^31 bytes");
-  if ((d->T * d->top_k + d->T) * ldh * s_w > lim)
-    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*max(I,Is)*sizeof(H) must be < 2^31 bytes");
+  // H's scales (FP8) are addressed as one range
+  if (s_w == 1 && (d->T * d->top_k + d->T) * (ldh / 128) * 4 > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*max(I,Is)/128*4 must be < 2^31 bytes");
   if (int64_t(2) * ldh * d->d * s_w > lim)
     return fail(MOE_ERR_UNSUPPORTED, "one expert's weights must be < 2^31 bytes");
   if (int64_t(d->n_experts) * 3 * d->d * 2 > lim)
@@ -380,14 +382,15 @@ moe_status validate_train(const moe_layer_desc* d) {
       (d->w_dtype != MOE_DT_BF16 && d->w_dtype != MOE_DT_FP8_E4M3))
     return fail(MOE_ERR_UNSUPPORTED,
                 "training supports bf16 activations with bf16 or FP8 weights only");
-  // 32-bit byte offsets of the backward's buffers
+  // 32-bit byte offsets of the backward's buffers: the input-gradient GEMMs
+  // address their row operands per tile from a 64-bit base; the
+  // weight-gradient GEMMs address one group's rows (an expert's segment, or
+  // all T rows for the shared expert) of x, dY, H and [da | db] as one range
   const int64_t lim = (int64_t(1) << 31) - 1;
-  const int64_t TK = d->T * d->top_k;
   const int64_t ldh = std::max(d->inter, d->shared_inter);
-  if (TK * d->d * 2 > lim)
-    return fail(MOE_ERR_UNSUPPORTED, "T*K*d*2 must be < 2^31 bytes for training");
-  if ((TK + d->T) * 2 * ldh * 2 > lim)
-    return fail(MOE_ERR_UNSUPPORTED, "T*(K+1)*2*max(I,Is)*2 must be < 2^31 bytes for training");
+  if (d->T * std::max<int64_t>(d->d, 2 * ldh) * 2 > lim)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T*max(d, 2*max(I,Is))*2 must be < 2^31 bytes for training");
   // one expert's fp32 weight gradient (the largest, [2 max(I,Is), d]) is
   // written through a buffer resource whose byte size must stay below 2^31,
   // so that the out-of-range offset of masked epilogue entries lies past it

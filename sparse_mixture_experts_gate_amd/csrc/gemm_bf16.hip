@@ -272,8 +272,6 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
   const int first = xcd_logical_block(blockIdx.x, nb);
   if (first >= total) return;
   const uint32_t hrow_bytes = static_cast<uint32_t>(a.ldh) * 2u;
-  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const i32x4_t rh = rsrc4(a.H, static_cast<uint32_t>(hrows) * hrow_bytes);
   // the shared group's tiles are the last ones
   const int shared_first = a.E > 0 ? gt.gnext[a.E - 1] : 0;
 
@@ -282,12 +280,15 @@ __global__ __launch_bounds__(C::NT, C::MINW) void ffn2_bf16_kernel(FfnArgs a) {
     const int Ig = c.shared ? a.Is : a.I;
     const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
     const int rows_left = c.rows - c.m * C::BM;
+    // H through a resource based at the tile's first row (64-bit base, 32-bit
+    // offsets inside the tile), so H itself may exceed 2^31 bytes
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(hrow0 + lr) * hrow_bytes : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * hrow_bytes : kInvalidRow;
     }
-    op.ra = rh;
+    op.ra = rsrc4(static_cast<const uint16_t*>(a.H) + hrow0 * a.ldh,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * hrow_bytes);
     const uint16_t* W = c.shared ? static_cast<const uint16_t*>(a.ws2)
                                  : static_cast<const uint16_t*>(a.w2) +
                                        static_cast<int64_t>(c.g) * a.d * a.I;

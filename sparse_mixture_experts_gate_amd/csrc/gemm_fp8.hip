@@ -238,7 +238,6 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   if (first >= total) return;
   const int hkb = a.ldh / 128;
   const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
-  const i32x4_t rh = rsrc4(a.H, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(a.ldh));
   const i32x4_t rsh =
       rsrc4(a.H_scale, static_cast<uint32_t>(hrows) * static_cast<uint32_t>(hkb) * 4u);
   // the shared group's tiles are the last ones
@@ -252,16 +251,19 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
     const int Ig = c.shared ? a.Is : a.I;
     const int64_t hrow0 = (c.shared ? a.TK : c.rbase) + static_cast<int64_t>(c.m) * C::BM;
     const int rows_left = c.rows - c.m * C::BM;
+    // H codes through a resource based at the tile's first row (64-bit base,
+    // 32-bit offsets inside the tile), so H itself may exceed 2^31 bytes
 #pragma unroll
     for (int p = 0; p < C::A_LOADS; ++p) {
       const int lr = r0 + p * C::RPP;
-      op.ao[p] = lr < rows_left
-                     ? static_cast<uint32_t>(hrow0 + lr) * static_cast<uint32_t>(a.ldh)
-                     : kInvalidRow;
+      op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * static_cast<uint32_t>(a.ldh)
+                                : kInvalidRow;
     }
+    op.ra = rsrc4(static_cast<const uint8_t*>(a.H) + hrow0 * a.ldh,
+                  static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) *
+                      static_cast<uint32_t>(a.ldh));
     op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>((hrow0 + tid) * hkb) * 4u
                                                  : kInvalidRow;
-    op.ra = rh;
     op.rsa = rsh;
     const uint8_t* W = c.shared ? static_cast<const uint8_t*>(a.ws2)
                                 : static_cast<const uint8_t*>(a.w2) +

@@ -58,15 +58,49 @@ def _desc(L, **kw):
     (dict(n_groups=4, topk_groups=2, group_topn=5), 1), (dict(inter=0), 1),
     (dict(shared_inter=-1), 1), (dict(act_dtype=0), 2), (dict(w_dtype=2, d=192), 2),
     (dict(d=200), 2), (dict(inter=96), 2), (dict(near_tie_eps=float("nan")), 1),
-    # 32-bit byte-offset limits: x, H, one expert's weights, the split router weights
-    (dict(T=1 << 22), 2), (dict(T=1 << 20, inter=1024), 2), (dict(inter=1 << 21), 2),
-    (dict(n_experts=512, d=699072), 2),
+    # 32-bit byte-offset limits: x, H's FP8 scales, one expert's weights, the
+    # split router weights
+    (dict(T=1 << 22), 2),
+    (dict(T=400000, inter=1 << 16, shared_inter=1 << 16, w_dtype=2), 2),
+    (dict(inter=1 << 21), 2), (dict(n_experts=512, d=699072), 2),
 ])
 def test_descriptor_validation(L, kw, status):
     n = ctypes.c_size_t(0)
     st = L.lib().moe_workspace_size(ctypes.byref(_desc(L, **kw)), ctypes.byref(n))
     assert st == status, L.lib().moe_last_error()
     assert L.lib().moe_last_error()
+
+
+def test_h_beyond_2_gib_is_accepted(L):
+    """H is addressed per tile from a 64-bit base, so a forward whose H holds
+    more than 2^31 bytes is accepted and its workspace holds all of H."""
+    n = ctypes.c_size_t(0)
+    T, inter = 1 << 20, 1024
+    d = _desc(L, T=T, inter=inter, shared_inter=inter)
+    assert L.lib().moe_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0, \
+        L.lib().moe_last_error()
+    h_bytes = T * (2 + 1) * inter * 2
+    assert h_bytes > 1 << 31
+    assert n.value >= h_bytes
+
+
+def test_training_accepts_v3_batches_beyond_32k_tokens(L):
+    """The backward's row operands are addressed per tile (input-gradient
+    GEMMs) or per group (weight-gradient GEMMs), so at the V3 shape training
+    takes batches up to T * max(d, 2 max(I, Is)) * 2 < 2^31 bytes, for bf16
+    and FP8 weights."""
+    lib = L.lib()
+    n = ctypes.c_size_t(0)
+    v3 = dict(d=7168, n_experts=256, top_k=8, n_groups=8, topk_groups=4, group_topn=2,
+              inter=2048, shared_inter=2048)
+    t_max = ((1 << 31) - 1) // (7168 * 2)
+    for w in (L.MOE_DT_BF16, L.MOE_DT_FP8_E4M3):
+        for T in (32768, 131072, t_max):
+            d = _desc(L, T=T, w_dtype=w, **v3)
+            assert lib.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0, \
+                lib.moe_last_error()
+        d = _desc(L, T=t_max + 1, w_dtype=w, **v3)
+        assert lib.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 2
 
 
 def test_valid_descriptor_sizes(L):

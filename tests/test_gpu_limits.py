@@ -1,6 +1,8 @@
 """GPU parity at the largest calls the descriptor accepts: the kernels address
-activations, H and the routed rows with 32-bit byte offsets, so the last
-tokens and the last permuted rows sit just below 2^31 bytes. The largest T is
+the gathered activation rows (and, in the backward, the routed rows) with
+32-bit byte offsets, so the last tokens and the last permuted rows sit just
+below 2^31 bytes; the forward's H is addressed per tile from a 64-bit base and
+lies well beyond 2^31 bytes at the forward's limit. The largest T is
 found through the library's own validation (moe_workspace_size /
 moe_backward_workspace_size), on a layer narrow enough that the oracle checks
 the rows near the end one by one: routing bit-exact on every token from the
@@ -51,9 +53,11 @@ def _sample(T, perm, extra=4):
 def test_forward_at_size_limit():
     wl = WIDE
     T = _largest_T(wl, L.lib().moe_workspace_size)
-    # H is the binding limit here: T * (K + 1) * max(I, Is) * 2 bytes < 2^31
-    assert T * (wl.K + 1) * max(wl.I, wl.Is) * 2 < (1 << 31)
-    assert (T + 1) * (wl.K + 1) * max(wl.I, wl.Is) * 2 >= (1 << 31) - 1
+    # x is the binding limit here: T * d * 2 bytes < 2^31; H (T (K + 1) rows of
+    # max(I, Is) bf16) is larger than 2^31 bytes, so its last rows are read
+    # through the per-tile resource
+    assert T * wl.d * 2 < (1 << 31) and (T + 1) * wl.d * 2 >= (1 << 31) - 1
+    assert T * (wl.K + 1) * max(wl.I, wl.Is) * 2 > (1 << 31)
     _log(f"forward at the size limit: T = {T}")
     wl = wl.with_(T=T)
     P = make_inputs(wl, DEV)
@@ -75,11 +79,28 @@ def test_forward_at_size_limit():
     assert err <= TOL["bf16"]
 
 
+def _channel_grads(x, w13, w2, dY, chans):
+    """Weight gradients of intermediate channels `chans` of one expert over all
+    its rows: SwiGLU acts on each intermediate channel alone, so the rows c
+    and I + c of dW13 and the column c of dW2 are those of the expert cut down
+    to that channel (I = 1). Returns {c: (dW13 rows [2, d], dW2 column [d])}."""
+    inter = w13.shape[0] // 2
+    out = {}
+    for c in chans:
+        _, d13, d2, _ = O.swiglu_expert_backward(x, w13[[c, inter + c]], w2[:, [c]], dY)
+        out[c] = (d13, d2[:, 0])
+    return out
+
+
 def test_backward_at_size_limit():
     wl = WIDE
     T = _largest_T(wl, L.lib().moe_backward_workspace_size)
-    # [da | db] is the binding limit: T * (K + 1) * 2 max(I, Is) * 2 bytes < 2^31
-    assert T * (wl.K + 1) * 2 * max(wl.I, wl.Is) * 2 < (1 << 31)
+    # the shared expert's rows in the weight-gradient GEMMs bind:
+    # T * max(d, 2 max(I, Is)) * 2 bytes < 2^31; the routed buffers ([T K, d]
+    # gradients, [T (K + 1), 2 max(I, Is)] [da | db]) lie beyond 2^31 bytes
+    row = max(wl.d, 2 * max(wl.I, wl.Is)) * 2
+    assert T * row < (1 << 31) and (T + 1) * row >= (1 << 31) - 1
+    assert T * wl.K * wl.d * 2 > (1 << 31)
     _log(f"backward at the size limit: T = {T}")
     wl = wl.with_(T=T)
     P = make_inputs(wl, DEV)
@@ -100,7 +121,9 @@ def test_backward_at_size_limit():
     err = row_rel_err(host(dx[t]), ref.dx)
     _log(f"  tokens {rows.tolist()}: dx max row-rel err {err:.2e}")
     assert err <= TOL["bf16"]
-    # the expert whose rows are last in the permuted buffers
+    # weight gradients over all rows, three intermediate channels each: the
+    # expert whose rows are last in the permuted buffers, and the shared
+    # expert (every token)
     counts = host(sv["counts"])
     e = int(np.nonzero(counts)[0][-1])
     toks, slots = np.nonzero(idx == e)
@@ -109,11 +132,21 @@ def test_backward_at_size_limit():
     gate = s_sel[np.arange(len(toks)), slots] / s_sel.sum(1)
     xe = host(P["x"][torch.as_tensor(toks, device=DEV)])
     dye = host(dy[torch.as_tensor(toks, device=DEV)])
-    _, dW13, dW2, _ = O.swiglu_expert_backward(xe, w13[e], w2[e], gate[:, None] * dye)
-    e13 = mat_rel_err(host(gr["dw13"][e]), dW13)
-    e2 = mat_rel_err(host(gr["dw2"][e]), dW2)
-    _log(f"  expert {e} ({len(toks)} tokens): dw13 {e13:.2e} dw2 {e2:.2e}")
-    assert e13 <= TOL["bf16"] and e2 <= TOL["bf16"]
+    chans = [0, wl.I // 2 + 1, wl.I - 1]
+    dw13, dw2 = host(gr["dw13"][e]), host(gr["dw2"][e])
+    for c, (d13, d2) in _channel_grads(xe, w13[e], w2[e], gate[:, None] * dye, chans).items():
+        e13 = mat_rel_err(dw13[[c, wl.I + c]], d13)
+        e2 = mat_rel_err(dw2[:, c], d2)
+        _log(f"  expert {e} ({len(toks)} tokens), channel {c}: dw13 {e13:.2e} dw2 {e2:.2e}")
+        assert e13 <= TOL["bf16"] and e2 <= TOL["bf16"]
+    x_all, dy_all = host(P["x"]), host(dy)
+    dws13, dws2 = host(gr["dws13"]), host(gr["dws2"])
+    chans = [0, wl.Is // 3, wl.Is - 1]
+    for c, (d13, d2) in _channel_grads(x_all, ws13, ws2, dy_all, chans).items():
+        e13 = mat_rel_err(dws13[[c, wl.Is + c]], d13)
+        e2 = mat_rel_err(dws2[:, c], d2)
+        _log(f"  shared expert ({T} tokens), channel {c}: dw13 {e13:.2e} dw2 {e2:.2e}")
+        assert e13 <= TOL["bf16"] and e2 <= TOL["bf16"]
 
 
 def test_fp8_forward_at_size_limit():
