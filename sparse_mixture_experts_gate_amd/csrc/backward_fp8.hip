@@ -32,6 +32,7 @@ namespace dsmoe {
 namespace {
 
 constexpr int kE4M3 = 0, kE5M2 = 1;
+constexpr int kNonTemporal = 2;  // cache-policy bit of buffer stores (nt)
 
 using T8Bwd = Tile8<128, 256, 64, 64>;  // 8 waves of 64 x 64, 144 KB ring
 
@@ -396,7 +397,8 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
   // stores two 128-byte row pieces. Buffer stores with out-of-range offsets
   // for the masked entries: every call issues exactly MI * NJ * 16 stores (no
   // branch skips one), which lets them drain during the next tile's first k
-  // block.
+  // block. The gradients (as large as the weights, in fp32) are written with
+  // the non-temporal policy, so that they do not push the operands out of L2.
   auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const Coord c = coord(tile);
     float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
@@ -414,7 +416,8 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
           const uint32_t off = (m < c.M && n < c.N)
                                    ? (static_cast<uint32_t>(m) * c.N + n) * 4u
                                    : kInvalidRow;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0,
+                                                kNonTemporal);
         }
       }
     }
