@@ -133,6 +133,51 @@ def test_fp8_backward_no_shared_empty_experts():
             assert not dw13[e].any() and not dw2[e].any()
 
 
+def test_fp8_backward_single_token_zero_tokens_and_large_k():
+    """Degenerate sizes of the FP8 backward: one token (every 128x1 tile holds
+    one row, padded with zeros), no token (the weight gradients are
+    zero-filled, whatever the buffers held), and more than eight experts per
+    token (K = 12 of 24, two groups allowed of four)."""
+    wl = FP8_SMALL
+    _log("FP8 backward: T = 1")
+    P, layer, y, sv, dy, dx, gr = _run(wl, T=1)
+    ref = _oracle(wl, P, sv, dy)
+    tol = TOL["fp8"]
+    assert row_rel_err(host(dx), ref.dx) <= tol
+    counts = host(sv["counts"])
+    dw13, dw2 = host(gr["dw13"]), host(gr["dw2"])
+    for e in range(wl.E):
+        if counts[e]:
+            assert mat_rel_err(dw13[e], ref.dw13[e]) <= tol
+            assert mat_rel_err(dw2[e], ref.dw2[e]) <= tol
+        else:
+            assert not dw13[e].any() and not dw2[e].any()
+    assert mat_rel_err(host(gr["dws13"]), ref.dws13) <= tol
+    assert mat_rel_err(host(gr["dws2"]), ref.dws2) <= tol
+    _log("FP8 backward: T = 0 zero-fills the weight gradients")
+    g0 = {k: (None if v is None else torch.full_like(v, 3.0)) for k, v in gr.items()}
+    x0 = P["x"][:0]
+    sv0 = layer.alloc_saved(0)
+    layer.forward_train(x0, sv0)
+    dx0, g0 = layer.backward(x0, dy[:0], sv0, grads=g0)
+    torch.cuda.synchronize()
+    assert dx0.numel() == 0
+    for k, v in g0.items():
+        if v is not None:
+            assert not v.any(), k
+    wl = FP8_SMALL.with_(name="fp8_k12", T=200, E=24, K=12, G=4, M=2, n_clusters=4)
+    _log("FP8 backward: K = 12")
+    P, layer, y, sv, dy, dx, gr = _run(wl)
+    ref = _oracle(wl, P, sv, dy)
+    assert row_rel_err(host(dx), ref.dx) <= tol
+    counts = host(sv["counts"])
+    dw13, dw2 = host(gr["dw13"]), host(gr["dw2"])
+    errs = [max(mat_rel_err(dw13[e], ref.dw13[e]), mat_rel_err(dw2[e], ref.dw2[e]))
+            for e in np.nonzero(counts)[0]]
+    _log(f"  dx {row_rel_err(host(dx), ref.dx):.2e} dW max {max(errs):.2e}")
+    assert max(errs) <= tol
+
+
 def test_fp8_backward_v3_sampled():
     """The V3 layer in FP8 (T = 8192, d = 7168, 256 experts of 2048, shared
     expert of 2048) as the benchmark runs it: the input gradients of 256
