@@ -325,7 +325,10 @@ moe_status moe_backward(const moe_layer_desc* desc, const void* x, const float* 
  * block of W^T with the same scale, so this is exactly the block
  * quantization of the transposed matrices (mhpq.cn "DeepSeek-V3 高效训练
  * 关键技术全景解析" §4.1: 128x128 weight blocks). rows, cols multiples of
- * 128. Weight preparation: once per weight set. */
+ * 128. Weight preparation: once per weight set. Caller-owned device buffers;
+ * errors: MOE_ERR_INVALID_ARGUMENT (sizes, NULL), MOE_ERR_MISALIGNED,
+ * MOE_ERR_UNSUPPORTED (more than 2^31 64x64 tiles); nothing is enqueued
+ * on error. */
 moe_status moe_transpose_fp8_blocks(const uint8_t* q, const float* scale, int64_t n_mats,
                                     int32_t rows, int32_t cols, uint8_t* qt, float* scale_t,
                                     hipStream_t stream);
@@ -346,7 +349,11 @@ moe_status moe_transpose_fp8_blocks(const uint8_t* q, const float* scale, int64_
  *     channel): dY and [da | db] in E5M2, H and x in E4M3.
  * The gates, the router and the combine stay in high precision, as in
  * moe_backward. x, w_router, w, saved, dy, dx, g as in moe_backward (saved
- * from moe_forward_train with the same FP8 weights). */
+ * from moe_forward_train with the same FP8 weights). ws: ws_bytes >=
+ * moe_backward_workspace_size(desc). Errors (nothing is enqueued):
+ * MOE_ERR_UNSUPPORTED for weights other than E4M3 or sizes past the
+ * training limits, MOE_ERR_INVALID_ARGUMENT for NULL buffers,
+ * MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE_TOO_SMALL. */
 moe_status moe_backward_fp8(const moe_layer_desc* desc, const void* x, const float* w_router,
                             const moe_weights* w, const moe_weights* wt, const moe_saved* saved,
                             const void* dy, void* dx, const moe_grads* g, void* ws,

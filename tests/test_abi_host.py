@@ -261,3 +261,32 @@ def test_noalloc_forward_validates_before_touching_the_device(L):
     assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0 and n.value > 128 << 20
     assert lib.deepseek_moe_forward_noalloc(*args(big)) == 4
     assert b"fixed scratch" in lib.moe_last_error()
+
+
+def test_backward_fp8_validation_before_any_launch(L):
+    """moe_backward_fp8 checks everything on the host and returns before
+    enqueueing: bf16 weights, missing transposed weights and a short
+    workspace each give their own status."""
+    lib = L.lib()
+    good = 4096
+    n = ctypes.c_size_t(0)
+    d8 = _desc(L, w_dtype=L.MOE_DT_FP8_E4M3)
+    assert lib.moe_backward_workspace_size(ctypes.byref(d8), ctypes.byref(n)) == 0
+    need = n.value
+    w = L.MoeWeights(*([good] * 8))
+    sv = L.MoeSaved(*([good] * 10))
+    g = L.MoeGrads(*([good] * 5))
+
+    def call(desc, wt, ws_bytes):
+        return lib.moe_backward_fp8(ctypes.byref(desc), good, good, ctypes.byref(w),
+                                    None if wt is None else ctypes.byref(wt), ctypes.byref(sv),
+                                    good, good, ctypes.byref(g), good, ws_bytes, None)
+
+    assert call(_desc(L), w, need) == 2
+    assert b"FP8 weights" in lib.moe_last_error()
+    assert call(d8, None, need) == 1
+    assert b"transposed weights" in lib.moe_last_error()
+    assert call(d8, w, need - 1) == 4
+    assert b"workspace" in lib.moe_last_error()
+    bad = L.MoeWeights(*([good] * 3 + [4100] + [good] * 4))
+    assert call(d8, bad, need) == 3
