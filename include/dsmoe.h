@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DSMOE_ABI_VERSION 1
+#define DSMOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -81,6 +81,10 @@ typedef enum moe_dtype {
  *   near_tie_eps a token counts as a near tie when the K-th and (K+1)-th
  *                biased scores of eligible experts differ by <= eps, or the
  *                M-th and (M+1)-th group scores do (fp32 difference).
+ *   out_dtype    dtype of the layer output y: MOE_DT_F32 or MOE_DT_BF16 (the
+ *                combine's fp32 sum, stored as is or rounded to bf16 once);
+ *                y_perm and y_shared keep the activations' dtype. K <= 64
+ *                (one lane per selected expert in the routing wave).
  * Divisibility: d, I, Is multiples of 64 for BF16/F32 weights and of 128 for
  * FP8 weights (the GEMMs step through the contraction 64 elements at a time,
  * and an FP8 scale covers 128 of them). The router weights and bias are
@@ -105,6 +109,7 @@ typedef struct moe_layer_desc {
   int32_t act_dtype;
   int32_t w_dtype;
   float near_tie_eps;
+  int32_t out_dtype;
 } moe_layer_desc;
 
 /* Expert weights (device pointers, w_dtype elements, row-major):
@@ -169,7 +174,10 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* topk_idx,
                        const int32_t* counts, const void* x, int32_t* offsets, int32_t* perm,
                        int32_t* inv, void* x_perm, float* x_perm_scale, hipStream_t stream);
 
-/* Grouped expert FFNs: for every expert e, rows offsets[e]..offsets[e+1]-1
+/* Grouped expert FFNs (SwiGLU experts, fine-grained routed experts plus one
+ * shared expert: mhpq.cn §1.1; FP8 GEMMs with 1x128 / 128x128 scaling:
+ * mhpq.cn §4.1, gkm0120.cn Q8): for every expert e, rows offsets[e] ..
+ * offsets[e+1]-1
  *   y_perm[r] = W2_e (silu(W1_e a_r) * (W3_e a_r)),
  * with a_r = x_perm[r] when x_perm != NULL, else x[perm[r]]; and for every
  * token y_shared[t] = the shared expert applied to x[t].
@@ -183,22 +191,29 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* w, cons
                           size_t ws_bytes, hipStream_t stream);
 
 /* Gated combine: y[t] = y_shared[t] + sum_k topk_gate[t,k] * y_perm[inv[t,k]],
- * fp32 accumulation in slot order, y in act_dtype. y_shared may be NULL
- * (no shared expert). */
+ * fp32 accumulation in slot order, y in out_dtype; y_perm and y_shared in
+ * the activations' dtype. The shared expert is ungated and every token's K
+ * routed outputs are weighted by its gates (mhpq.cn "DeepSeek-V3 高效训练关键
+ * 技术全景解析" §1.1; kaiyunto.com walkthrough, DeepSeekMoE paragraph).
+ * y_shared may be NULL (no shared expert). */
 moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int32_t* inv,
                        const float* topk_gate, const void* y_shared, void* y,
                        hipStream_t stream);
 
 /* Bias update from this step's loads (in place): with balanced load T*K/E,
  * b[e] -= gamma if counts[e]*E > T*K, b[e] += gamma if counts[e]*E < T*K,
- * unchanged otherwise; fp32 arithmetic. The only call that mutates an input. */
+ * unchanged otherwise; fp32 arithmetic (kaiyunto.com walkthrough, DeepSeekMoE
+ * paragraph: bias update speed gamma; mhpq.cn §1.2: applied every step). The
+ * only call that mutates an input. */
 moe_status moe_bias_update(const moe_layer_desc* desc, const int32_t* counts, float gamma,
                            float* bias, hipStream_t stream);
 
-/* The whole layer: moe_gate, the counting sort, moe_expert_ffn (rows gathered
- * from x inside the GEMM) and moe_combine, enqueued back to back. It does NOT
- * update the bias: call moe_bias_update with `counts` afterwards.
- *   y [T, d] act_dtype OUT; topk_idx, topk_gate, counts OUT as in moe_gate;
+/* The whole layer (the DeepSeekMoE feed-forward layer of the preamble's
+ * sources: kaiyunto.com walkthrough, DeepSeekMoE paragraph; mhpq.cn §1.1,
+ * §1.2, §3.1, §4.1): moe_gate, the counting sort, moe_expert_ffn (rows
+ * gathered from x inside the GEMM) and moe_combine, enqueued back to back. It
+ * does NOT update the bias: call moe_bias_update with `counts` afterwards.
+ *   y [T, d] out_dtype OUT; topk_idx, topk_gate, counts OUT as in moe_gate;
  *   near_tie and logits optional OUT. */
 moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
                                 const float* w_router, const float* bias, const moe_weights* w,

@@ -34,7 +34,7 @@ class MoeLayerDesc(ctypes.Structure):
                 ("topk_groups", ctypes.c_int32), ("group_topn", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("near_tie_eps", ctypes.c_float)]
+                ("near_tie_eps", ctypes.c_float), ("out_dtype", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):

@@ -83,6 +83,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
   if (!(f32 || bf16 || fp8))
     return fail(MOE_ERR_UNSUPPORTED, "dtype pair act=%d w=%d not supported", d->act_dtype,
                 d->w_dtype);
+  if (d->out_dtype != MOE_DT_F32 && d->out_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "out_dtype = %d: y is fp32 or bf16", d->out_dtype);
   const int mult = fp8 ? 128 : 64;
   if (d->d % mult || d->inter % mult || d->shared_inter % mult)
     return fail(MOE_ERR_UNSUPPORTED, "d, inter, shared_inter must be multiples of %d", mult);
@@ -761,7 +763,7 @@ moe_status moe_combine(const moe_layer_desc* desc, const void* y_perm, const int
   st = check_opt({{y_shared, "y_shared"}});
   if (st) return st;
   HIP_TRY(launch_combine(y_perm, inv, topk_gate, desc->shared_inter > 0 ? y_shared : nullptr, y,
-                         desc->T, desc->top_k, desc->d, desc->act_dtype, stream),
+                         desc->T, desc->top_k, desc->d, desc->act_dtype, desc->out_dtype, stream),
           "combine");
   return MOE_OK;
 }
@@ -857,7 +859,7 @@ moe_status run_forward(const moe_layer_desc* desc, const void* x, const float* w
                true, stream);
   if (st) return st;
   HIP_TRY(launch_combine(yperm, inv, topk_gate, yshared, y, desc->T, desc->top_k, desc->d,
-                         desc->act_dtype, stream),
+                         desc->act_dtype, desc->out_dtype, stream),
           "combine");
   HIP_TRY(prof_record(5, stream), "profile event");
   return MOE_OK;
@@ -954,7 +956,7 @@ moe_status moe_forward_train(const moe_layer_desc* desc, const void* x, const fl
                L.ffn, false, true, stream, sv->h, sv->gu);
   if (st) return st;
   HIP_TRY(launch_combine(sv->y_perm, sv->inv, sv->topk_gate, yshared, y, desc->T, desc->top_k,
-                         desc->d, desc->act_dtype, stream),
+                         desc->d, desc->act_dtype, desc->out_dtype, stream),
           "combine");
   return MOE_OK;
 }

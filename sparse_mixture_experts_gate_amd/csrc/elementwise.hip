@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels: gated combine, bias update, FP8 quantizers.
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -25,12 +27,12 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
   }
 }
 
-template <int KT>
+template <int KT, bool OUT_F32>
 __global__ __launch_bounds__(1024) void combine_bf16_kernel(const uint16_t* __restrict__ yperm,
                                                            const int32_t* __restrict__ inv,
                                                            const float* __restrict__ gate,
                                                            const uint16_t* __restrict__ yshared,
-                                                           uint16_t* __restrict__ y, int K_rt, int d) {
+                                                           void* __restrict__ y, int K_rt, int d) {
   const int K = KT > 0 ? KT : K_rt;
   const int64_t t = blockIdx.x;
   const int nch = d / 8;
@@ -66,20 +68,27 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const uint16_t* __re
         for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(g, f[q], acc[q]);
       }
     }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(y + t * d + c * 8) = o;
+    if constexpr (OUT_F32) {
+      float4* yo = reinterpret_cast<float4*>(static_cast<float*>(y) + t * d + c * 8);
+      yo[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      yo[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + t * d + c * 8) = o;
+    }
   }
 }
 
+template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ yperm,
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ gate,
                                                           const float* __restrict__ yshared,
-                                                          float* __restrict__ y, int K, int d) {
+                                                          void* __restrict__ y, int K, int d) {
   const int64_t t = blockIdx.x;
   const int nch = d / 4;
   for (int c = threadIdx.x; c < nch; c += blockDim.x) {
@@ -94,7 +103,11 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
       acc.z = __builtin_fmaf(g, v.z, acc.z);
       acc.w = __builtin_fmaf(g, v.w, acc.w);
     }
-    *reinterpret_cast<float4*>(y + t * d + c * 4) = acc;
+    if constexpr (OUT_BF16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + t * d + c * 4) =
+          make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + t * d + c * 4) = acc;
   }
 }
 
@@ -225,25 +238,40 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,
                           const void* yshared, void* y, int64_t T, int K, int d, int io_dtype,
-                          hipStream_t s) {
+                          int out_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (io_dtype == 1) {
     const auto* yp = static_cast<const uint16_t*>(yperm);
     const auto* ys = static_cast<const uint16_t*>(yshared);
-    auto* yo = static_cast<uint16_t*>(y);
     int nthr = ((d / 8 + 63) / 64) * 64;
     if (nthr > 1024) nthr = 1024;
     const dim3 grid(static_cast<unsigned>(T)), block(static_cast<unsigned>(nthr));
-    if (K == 8)
-      hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
-    else if (K == 6)
-      hipLaunchKernelGGL(combine_bf16_kernel<6>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
+    auto go = [&](auto out_f32) {
+      constexpr bool F = decltype(out_f32)::value;
+      if (K == 8)
+        hipLaunchKernelGGL((combine_bf16_kernel<8, F>), grid, block, 0, s, yp, inv, gate, ys, y, K,
+                           d);
+      else if (K == 6)
+        hipLaunchKernelGGL((combine_bf16_kernel<6, F>), grid, block, 0, s, yp, inv, gate, ys, y, K,
+                           d);
+      else
+        hipLaunchKernelGGL((combine_bf16_kernel<0, F>), grid, block, 0, s, yp, inv, gate, ys, y, K,
+                           d);
+    };
+    if (out_dtype == 0)
+      go(std::true_type{});
     else
-      hipLaunchKernelGGL(combine_bf16_kernel<0>, grid, block, 0, s, yp, inv, gate, ys, yo, K, d);
-  } else
-    hipLaunchKernelGGL(combine_f32_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
-                       static_cast<const float*>(yperm), inv, gate,
-                       static_cast<const float*>(yshared), static_cast<float*>(y), K, d);
+      go(std::false_type{});
+  } else {
+    const auto* yp = static_cast<const float*>(yperm);
+    const auto* ys = static_cast<const float*>(yshared);
+    if (out_dtype == 1)
+      hipLaunchKernelGGL(combine_f32_kernel<true>, dim3(static_cast<unsigned>(T)), dim3(256), 0, s,
+                         yp, inv, gate, ys, y, K, d);
+    else
+      hipLaunchKernelGGL(combine_f32_kernel<false>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+                         s, yp, inv, gate, ys, y, K, d);
+  }
   return hipGetLastError();
 }
 

@@ -241,7 +241,7 @@ hipError_t launch_sum_groups(const float* part, int G, int64_t n, float* out, hi
 // ---- elementwise (elementwise.hip) -----------------------------------------
 hipError_t launch_combine(const void* yperm, const int32_t* inv, const float* gate,
                           const void* yshared, void* y, int64_t T, int K, int d, int io_dtype,
-                          hipStream_t s);
+                          int out_dtype, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, float gamma, float* bias, int E,
                               int64_t T, int K, hipStream_t s);
 hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, int rows,

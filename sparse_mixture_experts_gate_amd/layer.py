@@ -15,7 +15,8 @@ _W = {"f32": L.MOE_DT_F32, "bf16": L.MOE_DT_BF16, "fp8": L.MOE_DT_FP8_E4M3}
 def make_desc(wl: Workload, T: int, near_tie_eps: float = 1e-6) -> L.MoeLayerDesc:
     return L.MoeLayerDesc(T=T, d=wl.d, n_experts=wl.E, top_k=wl.K, n_groups=wl.G,
                           topk_groups=wl.M, group_topn=wl.topn, inter=wl.I, shared_inter=wl.Is,
-                          act_dtype=_ACT[wl.act], w_dtype=_W[wl.w], near_tie_eps=near_tie_eps)
+                          act_dtype=_ACT[wl.act], w_dtype=_W[wl.w], near_tie_eps=near_tie_eps,
+                          out_dtype=_ACT[wl.out_dtype])
 
 
 def quantize_fp8_blocks(w: torch.Tensor):
@@ -60,7 +61,7 @@ class MoELayer:
 
     def alloc_outputs(self, T: int) -> dict:
         wl, dev = self.wl, self.device
-        ydt = torch.float32 if wl.act == "f32" else torch.bfloat16
+        ydt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
         return {"y": torch.empty(T, wl.d, dtype=ydt, device=dev),
                 "topk_idx": torch.empty(T, wl.K, dtype=torch.int32, device=dev),
                 "topk_gate": torch.empty(T, wl.K, dtype=torch.float32, device=dev),
@@ -104,7 +105,8 @@ class MoELayer:
         """y [T, d] and the tensors the backward needs (moe_forward_train)."""
         T = x.shape[0]
         saved = self.alloc_saved(T) if saved is None else saved
-        y = torch.empty(T, self.wl.d, dtype=torch.bfloat16, device=self.device)
+        ydt = torch.float32 if self.wl.out_dtype == "f32" else torch.bfloat16
+        y = torch.empty(T, self.wl.d, dtype=ydt, device=self.device)
         near_tie = torch.empty(1, dtype=torch.int32, device=self.device)
         L.moe_forward_train(self.desc(T), x, self.w_router, self.bias, self.weights, y,
                             L.make_saved(**saved), near_tie, self.workspace(T), stream)

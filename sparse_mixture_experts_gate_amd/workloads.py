@@ -45,9 +45,14 @@ class Workload:
     seed: int = 0
     x_seed: int | None = None
     gamma: float = 0.001
+    out: str | None = None     # dtype of y: "f32" | "bf16"; None = act
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
+
+    @property
+    def out_dtype(self) -> str:
+        return self.out or self.act
 
     @property
     def flops_per_token(self) -> float:

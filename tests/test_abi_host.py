@@ -39,14 +39,14 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert L.lib().moe_status_string(4) == b"workspace too small"
 
 
 def _desc(L, **kw):
     base = dict(T=64, d=256, n_experts=16, top_k=2, n_groups=1, topk_groups=1, group_topn=2,
                 inter=128, shared_inter=128, act_dtype=L.MOE_DT_BF16, w_dtype=L.MOE_DT_BF16,
-                near_tie_eps=1e-6)
+                near_tie_eps=1e-6, out_dtype=L.MOE_DT_BF16)
     base.update(kw)
     return L.MoeLayerDesc(**base)
 
@@ -58,6 +58,7 @@ def _desc(L, **kw):
     (dict(n_groups=4, topk_groups=2, group_topn=5), 1), (dict(inter=0), 1),
     (dict(shared_inter=-1), 1), (dict(act_dtype=0), 2), (dict(w_dtype=2, d=192), 2),
     (dict(d=200), 2), (dict(inter=96), 2), (dict(near_tie_eps=float("nan")), 1),
+    (dict(out_dtype=2), 2), (dict(out_dtype=-1), 2),
     # 32-bit byte-offset limits: x, H's FP8 scales, one expert's weights, the
     # split router weights
     (dict(T=1 << 22), 2),

@@ -209,6 +209,50 @@ def test_forward_parity(name, nrows):
     assert err <= TOL[wl.w]
 
 
+@pytest.mark.parametrize("name,out", [("small_bf16", "f32"), ("tiny_f32", "bf16"),
+                                      ("small_fp8", "f32")])
+def test_output_dtype(name, out):
+    """out_dtype: the combine's fp32 sum stored as is (fp32) or rounded once
+    (bf16). The two outputs of one layer agree bit for bit after that rounding,
+    and the fp32 output of a bf16 layer is within the bound of the oracle's
+    fp64 result without the final rounding."""
+    wl = (CONFIGS["small_bf16"].with_(name="small_fp8", w="fp8") if name == "small_fp8"
+          else CONFIGS[name]).with_(T=777)
+    _log(f"output dtype {out} on {wl.name}")
+    P = make_inputs(wl, DEV)
+    base = forward(M.MoELayer(wl, P), P["x"])
+    other = forward(M.MoELayer(wl.with_(out=out), P), P["x"])
+    torch.cuda.synchronize()
+    want = torch.float32 if out == "f32" else torch.bfloat16
+    assert other["y"].dtype == want
+    assert torch.equal(other["topk_idx"], base["topk_idx"])
+    if out == "f32":
+        assert torch.equal(other["y"].to(torch.bfloat16), base["y"])
+        rr = O.route(host(other["logits"]), host(P["bias"]), **route_args(wl))
+        rows = np.arange(0, wl.T, 7)
+        if wl.w == "fp8":
+            ref = O.layer_output_fp8(host(P["x"])[rows], rr.idx[rows], rr.gate[rows],
+                                     *_fp8_weights(P, rr.idx[rows]))
+        else:
+            ref = oracle_rows(wl, P, rows, rr.idx, rr.gate)
+        err = row_rel_err(host(other["y"])[rows], ref)
+        _log(f"  fp32 output vs the oracle: {err:.2e}")
+        assert err <= TOL[wl.w]
+    else:
+        assert torch.equal(base["y"].to(torch.bfloat16), other["y"])
+
+
+def _fp8_weights(P, idx):
+    """The oracle's own 128x128 E4M3 quantization of the experts in idx and
+    of the shared expert, as layer_output_fp8 takes them (dicts by expert)."""
+    need = sorted({int(e) for e in np.unique(idx)})
+    q13 = {e: O.quantize_blocks_128(host(P["w13"][e])) for e in need}
+    q2 = {e: O.quantize_blocks_128(host(P["w2"][e])) for e in need}
+    return ({e: q13[e][0] for e in need}, {e: q13[e][1] for e in need},
+            {e: q2[e][0] for e in need}, {e: q2[e][1] for e in need},
+            *O.quantize_blocks_128(host(P["ws13"])), *O.quantize_blocks_128(host(P["ws2"])))
+
+
 def test_staged_entry_points_match_fused_forward():
     """moe_gate -> moe_permute (x_perm) -> moe_expert_ffn -> moe_combine gives the
     fused forward's output bit for bit; the gather-in-GEMM path and the
