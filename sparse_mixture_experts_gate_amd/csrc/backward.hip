@@ -451,7 +451,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
   // product, so one register across the wave stores two 128-byte row pieces.
   // Buffer stores with out-of-range offsets for the masked entries: every
   // call issues exactly MI * NJ * 16 stores (no branch can skip one), which
-  // lets them drain during the next tile's first step.
+  // lets them drain during the next tile's first step. Non-temporal: the call
+  // does not read these outputs again (backward 24.2 -> 23.7 ms at V3 shape).
   auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const Coord c = coord(tile);
     float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
@@ -469,7 +470,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
           const uint32_t off = (m < c.M && n < c.N)
                                    ? (static_cast<uint32_t>(m) * c.N + n) * 4u
                                    : kInvalidRow;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][nj][r]), ro, off, 0,
+                                                kNonTemporal);
         }
       }
     }

@@ -32,7 +32,6 @@ namespace dsmoe {
 namespace {
 
 constexpr int kE4M3 = 0, kE5M2 = 1;
-constexpr int kNonTemporal = 2;  // cache-policy bit of buffer stores (nt)
 
 using T8Bwd = Tile8<128, 256, 64, 64>;  // 8 waves of 64 x 64, 144 KB ring
 

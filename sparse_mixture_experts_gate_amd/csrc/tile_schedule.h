@@ -80,6 +80,9 @@ __device__ __forceinline__ void vm_wait() {
 // byte offset; offsets at or beyond the resource size read as zeros in
 // hardware, which is how padding rows are handled without branches.
 constexpr uint32_t kInvalidRow = 0x80000000u;
+// Cache-policy bit of buffer stores: non-temporal, for outputs that no kernel
+// of the call reads back soon (the fp32 weight gradients).
+constexpr int kNonTemporal = 2;
 
 // Raw buffer descriptor as four scalar words: base address, no stride,
 // `bytes` records (range-checked: offsets at or beyond it read as zeros).
