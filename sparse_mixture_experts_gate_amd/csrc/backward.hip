@@ -451,8 +451,9 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
   // product, so one register across the wave stores two 128-byte row pieces.
   // Buffer stores with out-of-range offsets for the masked entries: every
   // call issues exactly MI * NJ * 16 stores (no branch can skip one), which
-  // lets them drain during the next tile's first step. Non-temporal: the call
-  // does not read these outputs again (backward 24.2 -> 23.7 ms at V3 shape).
+  // with three stages lets them drain during the next tile's first step.
+  // Non-temporal: the call does not read these outputs again (backward 24.2
+  // -> 23.7 ms at V3 shape).
   auto epilogue = [&](int tile, f32x16_t (&acc)[C::MI][C::NJ]) {
     const Coord c = coord(tile);
     float* out = c.g < w.E ? w.out + static_cast<int64_t>(c.g) * w.M * w.N : w.out_s;
@@ -477,7 +478,8 @@ __global__ __launch_bounds__(C::NT, C::MINW) void wgrad_bf16_kernel(WgradArgs w)
     }
   };
   constexpr int kStores = C::MI * C::NJ * 16;
-  constexpr int kPost = kInflight<C> + kStores < 63 ? kInflight<C> + kStores : 63;
+  constexpr int kPost =
+      C::NST < 3 ? -1 : kInflight<C> + kStores < 63 ? kInflight<C> + kStores : 63;
   gemm_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, false, kPost,
               true, true>(lds, first, nb, total, next_ops, nk_of, epilogue);
 }
@@ -546,8 +548,15 @@ hipError_t launch_dgrad1_bf16(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Weight-gradient tiles of 256 x 256 (8 waves of 64 x 128) with a two-stage
+// ring (128 KB; three stages would need 192 KB): each CU moves its loads and
+// its fp32 stores through one memory pipeline, and this tile loads a third
+// fewer bytes per output than 128 x 256 (backward 23.5-24.0 -> 22.8-23.2 ms
+// at V3 shape, same results bit for bit).
+using TileWgrad = Tile<256, 256, 64, 128, 2>;
+
 hipError_t launch_wgrad_bf16(const WgradArgs& w, hipStream_t s) {
-  using C = TilePrefill;
+  using C = TileWgrad;
   static int occ = 0;
   if (!occ) occ = occupancy_of(wgrad_bf16_kernel<C>, C::NT);
   const int g = ((device_cu_count() * occ + 7) / 8) * 8;

@@ -33,7 +33,7 @@ struct Tile {
   // waves per SIMD the register budget is sized for
   static constexpr int MINW = (WM * WN >= 64 * 128) ? 1 : 2;
   static constexpr int LDS_ELEMS = NST * STAGE;
-  static_assert(NST >= 3, "loads run at least two steps ahead");
+  static_assert(NST >= 2, "loads run at least one step ahead");
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must cover the load passes");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA sub-tiles");
 };
@@ -231,6 +231,9 @@ __device__ __forceinline__ void gemm_stream(uint16_t* lds, int first, int nb, in
   constexpr int INFLIGHT = kInflight<C>;
   static_assert(INFLIGHT <= 63, "vmcnt range");
   static_assert(BK / 16 == 4, "four MFMA sub-steps per k-step");
+  // with two stages the next tile's first waited stage is loaded after the
+  // epilogue's stores, so they cannot drain past that wait
+  static_assert(POST < 0 || NST >= 3, "POST needs loads two steps ahead");
   const uint32_t lds0 = lds_addr(lds);
 
   // issue side
