@@ -458,15 +458,6 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s,
   return launch_ffn_bf16_cfg<TilePrefill, TilePrefill, false>(a, s, mid);
 }
 
-hipError_t launch_gemm2_bf16(const FfnArgs& a, hipStream_t s) {
-  using C = TilePrefill;
-  static int occ = 0;
-  if (!occ) occ = occupancy_blocks(ffn2_bf16_kernel<C>, C::NT);
-  const int g = ((device_cu_count() * occ + 7) / 8) * 8;
-  hipLaunchKernelGGL((ffn2_bf16_kernel<C>), dim3(g), dim3(C::NT), 0, s, a);
-  return hipGetLastError();
-}
-
 int router_splits(int64_t T, int d, int E, int act_dtype) {
   if (act_dtype != 1) return 1;
   // enough workgroups to cover the chip; each split a multiple of 64 in k

@@ -99,10 +99,6 @@ GemmTiling choose_tiling_fp8(double rows_per_expert);
 // `mid` (may be NULL) is recorded between the gate/up and the down GEMM.
 hipError_t launch_ffn_bf16(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s, hipEvent_t mid);
-// The down-projection kernel alone with 128 x 256 tiles over a.tiles2:
-// per group, rows of a.H [.., ldh] (K = a.I, or a.Is for the shared group)
-// times the group's [d, K] weight a.w2 (a.ws2) -> a.yperm / a.yshared.
-hipError_t launch_gemm2_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnArgs& a, const GemmTiling& t, hipStream_t s, hipEvent_t mid);
 
 // ---- backward (backward.hip), bf16 activations and weights ------------------
