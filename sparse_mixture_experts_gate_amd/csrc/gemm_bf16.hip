@@ -439,6 +439,7 @@ GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype) {
   GemmTiling t{};
   const double rows_per_expert = static_cast<double>(T) * K / E;
   if (w_dtype == 2) return choose_tiling_fp8(rows_per_expert);
+  if (w_dtype == 0) return tiling_f32();
   if (rows_per_expert < 48.0) {
     t.bm1 = TileDecode::BM; t.bnh1 = TileDecode::BN / 2;
     t.bm2 = TileDecode::BM; t.bn2 = TileDecode::BN; t.variant = 1;

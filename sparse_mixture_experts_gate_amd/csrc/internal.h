@@ -94,6 +94,8 @@ struct GemmTiling {
 };
 
 GemmTiling choose_tiling(int64_t T, int K, int E, int w_dtype);
+// fp32 tiles (gemm_f32.hip): 32 rows, 32 H columns / 64 output columns.
+GemmTiling tiling_f32();
 // FP8 tiles (gemm_fp8.hip), by the mean number of rows per expert.
 GemmTiling choose_tiling_fp8(double rows_per_expert);
 // `mid` (may be NULL) is recorded between the gate/up and the down GEMM.

@@ -303,6 +303,8 @@ def test_forward_deterministic():
     (1, 128, 12, 3, 64, 64, 1, 1, "bf16"), (3, 192, 12, 3, 192, 0, 1, 1, "bf16"),
     (129, 256, 16, 4, 320, 128, 4, 2, "bf16"), (200, 128, 8, 8, 64, 64, 1, 1, "bf16"),
     (37, 128, 10, 2, 64, 0, 1, 1, "f32"), (300, 320, 24, 5, 448, 192, 6, 3, "bf16"),
+    (1, 128, 12, 3, 64, 64, 1, 1, "f32"), (129, 256, 16, 4, 320, 128, 4, 2, "f32"),
+    (300, 320, 24, 5, 448, 192, 6, 3, "f32"),
 ])
 def test_forward_ragged_shapes(T, d, E, K, I, Is, G, Mg, act):
     wl = Workload("ragged", T=T, d=d, E=E, K=K, I=I, Is=Is, G=G, M=Mg, topn=1, act=act, w=act,
