@@ -232,7 +232,7 @@ moe_status deepseek_moe_forward(const moe_layer_desc* desc, const void* x,
  *   - A call whose workspace (moe_workspace_size) exceeds the array returns
  *     MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (at the V3 shape,
  *     d = 7168 and 256 experts of 2048 plus a shared one, calls of up to 532
- *     tokens fit with bf16 weights and up to 557 with FP8 weights).
+ *     tokens fit with bf16 weights and up to 552 with FP8 weights).
  *   - Every call on one GPU uses the same array: calls on one GPU that
  *     overlap in time (e.g. on different streams without ordering between
  *     them) race and must be serialized by the caller. Nothing in the array

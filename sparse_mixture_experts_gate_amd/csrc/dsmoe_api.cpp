@@ -147,7 +147,7 @@ GateLayout gate_layout(const moe_layer_desc* d) {
 struct FfnLayout {
   GemmTiling tiling;
   int ldh;
-  size_t tiles1, tiles2, xq, xs, H, Hs, bytes;
+  size_t tiles1, tiles2, xq, xs, xsT, H, Hs, bytes;
 };
 
 FfnLayout ffn_layout(const moe_layer_desc* d) {
@@ -163,6 +163,7 @@ FfnLayout ffn_layout(const moe_layer_desc* d) {
   L.xq = c.take(fp8 ? size_t(T) * d->d : 0);
   L.xs = c.take(fp8 ? sizeof(float) * size_t(T) * (d->d / 128) : 0);
   const int64_t hrows = TK + (d->shared_inter > 0 ? T : 0);
+  L.xsT = c.take(fp8 ? sizeof(float) * size_t(hrows) * (d->d / 128) : 0);
   L.Hs = c.take(fp8 ? sizeof(float) * size_t(hrows) * (L.ldh / 128) : 0);
   L.H = c.take(size_t(hrows) * L.ldh * h_bytes(d));
   L.bytes = c.off;
@@ -345,6 +346,7 @@ moe_status run_ffn(const moe_layer_desc* d, const moe_weights* w, const void* x,
   a.H = (h_out && !fp8w) ? h_out : at<void>(ws, L.H);
   a.h16 = fp8w ? h_out : nullptr;
   a.H_scale = at<float>(ws, L.Hs);
+  a.xsT = at<float>(ws, L.xsT);
   a.gu = gu_out;
   a.yperm = y_perm;
   a.yshared = y_shared;

@@ -62,16 +62,14 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
   const int first = xcd_logical_block(blockIdx.x, nb);
   if (first >= total) return;
   const int dkb = a.d / 128;
-  const int hkb = a.ldh / 128;
-  const float* XS = a.perm ? a.x_scale : a.xperm_scale;
   const i32x4_t rxs = rsrc4(a.x, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(a.d));
   const i32x4_t rx =
       a.perm ? rxs : rsrc4(a.xperm, static_cast<uint32_t>(a.TK) * static_cast<uint32_t>(a.d));
-  // activation scales: gathered rows (or x_perm rows) and the shared rows
-  const i32x4_t rsxp =
-      rsrc4(XS, static_cast<uint32_t>(a.perm ? a.T : a.TK) * static_cast<uint32_t>(dkb) * 4u);
+  // activation scales, k-block major (scale_rows_kernel): the routed rows in
+  // the permuted order, then the shared rows
+  const int64_t srows = a.TK + (a.Is > 0 ? a.T : 0);
   const i32x4_t rsx =
-      rsrc4(a.x_scale, static_cast<uint32_t>(a.T) * static_cast<uint32_t>(dkb) * 4u);
+      rsrc4(a.xsT, static_cast<uint32_t>(srows) * static_cast<uint32_t>(dkb) * 4u);
   const i32x4_t rperm = rsrc4(a.perm, static_cast<uint32_t>(a.TK) * 4u);
   const int nk = a.d / BK8;
   uint8_t* H = static_cast<uint8_t*>(a.H);
@@ -122,12 +120,13 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       op.ao[p] = row >= 0 ? static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) : kInvalidRow;
     }
     op.sa_off = kInvalidRow;
-    if (tid < C::BM) {
-      const int row = src_row(tid);
-      if (row >= 0) op.sa_off = static_cast<uint32_t>(row * dkb) * 4u;
+    if (tid < C::BM && src_row(tid) >= 0) {
+      const int gr = c.m * C::BM + tid;
+      op.sa_off = static_cast<uint32_t>(c.shared ? a.TK + gr : c.rbase + gr) * 4u;
     }
+    op.sa_step = static_cast<uint32_t>(srows) * 4u;
     op.ra = c.shared ? rxs : rx;
-    op.rsa = c.shared ? rsx : rsxp;
+    op.rsa = rsx;
     const uint8_t* W = c.shared ? static_cast<const uint8_t*>(a.ws13)
                                 : static_cast<const uint8_t*>(a.w13) +
                                       static_cast<int64_t>(c.g) * 2 * a.I * a.d;
@@ -191,7 +190,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
               amax == 0.0f ? 0u : e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
         }
       if (wn == 0 && lane < 32)
-        a.H_scale[(hrow0 + lr) * hkb + c.n] = amax == 0.0f ? 1.0f : amax / 448.0f;
+        a.H_scale[c.n * srows + hrow0 + lr] = amax == 0.0f ? 1.0f : amax / 448.0f;
       if constexpr (TRAIN) {
         const int Ig = c.shared ? a.Is : a.I;
         const int64_t hr = hrow0 + lr;
@@ -262,8 +261,9 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
     op.ra = rsrc4(static_cast<const uint8_t*>(a.H) + hrow0 * a.ldh,
                   static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) *
                       static_cast<uint32_t>(a.ldh));
-    op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>((hrow0 + tid) * hkb) * 4u
+    op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>(hrow0 + tid) * 4u
                                                  : kInvalidRow;
+    op.sa_step = static_cast<uint32_t>(hrows) * 4u;
     op.rsa = rsh;
     const uint8_t* W = c.shared ? static_cast<const uint8_t*>(a.ws2)
                                 : static_cast<const uint8_t*>(a.w2) +
@@ -320,6 +320,30 @@ int occupancy8(K kernel, int threads) {
   return nb;
 }
 
+// The activation scales in the layout the gate/up GEMM reads: k-block major,
+// the routed rows in the permuted order (each from its token's row of
+// x_scale, or from the scales of x_perm), then the shared rows, so that a
+// tile's row scales of one k block are one contiguous run of 4-byte values
+// instead of one cache line per row.
+__global__ __launch_bounds__(256) void scale_rows_kernel(FfnArgs a, int dkb, int64_t srows) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= srows * dkb) return;
+  const int kb = static_cast<int>(i / srows);
+  const int64_t r = i - kb * srows;
+  float v = 0.0f;
+  if (r < a.TK) {
+    if (a.perm) {
+      const int tok = a.perm[r];
+      if (tok >= 0 && tok < a.T) v = a.x_scale[static_cast<int64_t>(tok) * dkb + kb];
+    } else {
+      v = a.xperm_scale[r * dkb + kb];
+    }
+  } else {
+    v = a.x_scale[(r - a.TK) * dkb + kb];
+  }
+  a.xsT[i] = v;
+}
+
 template <class C1, class C2, bool TRAIN>
 hipError_t launch_fp8_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   static int occ1 = 0, occ2 = 0;
@@ -328,6 +352,14 @@ hipError_t launch_fp8_pair(const FfnArgs& a, hipStream_t s, hipEvent_t mid) {
   const int cus = device_cu_count();
   const int g1 = ((cus * occ1 + 7) / 8) * 8;
   const int g2 = ((cus * occ2 + 7) / 8) * 8;
+  const int dkb = a.d / 128;
+  const int64_t srows = a.TK + (a.Is > 0 ? a.T : 0);
+  if (srows > 0) {
+    hipLaunchKernelGGL(scale_rows_kernel, dim3(static_cast<unsigned>((srows * dkb + 255) / 256)),
+                       dim3(256), 0, s, a, dkb, srows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((ffn1_fp8_kernel<C1, TRAIN>), dim3(g1), dim3(C1::NT), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -88,6 +88,10 @@ struct StreamOps8 {
   uint32_t ao[C::A_LOADS], bo[C::B_LOADS];
   uint32_t sa_off, sb_lo, sb_hi;
   uint32_t sb_off;  // row scales for B (SBROW): this thread's B row
+  // bytes between the A row scales of consecutive k blocks: 4 for scales
+  // stored row-major, the row count for k-block-major scales (a tile's row
+  // scales of one k block are then contiguous)
+  uint32_t sa_step = 4;
   int nk;
 };
 
@@ -126,7 +130,8 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
       dma16(op.rb, op.bo[p] + off, b_base + p * C::RPP * BK8);
   }
   const uint32_t kb4 = static_cast<uint32_t>(kb) * 4u;
-  dma4(op.rsa, op.sa_off + kb4, __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
+  dma4(op.rsa, op.sa_off + static_cast<uint32_t>(kb) * op.sa_step,
+       __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
   if constexpr (SBROW) {
     dma4(op.rsb, op.sb_off + kb4,
          __builtin_amdgcn_readfirstlane(sb0 + (st * C::NT + wave * 64) * 4));

@@ -71,12 +71,14 @@ struct FfnArgs {
   const int32_t* perm;     // gather rows of x for routed groups (NULL -> xperm)
   const void* xperm;       // [TK, d] contiguous routed rows (used when perm == NULL)
   const float* xperm_scale;
+  float* xsT;              // fp8: activation scales [d/128, TK + T], k-block major: the
+                           // routed rows in the permuted order, then the shared rows
   const void* w13;
   const void* ws13;
   const float* w13_scale;
   const float* ws13_scale;
   void* H;                 // [TK + T, ldh]
-  float* H_scale;          // fp8: [TK + T, ldh/128]
+  float* H_scale;          // fp8: [ldh/128, TK + T], k-block major
   void* gu;                // training forward: pre-activations [TK + T, 2 ldh] bf16, or NULL
   void* h16;               // FP8 training forward: H [TK + T, ldh] in bf16, or NULL
   // GEMM2
