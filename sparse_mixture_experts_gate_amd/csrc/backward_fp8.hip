@@ -74,7 +74,8 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
   const int first = xcd_logical_block(blockIdx.x, nb);
   if (first >= total) return;
   const int dkb = a.d / 128;
-  const int gkb = 2 * a.ldh / 128;
+  // rows of [da | db] (routed, then shared): the stride of its k-block-major scales
+  const int64_t hrows = a.TK + (a.Is > 0 ? a.T : 0);
   const uint32_t d = static_cast<uint32_t>(a.d);
   const i32x4_t rsyr = rsrc4(a.dys, static_cast<uint32_t>(a.TK) * dkb * 4u);
   const i32x4_t rsys = rsrc4(a.dyss, static_cast<uint32_t>(a.T) * dkb * 4u);
@@ -92,9 +93,9 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
       const int lr = r0 + p * C::RPP;
       op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * d : kInvalidRow;
     }
-    op.sa_off = (tid < C::BM && tid < rows_left)
-                    ? static_cast<uint32_t>((row0 + tid) * dkb) * 4u
-                    : kInvalidRow;
+    op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>(row0 + tid) * 4u
+                                                 : kInvalidRow;
+    op.sa_step = static_cast<uint32_t>(c.shared ? a.T : a.TK) * 4u;  // k-block-major scales
     op.ra = rsrc4((c.shared ? a.dysq : a.dyq) + row0 * a.d,
                   static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * d);
     op.rsa = c.shared ? rsys : rsyr;
@@ -194,7 +195,8 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
           }
         const int cgrp = c.n * C::BN + w0 * C::WN;  // first column of the wave pair's group
         if (wn == w0 && lane < 32 && cgrp < Ig)
-          a.dgs[hrow * gkb + (cbase + cgrp) / 128] = am == 0.0f ? 1.0f : am / 57344.0f;
+          a.dgs[static_cast<int64_t>((cbase + cgrp) / 128) * hrows + hrow] =
+              am == 0.0f ? 1.0f : am / 57344.0f;
       }
     }
     // red[] is rewritten by the next tile's epilogue only after at least one
@@ -241,9 +243,9 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
       const int lr = r0 + p * C::RPP;
       op.ao[p] = lr < rows_left ? static_cast<uint32_t>(lr) * lrow : kInvalidRow;
     }
-    op.sa_off = (tid < C::BM && tid < rows_left)
-                    ? static_cast<uint32_t>((hrow0 + tid) * gkb) * 4u
-                    : kInvalidRow;
+    op.sa_off = (tid < C::BM && tid < rows_left) ? static_cast<uint32_t>(hrow0 + tid) * 4u
+                                                 : kInvalidRow;
+    op.sa_step = static_cast<uint32_t>(hrows) * 4u;  // k-block-major scales
     op.ra = rsrc4(a.dgq + hrow0 * lrow,
                   static_cast<uint32_t>(rows_left < C::BM ? rows_left : C::BM) * lrow);
     op.rsa = rsg;

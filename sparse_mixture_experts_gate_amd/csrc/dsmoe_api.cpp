@@ -1211,11 +1211,11 @@ moe_status moe_backward_fp8(const moe_layer_desc* desc, const void* x, const flo
   b.dysq = shared ? at<uint8_t>(ws, L.dysq) : nullptr;
   b.dyss = shared ? at<float>(ws, L.dyss) : nullptr;
   HIP_TRY(launch_quant_rows(dyp, MOE_DT_BF16, nullptr, TK, d, at<uint8_t>(ws, L.dyq),
-                            at<float>(ws, L.dys), stream, 1),
+                            at<float>(ws, L.dys), stream, 1, true),
           "quantize gated output gradients");
   if (shared)
     HIP_TRY(launch_quant_rows(dy, MOE_DT_BF16, nullptr, T, d, at<uint8_t>(ws, L.dysq),
-                              at<float>(ws, L.dyss), stream, 1),
+                              at<float>(ws, L.dyss), stream, 1, true),
             "quantize output gradient");
   b.w2t = static_cast<const uint8_t*>(wt->w2);
   b.w2t_scale = wt->w2_scale;

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
                                                          const int32_t* __restrict__ perm,
                                                          int64_t n, int cols,
                                                          uint8_t* __restrict__ q,
-                                                         float* __restrict__ scale) {
+                                                         float* __restrict__ scale, bool kmajor) {
   const int l16 = threadIdx.x & 15;
   const int64_t tile = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int tpr = cols / 128;
@@ -216,9 +216,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   float v[8];
   float amax = 0.0f;
   int64_t base = 0;
+  int64_t row = 0;
+  int tc = 0;
   if (valid) {
-    const int64_t row = tile / tpr;
-    const int tc = static_cast<int>(tile % tpr);
+    row = tile / tpr;
+    tc = static_cast<int>(tile % tpr);
     const int64_t srow = perm ? static_cast<int64_t>(perm[row]) : row;
     base = row * cols + tc * 128 + l16 * 8;
     load8(src, dtype, srow * cols + tc * 128 + l16 * 8, v);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   float inv, sc;
   quant_params<FMT>(amax, inv, sc);
   *reinterpret_cast<uint2*>(q + base) = encode8<FMT>(v, amax, inv);
-  if (l16 == 0) scale[tile] = sc;
+  if (l16 == 0) scale[kmajor ? tc * n + row : tile] = sc;
 }
 
 }  // namespace
@@ -292,16 +294,17 @@ hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, i
 }
 
 hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm, int64_t n,
-                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt) {
+                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt,
+                             bool kmajor) {
   const int64_t tiles = n * (cols / 128);
   if (tiles == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((tiles + 15) / 16)), block(256);
   if (fmt == 1)
     hipLaunchKernelGGL(quant_rows_kernel<1>, grid, block, 0, s, src, src_dtype, perm, n, cols, q,
-                       scale);
+                       scale, kmajor);
   else
     hipLaunchKernelGGL(quant_rows_kernel<0>, grid, block, 0, s, src, src_dtype, perm, n, cols, q,
-                       scale);
+                       scale, kmajor);
   return hipGetLastError();
 }
 

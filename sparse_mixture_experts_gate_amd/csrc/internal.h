@@ -160,6 +160,7 @@ struct BwdFp8Args {
   int64_t T, TK;
   int E, d, I, Is, ldh;
   const uint8_t* dyq;         // [TK, d] E5M2 gated output gradients, 1x128 scales dys
+                              // (dys, dyss, dgs: k-block major, [blocks, rows])
   const float* dys;
   const uint8_t* dysq;        // [T, d] E5M2 output gradient (shared rows), scales dyss
   const float* dyss;
@@ -247,9 +248,12 @@ hipError_t launch_bias_update(const int32_t* counts, float gamma, float* bias, i
 hipError_t launch_quant_blocks(const void* src, int src_dtype, int64_t n_mats, int rows,
                                int cols, uint8_t* q, float* scale, hipStream_t s);
 // Row i of the output quantizes source row perm[i] (perm == NULL: row i);
-// fmt 0 = E4M3, 1 = E5M2.
+// fmt 0 = E4M3, 1 = E5M2. Scales row-major [n, cols/128], or with kmajor
+// k-block major [cols/128, n] (what the FP8 GEMMs read: a tile's row scales
+// of one k block contiguous).
 hipError_t launch_quant_rows(const void* src, int src_dtype, const int32_t* perm, int64_t n,
-                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt = 0);
+                             int cols, uint8_t* q, float* scale, hipStream_t s, int fmt = 0,
+                             bool kmajor = false);
 
 // number of compute units of the current device (cached per device)
 int device_cu_count();
