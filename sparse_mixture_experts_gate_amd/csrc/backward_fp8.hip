@@ -380,10 +380,10 @@ __global__ __launch_bounds__(C::NT, 2) void wgrad_fp8_kernel(WgradFp8Args w) {
       op.bo[p] = row < c.N ? static_cast<uint32_t>(row) * npad : kInvalidRow;
     }
     const int ra_row = c.mt * C::BM + tid, rb_row = c.nt * C::BN + tid;
-    op.sa_off = (tid < C::BM && ra_row < c.M) ? static_cast<uint32_t>(ra_row * c.mtg) * 4u
-                                              : kInvalidRow;
-    op.sb_off = (tid < C::BN && rb_row < c.N) ? static_cast<uint32_t>(rb_row * c.mtg) * 4u
-                                              : kInvalidRow;
+    op.sa_off = (tid < C::BM && ra_row < c.M) ? static_cast<uint32_t>(ra_row) * 4u : kInvalidRow;
+    op.sb_off = (tid < C::BN && rb_row < c.N) ? static_cast<uint32_t>(rb_row) * 4u : kInvalidRow;
+    op.sa_step = static_cast<uint32_t>(c.M) * 4u;  // k-block-major scales
+    op.sb_step = static_cast<uint32_t>(c.N) * 4u;
     op.sb_lo = op.sb_hi = 0;
     swizzle_rows8<C>(op.ao);
     swizzle_rows8<C>(op.bo);
@@ -515,7 +515,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantColsArgs q) {
   uint8_t* dst = q.q + cb + static_cast<int64_t>(c0 + ch) * npad + blk * 128 + 32 * s;
   reinterpret_cast<uint4*>(dst)[0] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   reinterpret_cast<uint4*>(dst)[1] = make_uint4(w4[4], w4[5], w4[6], w4[7]);
-  if (s == 0) q.scale[sbase + static_cast<int64_t>(c0 + ch) * mtg + blk] =
+  // scales k-block major inside the group ([blocks, channels]): a tile's
+  // channel scales of one token block are one contiguous run
+  if (s == 0) q.scale[sbase + static_cast<int64_t>(blk) * C + c0 + ch] =
       amax == 0.0f ? 1.0f : amax / Fp8Fmt<FMT>::kMax;
 }
 

@@ -92,6 +92,7 @@ struct StreamOps8 {
   // stored row-major, the row count for k-block-major scales (a tile's row
   // scales of one k block are then contiguous)
   uint32_t sa_step = 4;
+  uint32_t sb_step = 4;  // the same for the B row scales (SBROW)
   int nk;
 };
 
@@ -133,7 +134,7 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
   dma4(op.rsa, op.sa_off + static_cast<uint32_t>(kb) * op.sa_step,
        __builtin_amdgcn_readfirstlane(sa0 + (st * C::NT + wave * 64) * 4));
   if constexpr (SBROW) {
-    dma4(op.rsb, op.sb_off + kb4,
+    dma4(op.rsb, op.sb_off + static_cast<uint32_t>(kb) * op.sb_step,
          __builtin_amdgcn_readfirstlane(sb0 + (st * C::NT + wave * 64) * 4));
   } else {
     const uint32_t sb_base =
