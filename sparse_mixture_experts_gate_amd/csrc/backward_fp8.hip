@@ -67,6 +67,8 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // the wave (row 0 of the wave grid) that loads this wave's weight block scale
+  const int sbw = (wn / (128 / C::WN)) * (128 / C::WN);
   const int r0 = tid >> 3;
   load_group_tables(gt, a.tiles_h, a.offsets, a.E);
   const int total = gt.total;
@@ -109,7 +111,9 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
       op.bo[p] = row < Ig ? static_cast<uint32_t>(row) * d : kInvalidRow;
     }
     op.rsb = rsrc4(WS, static_cast<uint32_t>(Ig / 128) * dkb * 4u);
-    op.sb_lo = op.sb_hi = static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * dkb) * 4u;
+    op.sb_lo = op.sb_hi =
+        wave == sbw ? static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * dkb) * 4u
+                    : kInvalidRow;
     swizzle_rows8<C>(op.ao);
     swizzle_rows8<C>(op.bo);
     op.nk = nk;
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad2_fp8_kernel(BwdFp8Args a) {
     // more k block, whose barrier orders these reads first
   };
   gemm8_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, kE4M3,
-               kE5M2>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
+               kE5M2>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue, sbw);
 }
 
 // ---- dA = E5M2([da | db]) [W1; W3] --------------------------------------------
@@ -220,6 +224,8 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // the wave (row 0 of the wave grid) that loads this wave's weight block scale
+  const int sbw = (wn / (128 / C::WN)) * (128 / C::WN);
   const int r0 = tid >> 3;
   load_group_tables(gt, a.tiles_d, a.offsets, a.E);
   const int total = gt.total;
@@ -262,7 +268,9 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
                            : kInvalidRow;
     }
     op.rsb = rsrc4(WS, static_cast<uint32_t>(a.d / 128) * kb * 4u);
-    op.sb_lo = op.sb_hi = static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * kb) * 4u;
+    op.sb_lo = op.sb_hi =
+        wave == sbw ? static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * kb) * 4u
+                    : kInvalidRow;
     swizzle_rows8<C>(op.ao);
     swizzle_rows8<C>(op.bo);
     op.nk = kb;
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(C::NT, 2) void dgrad1_fp8_kernel(BwdFp8Args a) {
     }
   };
   gemm8_stream<C, false, decltype(next_ops)&, decltype(nk_of)&, decltype(epilogue)&, kE4M3,
-               kE5M2>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
+               kE5M2>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue, sbw);
 }
 
 // ---- weight gradients: out_g = A_g B_g^T over the group's tokens ------------

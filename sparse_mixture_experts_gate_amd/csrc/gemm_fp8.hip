@@ -141,8 +141,9 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
       op.bo[p] = static_cast<uint32_t>(up ? Ig + col : col) * static_cast<uint32_t>(a.d);
     }
     op.rsb = rsrc4(WS, static_cast<uint32_t>(2 * Ig / 128) * static_cast<uint32_t>(dkb) * 4u);
-    op.sb_lo = static_cast<uint32_t>(c.n * dkb) * 4u;
-    op.sb_hi = static_cast<uint32_t>((Ig / 128 + c.n) * dkb) * 4u;
+    // every wave of the tile needs the same two block scales: wave 0 loads them
+    op.sb_lo = wave == 0 ? static_cast<uint32_t>(c.n * dkb) * 4u : kInvalidRow;
+    op.sb_hi = wave == 0 ? static_cast<uint32_t>((Ig / 128 + c.n) * dkb) * 4u : kInvalidRow;
     swizzle_rows8<C>(op.ao);
     swizzle_rows8<C>(op.bo);
     op.nk = nk;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn1_fp8_kernel(FfnArgs a) {
     // red[] is rewritten by the next tile's epilogue only after at least one
     // more k block, whose barrier orders these reads first
   };
-  gemm8_stream<C, true>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
+  gemm8_stream<C, true>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue, 0);
 }
 
 // y = dequant(H) dequant(W2)^T per group, bf16 out, stored from registers.
@@ -229,6 +230,8 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // the wave (row 0 of the wave grid) that loads this wave's weight block scale
+  const int sbw = (wn / (128 / C::WN)) * (128 / C::WN);
   const int r0 = tid >> 3;
   load_group_tables(gt, a.tiles2, a.offsets, a.E);
   const int total = gt.total;
@@ -278,8 +281,10 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
       op.bo[p] = row < a.d ? static_cast<uint32_t>(row) * static_cast<uint32_t>(Ig) : kInvalidRow;
     }
     op.rsb = rsrc4(WS, static_cast<uint32_t>(a.d / 128) * static_cast<uint32_t>(ikb) * 4u);
+    // the first wave of each 128-column scale block loads its block scale
     op.sb_lo = op.sb_hi =
-        static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * ikb) * 4u;
+        wave == sbw ? static_cast<uint32_t>(((c.n * C::BN + wn * C::WN) / 128) * ikb) * 4u
+                    : kInvalidRow;
     swizzle_rows8<C>(op.ao);
     swizzle_rows8<C>(op.bo);
     op.nk = Ig / BK8;
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(C::NT, 2) void ffn2_fp8_kernel(FfnArgs a) {
         }
     }
   };
-  gemm8_stream<C, false>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue);
+  gemm8_stream<C, false>(lds, lds_sa, lds_sb, first, nb, total, next_ops, nk_of, epilogue, sbw);
 }
 
 template <class K>

@@ -166,13 +166,13 @@ __device__ __forceinline__ void stage8_issue(uint32_t lds0, uint32_t sa0, uint32
 // 128-byte output row pieces (full cache lines for fp32 outputs).
 template <class C, bool SWIGLU, int FW, int FA, bool SBROW, bool SWAP, class Mid>
 __device__ __forceinline__ void stage8_mma(const uint8_t* lds, const float* lds_sa,
-                                           const float* lds_sb, int st, int wave, int wm, int wn,
+                                           const float* lds_sb, int st, int sbw, int wm, int wn,
                                            int lane, f32x16_t (&acc)[C::MI][C::NJ], Mid&& mid) {
   static_assert(SWAP || SBROW, "the A-first order is built for row scales on both sides");
   const uint8_t* As = lds + st * C::STAGE;
   const uint8_t* Bs = As + C::BM * BK8;
-  const float s_lo = SBROW ? 1.0f : lds_sb[(st * C::NWAVES + wave) * 2];
-  const float s_hi = SBROW ? 1.0f : SWIGLU ? lds_sb[(st * C::NWAVES + wave) * 2 + 1] : s_lo;
+  const float s_lo = SBROW ? 1.0f : lds_sb[(st * C::NWAVES + sbw) * 2];
+  const float s_hi = SBROW ? 1.0f : SWIGLU ? lds_sb[(st * C::NWAVES + sbw) * 2 + 1] : s_lo;
   const int rl = lane & 31;
   const int ch = 2 * (lane >> 5);  // first chunk of the lane's 32-byte k group
   float sl[C::MI], sh[C::MI];
@@ -297,9 +297,13 @@ template <class C, bool SWIGLU, class NextOps, class NkOf, class Epilogue, int F
           bool SBROW = false, bool SWAP = true, int POST = -1>
 __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float* lds_sb, int first,
                                              int nb, int total, NextOps&& next_ops, NkOf&& nk_of,
-                                             Epilogue&& epilogue) {
+                                             Epilogue&& epilogue, int sb_wave = -1) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // block scales (no SBROW): the wave whose slot holds this wave's two
+  // scales (waves with the same scales let one of them load them; the
+  // others' scale loads read out of range and fetch nothing)
+  const int sbw = sb_wave < 0 ? wave : sb_wave;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   constexpr int NST = C::NST;
   constexpr int INFLIGHT = C::template NL<SBROW> * (NST - 2);
@@ -366,7 +370,7 @@ __device__ __forceinline__ void gemm8_stream(uint8_t* lds, float* lds_sa, float*
         advance();
       }
       after_epilogue = POST >= 0 && kc < 2 && tc != first;
-      stage8_mma<C, SWIGLU, FW, FA, SBROW, SWAP>(lds, lds_sa, lds_sb, st, wave, wm, wn, lane, acc,
+      stage8_mma<C, SWIGLU, FW, FA, SBROW, SWAP>(lds, lds_sa, lds_sb, st, sbw, wm, wn, lane, acc,
                                                  mid);
       st = st == NST - 1 ? 0 : st + 1;
       st_issue = st_issue == NST - 1 ? 0 : st_issue + 1;
