@@ -180,3 +180,30 @@ def test_formats_and_axes_per_operand(monkeypatch):
         ("1x128", "e5m2", (n, d)), ("1x128", "e5m2", (n, 2 * inter)),
         ("128x1", "e5m2", (n, d)), ("128x1", "e4m3", (n, inter)),
         ("128x1", "e5m2", (n, 2 * inter)), ("128x1", "e4m3", (n, d))])
+
+
+def test_input_gradient_takes_the_quantized_gate_gradients(monkeypatch):
+    """dX is the product of the E5M2 1x128 tiles of [da | db] with the
+    dequantized [W1; W3]: it is linear in that operand, so a quantizer whose
+    tiles decode to twice the values must give exactly twice dX (powers of
+    two are exact in fp64), while the other outputs stay as they were."""
+    rng = np.random.default_rng(36)
+    n, d, inter = 24, 384, 128  # d != 2I: the spy must not touch dY's tiles
+    X = rng.normal(size=(n, d)).astype(F32)
+    w13q, w13s = O.quantize_blocks_128(rng.normal(0, 0.05, (2 * inter, d)).astype(F32))
+    w2q, w2s = O.quantize_blocks_128(rng.normal(0, 0.05, (d, inter)).astype(F32))
+    dY = rng.normal(size=(n, d))
+    base = FB.fp8_expert_backward(X, w13q, w13s, w2q, w2s, dY)
+    q1 = FB.quantize_1x128
+
+    def doubled(A, fmt):
+        q, s = q1(A, fmt)
+        if np.shape(A) == (n, 2 * inter):
+            s = (np.asarray(s, F32) * F32(2.0)).astype(F32)
+        return q, s
+
+    monkeypatch.setattr(FB, "quantize_1x128", doubled)
+    dX, dW13, dW2, Y = FB.fp8_expert_backward(X, w13q, w13s, w2q, w2s, dY)
+    assert np.array_equal(dX, 2.0 * base[0])
+    assert np.array_equal(dW13, base[1]) and np.array_equal(dW2, base[2])
+    assert np.array_equal(Y, base[3])

@@ -542,3 +542,33 @@ def test_fp8_layer_threaded_experts_identical():
     args = (x, idx, g, [q[0] for q in qs], [q[1] for q in qs], [q[0] for q in q2],
             [q[1] for q in q2])
     assert np.array_equal(O.layer_output_fp8(*args), O.layer_output_fp8(*args, workers=3))
+
+
+def test_fp8_layer_experts_take_the_e4m3_activation_tiles(monkeypatch):
+    """The FP8 experts multiply the 1x128 E4M3 tiles of x, not x itself
+    [GK Q8; MH §4.1]. Row 0 has max-abs 448, so its scale is 1 and its codes
+    follow from the format alone (3 mantissa bits, exponent bias 7, steps of
+    2^-9 below 2^-6, ties to the even code): 1.0625 lies halfway between 1 and
+    1.125 and goes to 1; 3.3 goes to 3.25; -0.01 is 5.12 subnormal steps and
+    goes to -5 * 2^-9; 300 lies between 288 and 320 and goes to 288. Every
+    expert call must see exactly these values in row 0."""
+    seen = []
+    orig = O.moe_oracle._fp8_expert
+    monkeypatch.setattr(O.moe_oracle, "_fp8_expert",
+                        lambda Xd, *a: (seen.append(np.array(Xd)), orig(Xd, *a))[1])
+    rng = np.random.default_rng(41)
+    T, d, I = 3, 128, 128
+    x = rng.normal(size=(T, d)).astype(F32)
+    x[0] = 0.0
+    x[0, :5] = [448.0, 1.0625, 3.3, -0.01, 300.0]
+    want = np.zeros(d)
+    want[:5] = [448.0, 1.0, 3.25, -5 * 2.0 ** -9, 288.0]
+    w13 = O.quantize_blocks_128(rng.normal(0, 0.05, (2 * I, d)).astype(F32))
+    w2 = O.quantize_blocks_128(rng.normal(0, 0.05, (d, I)).astype(F32))
+    idx = np.zeros((T, 1), np.int32)
+    g = np.ones((T, 1), F32)
+    O.layer_output_fp8(x, idx, g, [w13[0]], [w13[1]], [w2[0]], [w2[1]],
+                       w13[0], w13[1], w2[0], w2[1])
+    assert len(seen) == 2  # the shared expert and expert 0, each on all rows
+    for Xd in seen:
+        assert np.array_equal(Xd[0], want)
