@@ -208,19 +208,32 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ pa
   if (tid == 0 && ntie && near_tie) atomicAdd(near_tie, ntie);
 }
 
-// fp32 activations: plain fp32 dot products, one thread per (token, expert).
-__global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x,
-                                                         const float* __restrict__ w, int64_t T,
-                                                         int d, int E, float* __restrict__ out) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= T * E) return;
+// fp32 activations: plain fp32 dot products, one wave per (token, expert).
+// Lane l takes the 4-element pieces l, l + 64, ... of the contraction (d is
+// a multiple of 64, rows 16-byte aligned), and a butterfly over the wave adds
+// the 64 partial sums in a fixed order.
+constexpr int kRouterF32Waves = 4;  // waves (dot products) per workgroup
+__global__ __launch_bounds__(64 * kRouterF32Waves) void router_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, int64_t T, int d, int E,
+    float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRouterF32Waves + (threadIdx.x >> 6);
+  if (i >= T * E) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
   const int64_t t = i / E;
   const int e = static_cast<int>(i % E);
-  const float* xr = x + t * d;
-  const float* wr = w + static_cast<int64_t>(e) * d;
+  const float4* xr = reinterpret_cast<const float4*>(x + t * d);
+  const float4* wr = reinterpret_cast<const float4*>(w + static_cast<int64_t>(e) * d);
   float acc = 0.0f;
-  for (int k = 0; k < d; ++k) acc = __builtin_fmaf(xr[k], wr[k], acc);
-  out[i] = acc;
+  for (int k = lane; k < d / 4; k += 64) {
+    const float4 a = xr[k], b = wr[k];
+    acc = __builtin_fmaf(a.x, b.x, acc);
+    acc = __builtin_fmaf(a.y, b.y, acc);
+    acc = __builtin_fmaf(a.z, b.z, acc);
+    acc = __builtin_fmaf(a.w, b.w, acc);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (lane == 0) out[i] = acc;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -242,8 +255,10 @@ hipError_t launch_router_f32(const float* x, const float* w, int64_t T, int d, i
                              hipStream_t s) {
   const int64_t n = T * E;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     s, x, w, T, d, E, out);
+  if (d % 64) return hipErrorInvalidValue;
+  const int64_t blocks = (n + kRouterF32Waves - 1) / kRouterF32Waves;
+  hipLaunchKernelGGL(router_f32_kernel, dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kRouterF32Waves), 0, s, x, w, T, d, E, out);
   return hipGetLastError();
 }
 
