@@ -9,6 +9,7 @@ import torch
 
 import sparse_mixture_experts_gate_amd as M
 from sparse_mixture_experts_gate_amd.workloads import CONFIGS, make_inputs, make_tokens
+from test_gpu_sweep import CASES
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -49,6 +50,21 @@ def test_noalloc_forward_matches_workspace_forward(name, T1, T2):
     _compare(layer, P["x"], name)
     x2 = make_tokens(wl, T2, 11, DEV)
     _compare(layer, x2, name)
+
+
+SWEEP = CASES[:24]
+
+
+@pytest.mark.parametrize("wl", SWEEP, ids=[w.name for w in SWEEP])
+def test_noalloc_forward_sweep(wl):
+    """The seeded small shapes of the parity sweep (fp32, bf16 and FP8 layers,
+    group limits, ragged T): two calls in a row, the second with a third of
+    the tokens, equal bit for bit to the workspace forward."""
+    print(f"noalloc sweep {wl}", flush=True)
+    P = make_inputs(wl, DEV)
+    layer = M.MoELayer(wl, P)
+    _compare(layer, P["x"], wl.name)
+    _compare(layer, P["x"][: max(1, wl.T // 3)].contiguous(), wl.name)
 
 
 def test_noalloc_forward_rejects_calls_beyond_the_scratch():
