@@ -42,6 +42,15 @@ MUTANTS = [
     ("bias_step_wrong_sign", "moe_oracle.py", "b[e] = F32(b[e] - g32)", "b[e] = F32(b[e] + g32)"),
     ("balanced_load_without_k", "moe_oracle.py", "total = int(n_tokens) * int(top_k)",
      "total = int(n_tokens)"),
+    ("near_tie_strict", "moe_oracle.py",
+     "if order.shape[0] > K and F32(ct[order[K - 1]] - ct[order[K]]) <= eps32:",
+     "if order.shape[0] > K and F32(ct[order[K - 1]] - ct[order[K]]) < F32(0.0):"),
+    ("zero_sum_gates_zero", "moe_oracle.py", "gate[t] = F32(1.0) / F32(K)",
+     "gate[t] = F32(0.0)"),
+    ("offsets_not_cumulative", "moe_oracle.py", "offsets[e + 1] = offsets[e] + counts[e]",
+     "offsets[e + 1] = counts[e]"),
+    ("router_product_in_fp16", "moe_oracle.py", "return (x64 @ w64.T).astype(F32)",
+     "return (x64 @ w64.T).astype(np.float16).astype(F32)"),
     # experts (§1.1: shared expert always on, routed experts gated)
     ("swiglu_operands_swapped", "moe_oracle.py", "return (_silu64(a) * b) @ w2.T",
      "return (a * _silu64(b)) @ w2.T"),
@@ -91,10 +100,24 @@ MUTANTS = [
     ("shared_dx_dropped", "moe_backward.py", "        dx += dXs\n", "        dx += 0.0\n"),
     ("expert_grad_ungated", "moe_backward.py", "dYe = g[rows, slots][:, None] * dy[rows]",
      "dYe = dy[rows]"),
+    ("dw2_without_silu", "moe_backward.py", "dW2 = dY.T @ h", "dW2 = dY.T @ (a * b)"),
+    ("dw13_gate_up_swapped", "moe_backward.py",
+     "dW13 = np.concatenate([da.T @ X, db.T @ X], axis=0)",
+     "dW13 = np.concatenate([db.T @ X, da.T @ X], axis=0)"),
+    ("router_grad_rows_misaligned", "moe_backward.py",
+     "du.reshape(-1)[:, None] * np.repeat(x, K, axis=0))",
+     "du.reshape(-1)[:, None] * np.tile(x, (K, 1)))"),
+    ("fp8_router_quotient_sign", "fp8_backward.py", "(dg - mean) / np.where",
+     "(dg + mean) / np.where"),
     # sequence-level balance loss
     ("balance_f_without_e", "seq_balance.py", "f = cnt * E / (K * L)", "f = cnt / (K * L)"),
     ("balance_grad_sign", "seq_balance.py", "(f[None, :] - F[:, None])",
      "(F[:, None] - f[None, :])"),
+    ("balance_affinity_unnormalized", "seq_balance.py",
+     "sn = np.where(dead[:, None], 1.0 / E, s / np.where(dead, 1.0, S)[:, None])",
+     "sn = np.where(dead[:, None], 1.0 / E, s)"),
+    ("balance_sigmoid_derivative_dropped", "seq_balance.py",
+     "du[rows] = ds * s[rows] * (1.0 - s[rows])", "du[rows] = ds * s[rows]"),
     # FP8 backward (E5M2 gradients, E4M3 activations and weights)
     ("e5m2_exponent_bias", "fp8_backward.py",
      "(1.0 + mant / 4.0) * np.exp2(ex - 15.0))", "(1.0 + mant / 4.0) * np.exp2(ex - 16.0))"),
