@@ -8,7 +8,6 @@ checks which operand each GEMM quantizes and along which axis; and the
 quantization error against its bound.
 """
 import numpy as np
-import pytest
 import torch
 
 import oracle as O

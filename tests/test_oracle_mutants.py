@@ -12,7 +12,6 @@ import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
-import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_SUITES = ["test_oracle_pins.py", "test_oracle_backward.py", "test_oracle_fp8_backward.py",

@@ -6,7 +6,6 @@ pages state, or a hand-worked example (tests/golden/).
 """
 import itertools
 import json
-import math
 import os
 
 import numpy as np

@@ -10,7 +10,6 @@ dropped term, a wrong sign, a transposed operand or a wrong normalization
 (by K, L or E) fails at least one of them.
 """
 import numpy as np
-import pytest
 import torch
 
 import oracle
