@@ -116,6 +116,11 @@ def test_route_golden_hand_example():
     (16, 2, 1, 1, 2, 300, "ties"), (16, 16, 1, 1, 2, 50, "normal"), (100, 5, 1, 1, 2, 257, "normal"),
     (96, 6, 4, 2, 3, 333, "normal"), (256, 8, 8, 4, 2, 1000, "saturate"),
     (512, 8, 16, 4, 1, 129, "normal"), (64, 6, 8, 3, 2, 1, "normal"), (8, 2, 4, 2, 2, 77, "ties"),
+    # the largest routing accepted: top-64 of 512 experts in 64 groups, with
+    # exactly K eligible experts (8 groups of 8), with the group scores from
+    # the top 8 of each group, and groups of 32 scored from their top 3
+    (512, 64, 64, 8, 1, 150, "ties"), (512, 64, 64, 64, 8, 200, "normal"),
+    (512, 32, 16, 4, 3, 100, "saturate"),
 ])
 def test_route_from_logits_edge_cases(E, K, G, Mg, topn, T, kind):
     _log(f"route edge E={E} K={K} G={G} M={Mg} topn={topn} T={T} {kind}")

@@ -51,7 +51,25 @@ def _cases(n=48, seed=2024, dtypes=("bf16", "f32", "fp8"), prefix="sweep"):
     return out
 
 
-CASES = _cases()
+def _limit_cases(prefix, dtypes):
+    """The largest routing the boundary accepts: 512 experts in 64 groups of
+    8 and top-64, so the tile tables hold all 512 routed groups. Case 0 on the
+    small-batch tiles (9 rows per expert) takes 8 of the 64 groups, exactly K
+    eligible experts per token; case 1 on the prefill tiles (75 rows per
+    expert) allows every group, with the group scores from the top 8."""
+    out = []
+    for dt in dtypes:
+        mult = 128 if dt == "fp8" else 64
+        for j, (T, Mg, topn, Is) in enumerate([(72, 8, 1, mult), (600, 64, 8, 0)]):
+            out.append(Workload(f"{prefix}_{dt}{j}", T=T, d=2 * mult, E=512, K=64, I=mult,
+                                Is=Is, G=64, M=Mg, topn=topn,
+                                act="f32" if dt == "f32" else "bf16", w=dt,
+                                x_kind="clusters", n_clusters=3, bias_kind="uniform",
+                                bias_amp=0.05, w_std=0.05, seed=900 + j))
+    return out
+
+
+CASES = _cases() + _limit_cases("limit", ("bf16", "f32", "fp8"))
 
 
 @pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
@@ -80,7 +98,8 @@ def test_forward_sweep(wl):
     assert err <= TOL[wl.w]
 
 
-TRAIN_CASES = _cases(12, seed=77, dtypes=("bf16", "fp8"), prefix="train")
+TRAIN_CASES = (_cases(12, seed=77, dtypes=("bf16", "fp8"), prefix="train") +
+               _limit_cases("train_limit", ("bf16", "fp8")))
 
 
 @pytest.mark.parametrize("wl", TRAIN_CASES, ids=[w.name for w in TRAIN_CASES])
@@ -100,10 +119,26 @@ def test_backward_sweep(wl):
     dw13, dw2 = host(gr["dw13"]), host(gr["dw2"])
     counts = host(sv["counts"])
     used = np.nonzero(counts)[0]
+    if wl.w == "fp8":
+        # FP8 weight gradients of experts with 1-3 tokens: the 128x1 tile of
+        # a channel then spans all of the expert's tokens, and its scale is
+        # set by the largest of them. One bf16 ulp of difference in that
+        # value (the kernel's fp32 sum order against the fp64 oracle) moves
+        # the scale and can move another token's E5M2 code by one step.
+        # Where two tokens' terms nearly cancel, that step is a large share of
+        # the result. At 512 experts, an expert with 2 tokens reads 0.17, and
+        # the oracle with that one value lowered by one bf16 ulp agrees with
+        # the kernel to 9e-5. Such experts are held to one E5M2 step (0.25)
+        # of the expert's largest entry; the others to the FP8 tolerance.
+        few = [e for e in used if counts[e] < 4]
+        used = [e for e in used if counts[e] >= 4]
+        for e in few:
+            for name, g, r in (("dw13", dw13[e], ref.dw13[e]), ("dw2", dw2[e], ref.dw2[e])):
+                assert mat_rel_err(g, r) <= 0.25, (name, int(e), int(counts[e]))
     errs = {"dx": row_rel_err(host(dx), ref.dx),
             "dw_router": mat_rel_err(host(gr["dw_router"]), ref.dw_router),
-            "dw13": max(mat_rel_err(dw13[e], ref.dw13[e]) for e in used),
-            "dw2": max(mat_rel_err(dw2[e], ref.dw2[e]) for e in used)}
+            "dw13": max((mat_rel_err(dw13[e], ref.dw13[e]) for e in used), default=0.0),
+            "dw2": max((mat_rel_err(dw2[e], ref.dw2[e]) for e in used), default=0.0)}
     if wl.Is:
         errs["dws13"] = mat_rel_err(host(gr["dws13"]), ref.dws13)
         errs["dws2"] = mat_rel_err(host(gr["dws2"]), ref.dws2)
